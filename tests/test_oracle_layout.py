@@ -1,0 +1,291 @@
+"""Pins for the oracle's block decoders (CPU only).
+
+The decoders are checked against (a) blocks whose bytes are written out by
+hand with the expected weights derived by hand from the layout reading, (b) a
+bit-probe: every single bit of a random block is flipped and exactly the
+weights that a forward byte->field table predicts must change, by exactly the
+predicted amount, and (c) encoder/decoder round trips.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+from oracle import kquant as kq
+
+
+def f16_bytes(x):
+    return np.array([x], dtype=np.float16).view(np.uint8)
+
+
+# ------------------------------------------------------------ Q6_K pins ----
+
+def q6k_block(d=1.0, sc=1, ql=0, qh=0):
+    b = np.zeros(210, dtype=np.uint8)
+    b[0:128] = ql
+    b[128:192] = qh
+    b[192:208] = np.array([sc] * 16 if np.isscalar(sc) else sc, dtype=np.int8).view(np.uint8)
+    b[208:210] = f16_bytes(d)
+    return b
+
+
+def test_q6k_all_zero_codes_give_minus_32():
+    w = kq.decode_q6k(q6k_block(d=1.0, sc=1, ql=0, qh=0))
+    assert np.array_equal(w, np.full(256, -32.0))
+
+
+def test_q6k_all_ones_codes_give_plus_31():
+    w = kq.decode_q6k(q6k_block(d=1.0, sc=1, ql=0xFF, qh=0xFF))
+    assert np.array_equal(w, np.full(256, 31.0))
+
+
+def test_q6k_scale_and_d_closed_form():
+    # q = 0 everywhere -> w_i = d * sc_{i//16} * (-32)
+    sc = [s - 8 for s in range(16)]
+    w = kq.decode_q6k(q6k_block(d=0.5, sc=sc))
+    expect = np.array([0.5 * (i // 16 - 8) * -32 for i in range(256)])
+    assert np.array_equal(w, expect)
+
+
+def test_q6k_hand_placed_bytes():
+    g = _golden("q6k_hand_block.txt")
+    b = q6k_block(d=1.0, sc=1)
+    for field, idx, val in g["set"]:
+        b[{"ql": 0, "qh": 128}[field] + int(idx)] = int(val, 16)
+    expect = np.full(256, -32.0)
+    for i, v in g["w"]:
+        expect[int(i)] = float(v)
+    assert np.array_equal(kq.decode_q6k(b), expect)
+
+
+def test_q6k_subnormal_d_is_exact():
+    d = np.float16(2.0 ** -20)   # subnormal f16
+    w = kq.decode_q6k(q6k_block(d=float(d), sc=3, ql=0x11, qh=0))
+    # q = 1 everywhere -> w = d*3*(1-32)
+    assert np.array_equal(w, np.full(256, float(d) * 3 * -31))
+
+
+# ------------------------------------------------------------ Q5_K pins ----
+
+def _golden(name):
+    """Parse a tests/golden fixture: {key: [tokens...]} (repeated keys -> list of lists)."""
+    out = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, rest = line.split(":", 1)
+            out.setdefault(key.strip(), []).append(rest.split())
+    return out
+
+
+# 12 scale bytes and the (sc, m) fields they hold, derived by hand from the
+# 6-bit packing stated in oracle/kquant.py.
+_G = _golden("q5k_scale_packing.txt")
+GOLD_SCALE_BYTES = [int(x, 16) for x in _G["bytes"][0]]
+GOLD_SC = [int(x) for x in _G["sc"][0]]
+GOLD_M = [int(x) for x in _G["m"][0]]
+
+
+def q5k_block(d=1.0, dmin=0.0, scale_bytes=None, qh=0, qs=0):
+    b = np.zeros(176, dtype=np.uint8)
+    b[0:2] = f16_bytes(d)
+    b[2:4] = f16_bytes(dmin)
+    if scale_bytes is not None:
+        b[4:16] = scale_bytes
+    b[16:48] = qh
+    b[48:176] = qs
+    return b
+
+
+def test_q5k_scale_unpack_golden():
+    sc, m = kq.q5k_scale_min(q5k_block(scale_bytes=GOLD_SCALE_BYTES))
+    assert list(sc) == GOLD_SC and list(m) == GOLD_M
+
+
+# all sc_j = 1, all m_j = 0
+UNIT_SCALES = [1, 1, 1, 1, 0, 0, 0, 0, 1, 1, 1, 1]
+
+
+def test_q5k_hand_placed_bytes():
+    g = _golden("q5k_hand_block.txt")
+    b = q5k_block(d=1.0, dmin=0.0, scale_bytes=UNIT_SCALES)
+    for field, idx, val in g["set"]:
+        b[{"qh": 16, "qs": 48}[field] + int(idx)] = int(val, 16)
+    expect = np.zeros(256)
+    for i, v in g["w"]:
+        expect[int(i)] = float(v)
+    assert np.array_equal(kq.decode_q5k(b), expect)
+
+
+def test_q5k_d_sc_q_closed_form():
+    # d=1, dmin=0, qs = 0xFF, qh = 0xFF -> q = 31 everywhere, w = sc_j * 31
+    w = kq.decode_q5k(q5k_block(d=1.0, dmin=0.0, scale_bytes=GOLD_SCALE_BYTES, qh=0xFF, qs=0xFF))
+    assert np.array_equal(w, np.array([GOLD_SC[i // 32] * 31.0 for i in range(256)]))
+
+
+def test_q5k_dmin_closed_form():
+    # d=0, dmin=1 -> w = -m_j, whatever the codes
+    w = kq.decode_q5k(q5k_block(d=0.0, dmin=1.0, scale_bytes=GOLD_SCALE_BYTES, qh=0x5A, qs=0x3C))
+    assert np.array_equal(w, np.array([-float(GOLD_M[i // 32]) for i in range(256)]))
+
+
+def test_q5k_fields_at_extremes():
+    for byte in (0x00, 0xFF):
+        sc, m = kq.q5k_scale_min(q5k_block(scale_bytes=[byte] * 12))
+        want = 63 if byte else 0
+        assert (sc == want).all() and (m == want).all()
+
+
+def test_q5k_subnormal_dmin_is_exact():
+    dmin = float(np.float16(2.0 ** -22))
+    w = kq.decode_q5k(q5k_block(d=0.0, dmin=dmin, scale_bytes=[0xFF] * 12))
+    assert np.array_equal(w, np.full(256, -63 * dmin))
+
+
+# --------------------------------------------------------------- bit probe --
+# Forward tables: (byte, bit) -> which value/field changes.  They are written
+# from the layout reading in the byte->field direction, the opposite of the
+# decoder's value->byte indexing, so an index mistake in either shows up.
+
+def _q5k_probe_prediction(base, byte, bit):
+    """Predicted change of the 256 weights when (byte, bit) of `base` flips."""
+    d = float(base[0:2].view(np.float16)[0])
+    dmin = float(base[2:4].view(np.float16)[0])
+    sc, m = kq.q5k_scale_min(base)
+    q = kq.q5k_codes(base)
+    sign = -1 if (int(base[byte]) >> bit) & 1 else 1
+    dw = np.zeros(256)
+    if 48 <= byte < 176:                      # qs
+        B = byte - 48
+        c, l = B // 32, B % 32
+        if bit < 4:
+            i, dq = 64 * c + l, sign * (1 << bit)
+        else:
+            i, dq = 64 * c + 32 + l, sign * (1 << (bit - 4))
+        dw[i] = d * sc[i // 32] * dq
+    elif 16 <= byte < 48:                     # qh
+        l = byte - 16
+        i = 32 * bit + l
+        dw[i] = d * sc[bit] * 16 * sign
+    elif 4 <= byte < 16:                      # packed 6-bit scale/min
+        p = byte - 4
+        if p < 4:
+            field, j, pos = ("sc", p, bit) if bit < 6 else ("sc", p + 4, 4 + bit - 6)
+        elif p < 8:
+            field, j, pos = ("m", p - 4, bit) if bit < 6 else ("m", p, 4 + bit - 6)
+        else:
+            field, j, pos = ("sc", p - 4, bit) if bit < 4 else ("m", p - 4, bit - 4)
+        delta = sign * (1 << pos)
+        for i in range(32 * j, 32 * j + 32):
+            dw[i] = d * delta * q[i] if field == "sc" else -dmin * delta
+    else:
+        return None                           # d / dmin: checked separately
+    return dw
+
+
+def _q6k_probe_prediction(base, byte, bit):
+    d = float(base[208:210].view(np.float16)[0])
+    sc = kq.q6k_scales(base)
+    q = kq.q6k_codes(base)
+    sign = -1 if (int(base[byte]) >> bit) & 1 else 1
+    dw = np.zeros(256)
+    if byte < 128:                            # ql
+        h, B = byte // 64, byte % 64
+        g2, l = B // 32, B % 32
+        g = g2 if bit < 4 else g2 + 2
+        i = 128 * h + 32 * g + l
+        dw[i] = d * sc[i // 16] * sign * (1 << (bit % 4))
+    elif byte < 192:                          # qh
+        B = byte - 128
+        h, l = B // 32, B % 32
+        i = 128 * h + 32 * (bit // 2) + l
+        dw[i] = d * sc[i // 16] * sign * 16 * (1 << (bit % 2))
+    elif byte < 208:                          # int8 scale: two's complement bit weight
+        s = byte - 192
+        delta = sign * (1 << bit) * (-1 if bit == 7 else 1)
+        for i in range(16 * s, 16 * s + 16):
+            dw[i] = d * delta * (q[i] - 32)
+    else:
+        return None
+    return dw
+
+
+@pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
+def test_bit_probe_every_bit(qtype):
+    from gguf_quant_block_amd import synth
+    g = synth.rng(99, 0, 0)
+    base = synth.blocks(qtype, 1, 256, g)[0]
+    dec = kq.decode_q5k if qtype == "q5_k" else kq.decode_q6k
+    pred = _q5k_probe_prediction if qtype == "q5_k" else _q6k_probe_prediction
+    w0 = dec(base)
+    nbits = 0
+    for byte in range(base.size):
+        for bit in range(8):
+            flipped = base.copy()
+            flipped[byte] ^= np.uint8(1 << bit)
+            dw = pred(base, byte, bit)
+            if dw is None:
+                continue
+            got = dec(flipped) - w0
+            assert np.array_equal(np.nonzero(got)[0], np.nonzero(dw)[0]), (byte, bit)
+            assert np.allclose(got, dw, rtol=0, atol=1e-12 * max(1.0, np.abs(w0).max())), (byte, bit)
+            nbits += 1
+    # every bit except the f16 header words is probed
+    assert nbits == 8 * (base.size - (4 if qtype == "q5_k" else 2))
+
+
+def test_header_words_scale_all_weights():
+    # Changing d (and dmin) rescales the weights as the formula says.
+    from gguf_quant_block_amd import synth
+    b5 = synth.q5k_blocks(1, 256, synth.rng(99, 1, 0))[0]
+    sc, m = kq.q5k_scale_min(b5)
+    q = kq.q5k_codes(b5)
+    for d, dmin in ((1.0, 0.0), (0.0, 1.0), (0.25, 2.0)):
+        b = b5.copy()
+        b[0:2] = f16_bytes(d)
+        b[2:4] = f16_bytes(dmin)
+        j = np.arange(256) // 32
+        assert np.array_equal(kq.decode_q5k(b), d * sc[j] * q - dmin * m[j])
+    b6 = synth.q6k_blocks(1, 256, synth.rng(99, 2, 0))[0]
+    b6[208:210] = f16_bytes(2.0)
+    s = np.arange(256) // 16
+    assert np.array_equal(kq.decode_q6k(b6), 2.0 * kq.q6k_scales(b6)[s] * (kq.q6k_codes(b6) - 32))
+
+
+# -------------------------------------------------------------- round trip --
+
+def test_encode_decode_round_trip():
+    g = np.random.default_rng(7)
+    for _ in range(20):
+        sc = g.integers(0, 64, 8)
+        m = g.integers(0, 64, 8)
+        q = g.integers(0, 32, 256)
+        d, dmin = float(np.float16(g.uniform(1e-3, 1e-2))), float(np.float16(g.uniform(0, 5e-3)))
+        b = kq.encode_q5k(d, dmin, sc, m, q)
+        sc2, m2 = kq.q5k_scale_min(b)
+        assert (sc2 == sc).all() and (m2 == m).all() and (kq.q5k_codes(b) == q).all()
+        j = np.arange(256) // 32
+        assert np.array_equal(kq.decode_q5k(b), d * sc[j] * q - dmin * m[j])
+
+        sc6 = g.integers(-32, 32, 16)
+        q6 = g.integers(0, 64, 256)
+        b6 = kq.encode_q6k(d, sc6, q6)
+        assert (kq.q6k_scales(b6) == sc6).all() and (kq.q6k_codes(b6) == q6).all()
+    # closed form built through the encoder: sc_s = s-8, q_i = i mod 64
+    b = kq.encode_q6k(1.0, [s - 8 for s in range(16)], [i % 64 for i in range(256)])
+    assert np.array_equal(kq.decode_q6k(b), np.array([(i // 16 - 8) * (i % 64 - 32) for i in range(256)], float))
+
+
+def test_random_blocks_decode_codes_in_range():
+    from gguf_quant_block_amd import synth
+    b5 = kq.as_blocks(synth.q5k_blocks(4, 1024, synth.rng(99, 3, 0)), "q5_k")
+    q5 = kq.q5k_codes(b5)
+    assert q5.min() >= 0 and q5.max() <= 31
+    b6 = kq.as_blocks(synth.q6k_blocks(4, 1024, synth.rng(99, 4, 0)), "q6_k")
+    q6 = kq.q6k_codes(b6)
+    assert q6.min() >= 0 and q6.max() <= 63
+    s = kq.q6k_scales(b6)
+    assert s.min() >= -32 and s.max() <= 31
