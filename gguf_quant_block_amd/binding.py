@@ -1,0 +1,200 @@
+"""ctypes binding of libfcgguf.so (the C-ABI declared in include/fc_gguf.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is not built, or no GPU is visible,
+calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfcgguf.so")
+
+Q5_K, Q6_K = 5, 6
+QTYPES = {"q5_k": Q5_K, "q6_k": Q6_K}
+BLOCK_BYTES = {Q5_K: 176, Q6_K: 210}
+PATHS = {"auto": 0, "decode": 1, "prefill": 2}
+
+_lib = None
+_lock = threading.Lock()
+
+_c_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_SIGS = {
+    "fc_gguf_create": (ctypes.c_int, [_c_i64, _c_i64, ctypes.c_int, _vp, ctypes.c_int, ctypes.POINTER(_vp)]),
+    "fc_gguf_create_grouped": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_int, _vp, ctypes.c_int,
+                                              ctypes.POINTER(_vp)]),
+    "fc_gguf_run": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp, _vp]),
+    "fc_gguf_run_grouped": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp]),
+    "fc_gguf_set_path": (ctypes.c_int, [_vp, ctypes.c_int]),
+    "fc_gguf_destroy": (ctypes.c_int, [_vp]),
+    "fc_gguf_info": (ctypes.c_int, [_vp, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64),
+                                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_c_i64)]),
+    "fc_gguf_debug_quantize": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "fc_gguf_debug_int_dots": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp]),
+    "fc_gguf_debug_weights": (ctypes.c_int, [_vp, _vp, _vp]),
+    "fc_gguf_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+class FcGgufError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run `python -m gguf_quant_block_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().fc_gguf_strerror(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise FcGgufError(code, what)
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible: the FC library has no CPU path")
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _blocks_arg(blocks):
+    """(pointer, on_device, keepalive) for a numpy or torch uint8 array."""
+    import numpy as np
+    if isinstance(blocks, np.ndarray):
+        arr = np.ascontiguousarray(blocks, dtype=np.uint8)
+        return ctypes.c_void_p(arr.ctypes.data), 0, arr
+    torch = _torch()
+    assert blocks.dtype == torch.uint8
+    t = blocks.contiguous()
+    return ctypes.c_void_p(t.data_ptr()), (1 if t.is_cuda else 0), t
+
+
+class FcGguf:
+    """One weight matrix W[N, K] in GGUF Q5_K or Q6_K blocks, resident on the GPU.
+
+    y = fc(A, R=None, out=None): A f16 [..., K] on cuda; R f16 [..., N] or None.
+    """
+
+    def __init__(self, N: int, K: int, qtype: str, blocks, *, experts: int | None = None):
+        self.N, self.K, self.qtype = int(N), int(K), qtype
+        self.experts = experts
+        ptr, on_dev, keep = _blocks_arg(blocks)
+        h = ctypes.c_void_p()
+        if experts is None:
+            _check(lib().fc_gguf_create(self.N, self.K, QTYPES[qtype], ptr, on_dev, ctypes.byref(h)),
+                   "fc_gguf_create")
+        else:
+            _check(lib().fc_gguf_create_grouped(int(experts), self.N, self.K, QTYPES[qtype], ptr, on_dev,
+                                                ctypes.byref(h)), "fc_gguf_create_grouped")
+        del keep
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().fc_gguf_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_path(self, path: str):
+        _check(lib().fc_gguf_set_path(self._h, PATHS[path]), "fc_gguf_set_path")
+
+    @property
+    def weight_bytes(self) -> int:
+        wb = ctypes.c_int64()
+        _check(lib().fc_gguf_info(self._h, None, None, None, ctypes.byref(wb)), "fc_gguf_info")
+        return wb.value
+
+    def __call__(self, A, R=None, out=None):
+        torch = _torch()
+        assert A.dtype == torch.float16 and A.is_cuda and A.shape[-1] == self.K
+        lead = A.shape[:-1]
+        A2 = A.reshape(-1, self.K).contiguous()
+        M = A2.shape[0]
+        if R is not None:
+            assert R.dtype == torch.float16 and R.shape == (*lead, self.N)
+            R = R.reshape(M, self.N).contiguous()
+        if out is None:
+            out = torch.empty((*lead, self.N), dtype=torch.float16, device=A.device)
+        assert out.is_contiguous() and out.dtype == torch.float16
+        _check(lib().fc_gguf_run(self._h, _ptr(A2), M, _ptr(R), _ptr(out), _stream()), "fc_gguf_run")
+        return out
+
+    def grouped(self, A, ids, a_per_slot: bool, out=None):
+        """MoE: Y[t, j] = A_row(t, j) . W_{ids[t, j]}^T; A f16 [T, K] or [T, top_k, K]."""
+        torch = _torch()
+        T, top_k = ids.shape
+        ids = ids.to(torch.int32).contiguous()
+        A = A.contiguous()
+        if out is None:
+            out = torch.empty((T, top_k, self.N), dtype=torch.float16, device=A.device)
+        _check(lib().fc_gguf_run_grouped(self._h, _ptr(A), T, 1 if a_per_slot else 0, _ptr(ids), top_k,
+                                         _ptr(out), _stream()), "fc_gguf_run_grouped")
+        return out
+
+    # ---- test exports ----
+    def debug_int_dots(self, qa):
+        torch = _torch()
+        M = qa.shape[0]
+        ns = self.K // (32 if self.qtype == "q5_k" else 16)
+        S = torch.empty((M, self.N, ns), dtype=torch.int32, device=qa.device)
+        _check(lib().fc_gguf_debug_int_dots(self._h, _ptr(qa.contiguous()), M, _ptr(S), _stream()),
+               "fc_gguf_debug_int_dots")
+        return S
+
+    def debug_weights(self):
+        torch = _torch()
+        out = torch.empty(self.weight_bytes, dtype=torch.uint8, device="cuda")
+        _check(lib().fc_gguf_debug_weights(self._h, _ptr(out), _stream()), "fc_gguf_debug_weights")
+        return out
+
+
+def debug_quantize(A):
+    """The decode path's per-32 int8 quantisation: (qa i8[M,K], s f32[M,K/32], T i32[M,K/32])."""
+    torch = _torch()
+    M, K = A.shape
+    qa = torch.empty((M, K), dtype=torch.int8, device=A.device)
+    s = torch.empty((M, K // 32), dtype=torch.float32, device=A.device)
+    T = torch.empty((M, K // 32), dtype=torch.int32, device=A.device)
+    _check(lib().fc_gguf_debug_quantize(_ptr(A.contiguous()), M, K, _ptr(qa), _ptr(s), _ptr(T), _stream()),
+           "fc_gguf_debug_quantize")
+    return qa, s, T

@@ -1,0 +1,274 @@
+// C-ABI of the GGUF K-quant FC library (declarations and contracts in
+// include/fc_gguf.h).  Host logic only: argument checks, weight upload and
+// Q6_K regroup, path selection from the row count, launch configuration and
+// the split-K workspace.  Every step of the computation runs in the HIP
+// kernels of this library.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "fc_gguf.h"
+#include "internal.h"
+
+struct fc_gguf {
+  int64_t E = 1, N = 0, K = 0;
+  int qtype = 0;
+  uint8_t* w = nullptr;         // device weights (Q5_K AoS; Q6_K planes, per expert)
+  size_t expert_bytes = 0;      // bytes of one [N, K] matrix
+  int path = FC_GGUF_PATH_AUTO;
+  int device = 0;
+  int num_cu = 256;
+  void* ws = nullptr;           // device workspace (split-K partials, MoE bucketing)
+  size_t ws_bytes = 0;
+  hipError_t last = hipSuccess;
+};
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int block_bytes(int qtype) {
+  return qtype == FC_GGUF_Q5_K ? 176 : (qtype == FC_GGUF_Q6_K ? 210 : 0);
+}
+
+int hip_fail(fc_gguf* h, hipError_t e) {
+  if (h) h->last = e;
+  return FC_GGUF_EHIP;
+}
+
+int default_path() {
+  const char* p = getenv("FC_GGUF_PATH");
+  if (!p) return FC_GGUF_PATH_AUTO;
+  if (!strcmp(p, "decode")) return FC_GGUF_PATH_DECODE;
+  if (!strcmp(p, "prefill")) return FC_GGUF_PATH_PREFILL;
+  return FC_GGUF_PATH_AUTO;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int ensure_ws(fc_gguf* h, size_t bytes) {
+  if (bytes <= h->ws_bytes) return FC_GGUF_OK;
+  if (h->ws) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(h, e);
+    hipFree(h->ws);
+    h->ws = nullptr;
+    h->ws_bytes = 0;
+  }
+  hipError_t e = hipMalloc(&h->ws, bytes);
+  if (e != hipSuccess) {
+    h->ws = nullptr;
+    h->last = e;
+    return FC_GGUF_ENOMEM;
+  }
+  h->ws_bytes = bytes;
+  return FC_GGUF_OK;
+}
+
+int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, int on_device,
+                fc_gguf_t* out) {
+  if (!out) return FC_GGUF_EINVAL;
+  *out = nullptr;
+  if (!blocks || E <= 0 || N <= 0 || K <= 0 || (K % 256) != 0) return FC_GGUF_EINVAL;
+  const int bb = block_bytes(qtype);
+  if (!bb) return FC_GGUF_EUNSUPPORTED;
+  if (N > kMaxDim || K > kMaxDim || E > 65536) return FC_GGUF_ERANGE;
+  const size_t nblk = (size_t)N * (size_t)(K / 256);
+  const size_t expert_bytes = nblk * (size_t)bb;
+  if (nblk > ((size_t)1 << 31) / 256) return FC_GGUF_ERANGE;
+
+  fc_gguf* h = new (std::nothrow) fc_gguf();
+  if (!h) return FC_GGUF_ENOMEM;
+  h->E = E;
+  h->N = N;
+  h->K = K;
+  h->qtype = qtype;
+  h->expert_bytes = expert_bytes;
+  h->path = default_path();
+  hipError_t e = hipGetDevice(&h->device);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return FC_GGUF_EHIP;
+  }
+  const size_t total = expert_bytes * (size_t)E;
+  e = hipMalloc(&h->w, total);
+  if (e != hipSuccess) {
+    delete h;
+    return FC_GGUF_ENOMEM;
+  }
+  const hipMemcpyKind kind = on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  if (qtype == FC_GGUF_Q5_K) {
+    e = hipMemcpy(h->w, blocks, total, kind);
+  } else {
+    // Q6_K: regroup every expert's blocks into its own QL|QH|SC|D planes.
+    const uint8_t* src = (const uint8_t*)blocks;
+    uint8_t* staging = nullptr;
+    if (!on_device) {
+      e = hipMalloc(&staging, total);
+      if (e == hipSuccess) e = hipMemcpy(staging, blocks, total, hipMemcpyHostToDevice);
+      src = staging;
+    }
+    for (int64_t x = 0; e == hipSuccess && x < E; ++x)
+      e = fcg::launch_q6k_regroup(src + x * expert_bytes, h->w + x * expert_bytes, nblk, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (staging) hipFree(staging);
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    hipFree(h->w);
+    delete h;
+    return FC_GGUF_EHIP;
+  }
+  *out = h;
+  return FC_GGUF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fc_gguf_create(int64_t N, int64_t K, int qtype, const void* blocks, int blocks_on_device,
+                   fc_gguf_t* out) {
+  return create_impl(1, N, K, qtype, blocks, blocks_on_device, out);
+}
+
+int fc_gguf_create_grouped(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks,
+                           int blocks_on_device, fc_gguf_t* out) {
+  return create_impl(E, N, K, qtype, blocks, blocks_on_device, out);
+}
+
+int fc_gguf_destroy(fc_gguf_t h) {
+  if (!h) return FC_GGUF_OK;
+  hipDeviceSynchronize();
+  if (h->w) hipFree(h->w);
+  if (h->ws) hipFree(h->ws);
+  delete h;
+  return FC_GGUF_OK;
+}
+
+int fc_gguf_set_path(fc_gguf_t h, int path) {
+  if (!h) return FC_GGUF_EINVAL;
+  if (path < FC_GGUF_PATH_AUTO || path > FC_GGUF_PATH_PREFILL) return FC_GGUF_EUNSUPPORTED;
+  h->path = path;
+  return FC_GGUF_OK;
+}
+
+int fc_gguf_info(fc_gguf_t h, int64_t* N, int64_t* K, int* qtype, int64_t* weight_bytes) {
+  if (!h) return FC_GGUF_EINVAL;
+  if (N) *N = h->N;
+  if (K) *K = h->K;
+  if (qtype) *qtype = h->qtype;
+  if (weight_bytes) *weight_bytes = (int64_t)(h->expert_bytes * (size_t)h->E);
+  return FC_GGUF_OK;
+}
+
+int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, void* stream) {
+  if (!h || M < 0) return FC_GGUF_EINVAL;
+  if (h->E != 1) return FC_GGUF_EINVAL;            // grouped handles use run_grouped
+  if (M == 0) return FC_GGUF_OK;
+  if (!A || !Y) return FC_GGUF_EINVAL;
+  if (M > kMaxDim || M * h->N > ((int64_t)1 << 31) || M * h->K > ((int64_t)1 << 31))
+    return FC_GGUF_ERANGE;
+  if (!aligned(A, 16) || !aligned(Y, 8) || (R && !aligned(R, 8))) return FC_GGUF_EINVAL;
+  const int N = (int)h->N, K = (int)h->K;
+  hipStream_t st = (hipStream_t)stream;
+  int path = h->path;
+  if (path == FC_GGUF_PATH_AUTO) path = M < 8 ? FC_GGUF_PATH_DECODE : FC_GGUF_PATH_PREFILL;
+  const fcg::f16* a = (const fcg::f16*)A;
+  const fcg::f16* r = (const fcg::f16*)R;
+  fcg::f16* y = (fcg::f16*)Y;
+  hipError_t e = hipSuccess;
+  if (path == FC_GGUF_PATH_DECODE) {
+    // rows in chunks of at most 7 (one launch each), smaller when the
+    // quantised activations of a chunk would not fit in one CU's LDS
+    int cap = 7;
+    while (cap > 1 && fcg::gemv_lds_bytes(h->qtype, cap, K) > 160 * 1024) --cap;
+    if (fcg::gemv_lds_bytes(h->qtype, cap, K) > 160 * 1024) return FC_GGUF_ERANGE;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += cap) {
+      const int mc = (int)(M - m0 < cap ? M - m0 : cap);
+      e = fcg::launch_gemv(h->qtype, h->w, a + m0 * K, r ? r + m0 * N : nullptr, y + m0 * N, mc,
+                           N, K, st);
+    }
+  } else {
+    int mt, nt, splits;
+    fcg::prefill_choose(h->qtype, (int)M, N, K, h->num_cu, &mt, &nt, &splits);
+    const size_t need = fcg::prefill_workspace_bytes((int)M, N, splits);
+    if (need) {
+      const int rc = ensure_ws(h, need);
+      if (rc != FC_GGUF_OK) return rc;
+    }
+    e = fcg::launch_prefill(h->qtype, h->w, a, r, y, (float*)h->ws, (int)M, N, K, mt, nt, splits,
+                            st);
+  }
+  if (e != hipSuccess) return hip_fail(h, e);
+  return FC_GGUF_OK;
+}
+
+int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, const int32_t* ids,
+                        int top_k, void* Y, void* stream) {
+  if (!h || T < 0) return FC_GGUF_EINVAL;
+  if (T == 0) return FC_GGUF_OK;
+  if (!A || !ids || !Y || top_k <= 0 || top_k > h->E || (a_per_slot != 0 && a_per_slot != 1))
+    return FC_GGUF_EINVAL;
+  if (T * top_k > ((int64_t)1 << 24) || T * top_k * h->K > ((int64_t)1 << 31) ||
+      T * top_k * h->N > ((int64_t)1 << 31))
+    return FC_GGUF_ERANGE;
+  if (!aligned(A, 16) || !aligned(Y, 8) || !aligned(ids, 4)) return FC_GGUF_EINVAL;
+  const size_t need = fcg::moe_workspace_bytes((int)h->E, (int)T, top_k);
+  const int rc = ensure_ws(h, need);
+  if (rc != FC_GGUF_OK) return rc;
+  hipError_t e = fcg::launch_moe(h->qtype, h->w, h->expert_bytes, (int)h->E, (int)h->N, (int)h->K,
+                                 (const fcg::f16*)A, (int)T, a_per_slot, ids, top_k, (fcg::f16*)Y,
+                                 h->ws, h->num_cu, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return FC_GGUF_EUNSUPPORTED;
+  if (e != hipSuccess) return hip_fail(h, e);
+  return FC_GGUF_OK;
+}
+
+int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s, int32_t* T,
+                           void* stream) {
+  if (M < 0 || K <= 0 || (K % 32) != 0) return FC_GGUF_EINVAL;
+  if (M == 0) return FC_GGUF_OK;
+  if (!A || !qa || !s || !T || !aligned(A, 16) || !aligned(qa, 16)) return FC_GGUF_EINVAL;
+  if (M * K > ((int64_t)1 << 31)) return FC_GGUF_ERANGE;
+  hipError_t e = fcg::launch_debug_quantize((const fcg::f16*)A, (int)M, (int)K, qa, s, T,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? FC_GGUF_OK : FC_GGUF_EHIP;
+}
+
+int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S, void* stream) {
+  if (!h || M < 0 || h->E != 1) return FC_GGUF_EINVAL;
+  if (M == 0) return FC_GGUF_OK;
+  if (!qa || !S || !aligned(qa, 16)) return FC_GGUF_EINVAL;
+  const int ns = (int)(h->K / (h->qtype == FC_GGUF_Q5_K ? 32 : 16));
+  if (M * h->N * ns > ((int64_t)1 << 31)) return FC_GGUF_ERANGE;
+  hipError_t e = fcg::launch_debug_int_dots(h->qtype, h->w, qa, (int)M, (int)h->N, (int)h->K, S,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? FC_GGUF_OK : hip_fail(h, e);
+}
+
+int fc_gguf_debug_weights(fc_gguf_t h, void* dst, void* stream) {
+  if (!h || !dst) return FC_GGUF_EINVAL;
+  hipError_t e = hipMemcpyAsync(dst, h->w, h->expert_bytes * (size_t)h->E, hipMemcpyDeviceToDevice,
+                                (hipStream_t)stream);
+  return e == hipSuccess ? FC_GGUF_OK : hip_fail(h, e);
+}
+
+const char* fc_gguf_strerror(int code) {
+  switch (code) {
+    case FC_GGUF_OK: return "ok";
+    case FC_GGUF_EINVAL: return "invalid argument";
+    case FC_GGUF_EUNSUPPORTED: return "unsupported qtype or path";
+    case FC_GGUF_ENOMEM: return "device allocation failed";
+    case FC_GGUF_EHIP: return "HIP runtime or launch error";
+    case FC_GGUF_ERANGE: return "size exceeds an internal limit";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

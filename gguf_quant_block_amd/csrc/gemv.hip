@@ -1,0 +1,737 @@
+// Decode path (M < 8): per-32 int8 activation quantisation fused into an
+// int8 GEMV that streams the raw Q5_K / Q6_K blocks once.
+//
+// OpenVINO PR #39119, section Implementation: the GEMV quantises the
+// activations per 32 values and takes int8 dot products directly against the
+// blocks; the residual Add is fused into the output store.
+//
+// Work layout (one launch, workgroup = 4 waves):
+//   * A wave owns R = 64 / (K/256) whole rows of W (one row per wave when a
+//     row has more than 64 blocks).  Their blocks are one contiguous byte
+//     range (Q5_K rows) or one range per plane (Q6_K), so the wave stages 64
+//     blocks at a time into its LDS slice with fully coalesced 16-byte
+//     global->LDS loads (global_load_lds_dwordx4), then every lane reads back
+//     and decodes ONE whole super-block with compile-time field offsets.
+//   * The activation loads are issued first, the staging loads second, and
+//     the workgroup quantises the M x K activations into LDS while the
+//     weights are in flight: int8 codes (16-byte chunks XOR-swizzled by the
+//     block index so lanes on different blocks hit different banks) and a
+//     per-(row, block) record of the f32 group scales s and the code sums
+//     the scale algebra needs (Q5_K: s*T per 32-group for the min term;
+//     Q6_K: 16-value sums for the -32 offset).
+//   * v_dot4_i32_i8 integer sums per sub-block, the scales applied in f32,
+//     the per-lane partials of a row summed in lane order (deterministic),
+//     plus R, rounded once to f16.
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace fcg {
+
+constexpr int GEMV_WAVES = 4;
+constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23: x + magic rounds x to an integer, ties to even
+
+// ------------------------------------------------------ LDS layout ----
+
+template <int QT> struct GemvFmt;
+template <> struct GemvFmt<QT_Q5K> {
+  static constexpr int REC = 20;           // words per (m, kb) record: s[8], s*T[8], pad[4]
+  static constexpr int STAGE = 64 * 176;   // one round of 64 blocks, AoS
+};
+template <> struct GemvFmt<QT_Q6K> {
+  static constexpr int REC = 28;           // s[8], T16[16], pad[4]
+  static constexpr int STAGE = 64 * 192;   // one round: QL (8 KB) | QH (4 KB)
+};
+
+struct GemvLayout {
+  size_t rec, part, dyn, total;   // dyn: dynamic LDS bytes; total: dynamic + static staging
+};
+
+// Dynamic LDS: qa int8 [MR][K] | rec u32 [MR][KB][REC] | part f32 [WAVES][MR][64].
+// The weight staging slices [WAVES][STAGE] are a separate static array, so
+// the compiler can tell the quantisation's LDS writes from the in-flight
+// global->LDS weight loads and does not wait for the latter before the former.
+template <int QT>
+__host__ __device__ constexpr GemvLayout gemv_layout(int MR, int K) {
+  const size_t qa = (size_t)MR * K;
+  const size_t rec = qa;
+  const size_t part = rec + (size_t)MR * (K / QK) * GemvFmt<QT>::REC * 4;
+  const size_t dyn = part + (size_t)GEMV_WAVES * MR * 64 * 4;
+  const size_t total = dyn + (size_t)GEMV_WAVES * GemvFmt<QT>::STAGE;
+  return GemvLayout{rec, part, dyn, total};
+}
+
+// byte offset of the 16-byte code chunk t (0..15) of block kb in row m
+__device__ __forceinline__ int qa_chunk(int m, int K, int kb, int t) {
+  return m * K + kb * QK + 16 * (t ^ (kb & 15));
+}
+
+// ------------------------------------------------ activation quantisation --
+// Per-32 int8 quantisation (OpenVINO PR #39119, sections Transformation and
+// Implementation: dynamic quantisation in groups of 32 for the int8 GEMV).
+// Symmetric: s = amax/127, inv = 127/amax (IEEE-correct f32 divisions),
+// code = round-half-even(fl32(a * inv)); |fl32(a * inv)| <= 127.5 so no clamp
+// is needed; an all-zero group gives s = 0 and codes 0.
+//
+// One lane quantises 8*V consecutive values (V = 1, 2 or 4); 4/V adjacent
+// lanes share a 32-value group and exchange its maximum, so every lane of the
+// group derives bit-identical s and inv.
+//   q[0 .. 2V):  packed int8 codes of the lane's values
+//   tsum:        sum of the group's 32 codes
+//   thalf[0,1]:  sums of the group's first and second 16 codes
+// All lanes of a group must call it together (it shuffles for V < 4).
+// round-half-even(fl32(a * inv)) in the low byte of the result.  The product
+// is rounded to f32 first and only then rounded to an integer (adding 1.5*2^23
+// rounds to the nearest integer, ties to even, for |x| < 2^22); the empty asm
+// keeps the compiler from fusing the two into one fma, which would round the
+// exact product once and differ on ties.
+__device__ __forceinline__ uint32_t rne_code(float a, float inv) {
+  float p = a * inv;
+  asm volatile("" : "+v"(p));
+  return __builtin_bit_cast(uint32_t, p + RNE_MAGIC);
+}
+
+template <int V>
+__device__ __forceinline__ void quant_lane(const uint4* raw, uint32_t* q, float& s, int& tsum,
+                                           int* thalf) {
+  half2v m2 = {(f16)0.f, (f16)0.f};
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(half2v, w[j] & 0x7FFF7FFFu));
+  }
+  float amax = fmaxf((float)m2[0], (float)m2[1]);
+  if constexpr (V < 4) amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  if constexpr (V < 2) amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  float inv = 0.f;
+  s = 0.f;
+  if (amax > 0.f) {
+    s = __fdiv_rn(amax, 127.0f);
+    inv = __fdiv_rn(127.0f, amax);
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      // four values -> four rounded floats -> the low byte of each is the code
+      const uint32_t r0 = rne_code(h2f(w[j]), inv);
+      const uint32_t r1 = rne_code(h2f(w[j] >> 16), inv);
+      const uint32_t r2 = rne_code(h2f(w[j + 1]), inv);
+      const uint32_t r3 = rne_code(h2f(w[j + 1] >> 16), inv);
+      const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(r3, r2, 0x0c0c0400u);
+      q[2 * i + (j >> 1)] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+  }
+  // code sums: 16-value halves and the group total
+  if constexpr (V == 4) {
+    int a = 0, b = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a = dot4((int)q[i], 0x01010101, a);
+#pragma unroll
+    for (int i = 4; i < 8; ++i) b = dot4((int)q[i], 0x01010101, b);
+    thalf[0] = a;
+    thalf[1] = b;
+  } else if constexpr (V == 2) {
+    int own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) own = dot4((int)q[i], 0x01010101, own);
+    const int other = __shfl_xor(own, 1, 64);
+    const bool first = (threadIdx.x & 1) == 0;
+    thalf[0] = first ? own : other;
+    thalf[1] = first ? other : own;
+  } else {
+    const int own = dot4((int)q[0], 0x01010101, dot4((int)q[1], 0x01010101, 0));
+    const int pair = own + __shfl_xor(own, 1, 64);
+    const int other = __shfl_xor(pair, 2, 64);
+    const bool first = (threadIdx.x & 2) == 0;
+    thalf[0] = first ? pair : other;
+    thalf[1] = first ? other : pair;
+  }
+  tsum = thalf[0] + thalf[1];
+}
+
+// Quantise MR rows of A into the LDS layout, on the workgroup's quantiser
+// waves only: lane ql of nlanes takes tasks ql, ql + nlanes, ... (one 32-value
+// group per task).  The activation loads of the first QPRE rounds are all
+// issued before any is used, so their latencies overlap.
+constexpr int QPRE = 4;
+
+template <int QT, int MR>
+__device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4 raw[4], uint8_t* smem,
+                                              uint32_t* rec) {
+  constexpr int REC = GemvFmt<QT>::REC;
+  const int KB = K / QK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = t < tasks ? raw[i] : make_uint4(0, 0, 0, 0);
+  uint32_t q[8];
+  float s;
+  int tsum, thalf[2];
+  quant_lane<4>(raw, q, s, tsum, thalf);
+  if (t < tasks) {
+    const int e = t * 32;                           // first value (flat over MR x K)
+    const int m = e / K, pos = e - m * K;
+    const int kb = pos / QK, t16 = (pos % QK) / 16, g = (pos % QK) / 32;
+    *(uint4*)(smem + qa_chunk(m, K, kb, t16)) = make_uint4(q[0], q[1], q[2], q[3]);
+    *(uint4*)(smem + qa_chunk(m, K, kb, t16 + 1)) = make_uint4(q[4], q[5], q[6], q[7]);
+    uint32_t* r = rec + ((size_t)m * KB + kb) * REC;
+    r[g] = __builtin_bit_cast(uint32_t, s);
+    if constexpr (QT == QT_Q5K) {
+      r[8 + g] = __builtin_bit_cast(uint32_t, s * (float)tsum);
+    } else {
+      r[8 + 2 * g] = (uint32_t)thalf[0];
+      r[8 + 2 * g + 1] = (uint32_t)thalf[1];
+    }
+  }
+}
+
+template <int QT, int MR>
+__device__ __forceinline__ void quantise_to_lds(const f16* A, int K, uint8_t* smem, int ql,
+                                                int nlanes) {
+  const int tasks = MR * K / 32;
+  uint32_t* rec = (uint32_t*)(smem + gemv_layout<QT>(MR, K).rec);
+  uint4 raw[QPRE][4];
+#pragma unroll
+  for (int r = 0; r < QPRE; ++r) {
+    const int t = r * nlanes + ql;
+    const int tc = t < tasks ? t : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[r][i] = *(const uint4*)(A + (size_t)tc * 32 + 8 * i);
+  }
+#pragma unroll
+  for (int r = 0; r < QPRE; ++r)
+    if (r * nlanes < tasks) quantise_task<QT, MR>(r * nlanes + ql, tasks, K, raw[r], smem, rec);
+  for (int t0 = QPRE * nlanes; t0 < tasks; t0 += nlanes) {
+    const int t = t0 + ql;
+    const int tc = t < tasks ? t : 0;
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *(const uint4*)(A + (size_t)tc * 32 + 8 * i);
+    quantise_task<QT, MR>(t, tasks, K, v, smem, rec);
+  }
+}
+
+// ----------------------------------------- codes and integer sub-block sums --
+// Q5_K: 176 B = d|dmin, scales[12], qh[32], qs[128] (11 x 16 B).  For the
+// sub-block pair (2c, 2c+1): qs[32c + l] low nibble -> value 64c + l, high
+// nibble -> 64c + 32 + l; bits 2c / 2c+1 of qh[l] are the fifth bits.
+// lo[w] / hi[w]: packed codes (0..31) of values 64c + 4w.. / 64c + 32 + 4w..
+template <int C>
+__device__ __forceinline__ void q5k_codes(const uint32_t* qh, const uint32_t* qs, uint32_t* lo,
+                                          uint32_t* hi) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint32_t d = qs[8 * C + w], h = qh[w];
+    const uint32_t hl = (4 - 2 * C >= 0 ? h << (4 - 2 * C) : h >> (2 * C - 4)) & 0x10101010u;
+    const uint32_t hh = (3 - 2 * C >= 0 ? h << (3 - 2 * C) : h >> (2 * C - 3)) & 0x10101010u;
+    lo[w] = (d & 0x0F0F0F0Fu) | hl;
+    hi[w] = ((d >> 4) & 0x0F0F0F0Fu) | hh;
+  }
+}
+
+// Q6_K: ql[64h + 32a + l] low nibble -> value 128h + 32a + l (pair 2a of
+// qh[32h + l]), high nibble -> value 128h + 32(a+2) + l (pair 2a+4).
+// lo[w] / hi[w]: packed codes (0..63) of values 128h+32a+4w.. / +64.
+template <int H, int A_>
+__device__ __forceinline__ void q6k_codes(const uint32_t* ql, const uint32_t* qh, uint32_t* lo,
+                                          uint32_t* hi) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint32_t d = ql[16 * H + 8 * A_ + w], h = qh[8 * H + w];
+    lo[w] = (d & 0x0F0F0F0Fu) | ((h << (4 - 2 * A_)) & 0x30303030u);
+    hi[w] = ((d >> 4) & 0x0F0F0F0Fu) | ((h >> (2 * A_)) & 0x30303030u);
+  }
+}
+
+__device__ __forceinline__ int dot16u(const uint32_t* c, uint4 a) {
+  int s = dot4((int)c[0], (int)a.x, 0);
+  s = dot4((int)c[1], (int)a.y, s);
+  s = dot4((int)c[2], (int)a.z, s);
+  return dot4((int)c[3], (int)a.w, s);
+}
+
+// ------------------------------------------------------- block kernels ----
+
+// Q5_K block -> part[m] (lane's contribution to row m): blk = the 44 words.
+template <int MR>
+__device__ __forceinline__ void q5k_block(const uint32_t* blk, int kb, int K, const uint8_t* smem,
+                                          const uint32_t* rec, int KB, float* part) {
+  const float d = h2f(blk[0]), dmin = h2f(blk[0] >> 16);
+  const uint32_t w0 = blk[1], w1 = blk[2], w2 = blk[3];
+  // 6-bit scales / mins as bytes: j = 0..3 and j = 4..7
+  const uint32_t sc_lo = w0 & 0x3F3F3F3Fu, m_lo = w1 & 0x3F3F3F3Fu;
+  const uint32_t sc_hi = (w2 & 0x0F0F0F0Fu) | ((w0 >> 2) & 0x30303030u);
+  const uint32_t m_hi = ((w2 >> 4) & 0x0F0F0F0Fu) | ((w1 >> 2) & 0x30303030u);
+  const uint32_t* qh = blk + 4;
+  const uint32_t* qs = blk + 12;
+  float X[MR], Z[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) X[m] = Z[m] = 0.f;
+  auto pair = [&](auto cc) {
+    constexpr int C = decltype(cc)::value;
+    uint32_t lo[8], hi[8];
+    q5k_codes<C>(qh, qs, lo, hi);
+    const uint32_t scw = C < 2 ? sc_lo : sc_hi, mw = C < 2 ? m_lo : m_hi;
+    const float sc0 = (float)((scw >> (16 * (C & 1))) & 0xFF), sc1 = (float)((scw >> (16 * (C & 1) + 8)) & 0xFF);
+    const float mn0 = (float)((mw >> (16 * (C & 1))) & 0xFF), mn1 = (float)((mw >> (16 * (C & 1) + 8)) & 0xFF);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const uint4 a0 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C));
+      const uint4 a1 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C + 1));
+      const uint4 a2 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C + 2));
+      const uint4 a3 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C + 3));
+      const int S0 = dot16u(lo, a0) + dot16u(lo + 4, a1);
+      const int S1 = dot16u(hi, a2) + dot16u(hi + 4, a3);
+      const uint32_t* r = rec + ((size_t)m * KB + kb) * GemvFmt<QT_Q5K>::REC;
+      const float2 s2 = *(const float2*)(r + 2 * C);
+      const float2 t2 = *(const float2*)(r + 8 + 2 * C);
+      X[m] = fmaf(sc0, s2.x * (float)S0, X[m]);
+      X[m] = fmaf(sc1, s2.y * (float)S1, X[m]);
+      Z[m] = fmaf(mn0, t2.x, Z[m]);
+      Z[m] = fmaf(mn1, t2.y, Z[m]);
+    }
+  };
+  pair(std::integral_constant<int, 0>{});
+  pair(std::integral_constant<int, 1>{});
+  pair(std::integral_constant<int, 2>{});
+  pair(std::integral_constant<int, 3>{});
+#pragma unroll
+  for (int m = 0; m < MR; ++m) part[m] += d * X[m] - dmin * Z[m];
+}
+
+// Q6_K block -> part[m]: ql (32 words), qh (16 words), sc (4 words), d bits.
+template <int MR>
+__device__ __forceinline__ void q6k_block(const uint32_t* ql, const uint32_t* qh, uint4 scv,
+                                          uint32_t dbits, int kb, int K, const uint8_t* smem,
+                                          const uint32_t* rec, int KB, float* part) {
+  const float d = h2f(dbits);
+  const uint32_t scw[4] = {scv.x, scv.y, scv.z, scv.w};
+  float X[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) X[m] = 0.f;
+  auto unit = [&](auto hh, auto aa) {
+    constexpr int H = decltype(hh)::value, A_ = decltype(aa)::value;
+    uint32_t lo[8], hi[8];
+    q6k_codes<H, A_>(ql, qh, lo, hi);
+    constexpr int s0 = 8 * H + 2 * A_;           // sub-blocks s0, s0+1 (lo) and s0+4, s0+5 (hi)
+    const int c0 = sext8(scw[s0 >> 2] >> (8 * (s0 & 3)));
+    const int c1 = sext8(scw[s0 >> 2] >> (8 * ((s0 + 1) & 3)));
+    const int c4 = sext8(scw[(s0 + 4) >> 2] >> (8 * ((s0 + 4) & 3)));
+    const int c5 = sext8(scw[(s0 + 5) >> 2] >> (8 * ((s0 + 5) & 3)));
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const uint4 a0 = *(const uint4*)(smem + qa_chunk(m, K, kb, s0));
+      const uint4 a1 = *(const uint4*)(smem + qa_chunk(m, K, kb, s0 + 1));
+      const uint4 a4 = *(const uint4*)(smem + qa_chunk(m, K, kb, s0 + 4));
+      const uint4 a5 = *(const uint4*)(smem + qa_chunk(m, K, kb, s0 + 5));
+      const uint32_t* r = rec + ((size_t)m * KB + kb) * GemvFmt<QT_Q6K>::REC;
+      const int2 tl = *(const int2*)(r + 8 + s0);
+      const int2 th = *(const int2*)(r + 8 + s0 + 4);
+      const int S0 = dot16u(lo, a0) - 32 * tl.x;
+      const int S1 = dot16u(lo + 4, a1) - 32 * tl.y;
+      const int S4 = dot16u(hi, a4) - 32 * th.x;
+      const int S5 = dot16u(hi + 4, a5) - 32 * th.y;
+      const int I = __mul24(c0, S0) + __mul24(c1, S1);
+      const int J = __mul24(c4, S4) + __mul24(c5, S5);
+      const float sI = __builtin_bit_cast(float, r[s0 >> 1]);
+      const float sJ = __builtin_bit_cast(float, r[(s0 + 4) >> 1]);
+      X[m] = fmaf(sI, (float)I, X[m]);
+      X[m] = fmaf(sJ, (float)J, X[m]);
+    }
+  };
+  unit(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+  unit(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+  unit(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  unit(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+#pragma unroll
+  for (int m = 0; m < MR; ++m) part[m] += d * X[m];
+}
+
+// ------------------------------------------------------------- staging ----
+// One round = local blocks [64r, 64r + nb) of the wave's range, nb <= 64.
+// Q5_K: the round's bytes are contiguous; chunk c lands in slot c, so lane b
+// reads its block at slots 11b .. 11b+10 (stride 11 is odd: no bank conflict).
+// Q6_K: QL (8 chunks/block) and QH (4 chunks/block) each contiguous; a lane
+// fetches the chunk that belongs in its fixed slot, with the chunks of a
+// block XOR-permuted so that the 16 lanes of a read phase hit 16 distinct
+// 16-byte bank groups.
+
+__device__ __forceinline__ int q6k_ql_slot(int b, int f) {       // b: local block, f: chunk 0..7
+  return 8 * b + (f ^ (((b & 7) >> 1) | (((b >> 3) & 1) << 2)));
+}
+__device__ __forceinline__ int q6k_qh_slot(int b, int f) {       // f: chunk 0..3
+  return 4 * b + (f ^ ((b >> 2) & 3));
+}
+
+__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Every lane issues every load (no branches, so the wait-count bookkeeping
+// after it stays exact): lanes past the round's blocks re-read the round's
+// first chunk into a slot that no lane reads back.  With nb == 0 (a wave
+// without rows) gb0 must point at a valid block (the caller passes 0).
+template <int QT>
+__device__ __forceinline__ void stage_round(const uint8_t* __restrict__ W, size_t nblk, size_t gb0,
+                                            int nb, uint8_t* stage, int lane, uint4& scv,
+                                            uint32_t& dbits) {
+  if constexpr (QT == QT_Q5K) {
+    const uint8_t* src = W + gb0 * Q5K_BYTES;
+    const int nchunks = nb * 11;
+#pragma unroll
+    for (int i = 0; i < 11; ++i) {
+      const int c = 64 * i + lane;
+      lds_dma16(src + 16 * (c < nchunks ? c : 0), stage + 1024 * i);
+    }
+  } else {
+    const uint8_t* ql = W + gb0 * 128;
+    const uint8_t* qh = W + 128 * nblk + gb0 * 64;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {          // QL: 8 blocks per instruction
+      const int slot = 64 * i + lane;      // = 8b + f'
+      const int b = slot >> 3, fp = slot & 7;
+      const int f = fp ^ (((b & 7) >> 1) | (((b >> 3) & 1) << 2));
+      lds_dma16(b < nb ? ql + 128 * b + 16 * f : ql, stage + 1024 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {          // QH: 16 blocks per instruction
+      const int slot = 64 * i + lane;      // = 4b + f'
+      const int b = slot >> 2, fp = slot & 3;
+      const int f = fp ^ ((b >> 2) & 3);
+      lds_dma16(b < nb ? qh + 64 * b + 16 * f : qh, stage + 8192 + 1024 * i);
+    }
+    // the lane's own block scales and d go straight to registers
+    const size_t gb = gb0 + (lane < nb ? lane : 0);
+    scv = *(const uint4*)(W + 192 * nblk + 16 * gb);
+    dbits = *(const uint16_t*)(W + 208 * nblk + 2 * gb);
+  }
+}
+
+// Workgroup barrier for the quantiser waves: their LDS writes complete
+// (lgkmcnt(0)) before they arrive.  (s_waitcnt immediate, gfx9 encoding:
+// vmcnt 63, expcnt 7, lgkmcnt 0.)
+__device__ __forceinline__ void barrier_after_lds_writes() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for the worker waves: they have written nothing that
+// other waves read, so they arrive without waiting for their own in-flight
+// global->LDS weight loads (those land in the wave's private staging slice).
+__device__ __forceinline__ void barrier_no_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_all_and_sync_wave() {
+  __builtin_amdgcn_s_waitcnt(0);        // vmcnt = expcnt = lgkmcnt = 0
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------- kernel --
+
+// Workgroup = GEMV_WAVES worker waves + NQ quantiser waves.  The workers
+// issue their weight loads and go straight to the barrier; the quantiser
+// waves issue no weight loads, so their activation loads return from L2 and
+// the quantisation completes while the weights are still in flight.
+template <int QT, int MR, int V>
+__global__ void __launch_bounds__(512)
+gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__ R,
+            f16* __restrict__ Y, int N, int K, int rows_per_wave) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ __align__(16) uint8_t stage_all[GEMV_WAVES * GemvFmt<QT>::STAGE];
+  const GemvLayout L = gemv_layout<QT>(MR, K);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int KB = K / QK;
+  const size_t nblk = (size_t)N * KB;
+
+  if (wave >= GEMV_WAVES) {
+    // quantiser waves
+    quantise_to_lds<QT, MR>(A, K, smem, (int)threadIdx.x - 64 * GEMV_WAVES,
+                            (int)blockDim.x - 64 * GEMV_WAVES);
+    barrier_after_lds_writes();
+    return;
+  }
+
+  const int n_w = (blockIdx.x * GEMV_WAVES + wave) * rows_per_wave;
+  int rows_w = N - n_w;
+  rows_w = rows_w < 0 ? 0 : (rows_w > rows_per_wave ? rows_per_wave : rows_w);
+  const int nb_w = rows_w * KB;                       // blocks of this wave
+  const size_t gb_w = (size_t)n_w * KB;               // its first block
+  uint8_t* stage = stage_all + (size_t)wave * GemvFmt<QT>::STAGE;
+  float* part_lds = (float*)(smem + L.part) + (size_t)wave * MR * 64;
+
+  // the first round of this wave's weight blocks -> its LDS slice
+  uint4 scv = make_uint4(0, 0, 0, 0);   // Q6_K: the lane's block scales and d
+  uint32_t dbits = 0;
+  stage_round<QT>(W, nblk, nb_w > 0 ? gb_w : 0, nb_w < 64 ? nb_w : 64, stage, lane, scv, dbits);
+  barrier_no_wait();                                  // quantised activations ready
+
+  const uint32_t* rec = (const uint32_t*)(smem + L.rec);
+  float part[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) part[m] = 0.f;
+  const int rounds = (nb_w + 63) / 64;
+  for (int r = 0; r < rounds; ++r) {
+    const int nb = nb_w - 64 * r < 64 ? nb_w - 64 * r : 64;
+    if (r > 0) stage_round<QT>(W, nblk, gb_w + 64 * r, nb, stage, lane, scv, dbits);
+    wait_all_and_sync_wave();
+    const int j = 64 * r + lane;                      // local block index
+    if (lane < nb) {
+      const int kb = j % KB;
+      if constexpr (QT == QT_Q5K) {
+        uint32_t blk[44];
+        const uint8_t* src = stage + 176 * lane;
+#pragma unroll
+        for (int c = 0; c < 11; ++c) {
+          const uint4 v = *(const uint4*)(src + 16 * c);
+          blk[4 * c] = v.x; blk[4 * c + 1] = v.y; blk[4 * c + 2] = v.z; blk[4 * c + 3] = v.w;
+        }
+        q5k_block<MR>(blk, kb, K, smem, rec, KB, part);
+      } else {
+        uint32_t ql[32], qh[16];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          const uint4 v = *(const uint4*)(stage + 16 * q6k_ql_slot(lane, f));
+          ql[4 * f] = v.x; ql[4 * f + 1] = v.y; ql[4 * f + 2] = v.z; ql[4 * f + 3] = v.w;
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const uint4 v = *(const uint4*)(stage + 8192 + 16 * q6k_qh_slot(lane, f));
+          qh[4 * f] = v.x; qh[4 * f + 1] = v.y; qh[4 * f + 2] = v.z; qh[4 * f + 3] = v.w;
+        }
+        q6k_block<MR>(ql, qh, scv, dbits, kb, K, smem, rec, KB, part);
+      }
+    }
+    // rows longer than 64 blocks (one row per wave): keep accumulating; the
+    // staging slice is reused only after every lane's reads have returned
+    if (r + 1 < rounds) wait_all_and_sync_wave();
+  }
+  // row sums in lane order, + R, store
+#pragma unroll
+  for (int m = 0; m < MR; ++m) part_lds[m * 64 + lane] = part[m];
+  wait_all_and_sync_wave();
+  if (lane < rows_w) {
+    const int per = KB < 64 ? KB : 64;                // lanes holding this row's partials
+    const int first = KB < 64 ? lane * KB : 0;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float y = 0.f;
+      for (int i = 0; i < per; ++i) y += part_lds[m * 64 + first + i];
+      const int n = n_w + lane;
+      if (R) y += (float)R[(size_t)m * N + n];
+      Y[(size_t)m * N + n] = (f16)y;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch --
+
+static int gemv_rows_per_wave(int K) {
+  const int KB = K / QK;
+  return KB <= 64 ? 64 / KB : 1;
+}
+
+static int gemv_quant_v(int M, int K) {
+  (void)M; (void)K;
+  return 4;      // 32 values (one group) per quantising lane
+}
+
+// quantiser waves per workgroup: one or two rounds of 32-value tasks per lane
+static int gemv_quant_waves(int M, int K) {
+  const int tasks = M * K / 32;
+  int nq = (tasks + 127) / 128;
+  return nq < 1 ? 1 : (nq > 4 ? 4 : nq);
+}
+
+static constexpr int gemv_static_lds(int qt) {
+  return GEMV_WAVES * (qt == QT_Q5K ? GemvFmt<QT_Q5K>::STAGE : GemvFmt<QT_Q6K>::STAGE);
+}
+
+template <int QT, int MR, int V>
+static hipError_t launch_gemv_t(const uint8_t* W, const f16* A, const f16* R, f16* Y, int N, int K,
+                                hipStream_t st) {
+  const size_t lds = gemv_layout<QT>(MR, K).dyn;   // plus the kernel's static staging
+  if (gemv_layout<QT>(MR, K).total > 160 * 1024) return hipErrorInvalidValue;
+  auto kern = gemv_kernel<QT, MR, V>;
+  // raise the dynamic-LDS limit once per instantiation, to what the CU's
+  // 160 KB leaves beside the kernel's static staging
+  static bool attr_set = false;
+  if (lds > 65536 && !attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024 - gemv_static_lds(QT));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int rpw = gemv_rows_per_wave(K);
+  const int rows_wg = GEMV_WAVES * rpw;
+  const int grid = (N + rows_wg - 1) / rows_wg;
+  const int threads = 64 * (GEMV_WAVES + gemv_quant_waves(MR, K));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, W, A, R, Y, N, K, rpw);
+  return hipGetLastError();
+}
+
+template <int QT, int MR>
+static hipError_t launch_gemv_m(const uint8_t* W, const f16* A, const f16* R, f16* Y, int N, int K,
+                                hipStream_t st) {
+  switch (gemv_quant_v(MR, K)) {
+    case 1: return launch_gemv_t<QT, MR, 1>(W, A, R, Y, N, K, st);
+    case 2: return launch_gemv_t<QT, MR, 2>(W, A, R, Y, N, K, st);
+    default: return launch_gemv_t<QT, MR, 4>(W, A, R, Y, N, K, st);
+  }
+}
+
+template <int QT>
+static hipError_t launch_gemv_q(const uint8_t* W, const f16* A, const f16* R, f16* Y, int M, int N,
+                                int K, hipStream_t st) {
+  switch (M) {
+    case 1: return launch_gemv_m<QT, 1>(W, A, R, Y, N, K, st);
+    case 2: return launch_gemv_m<QT, 2>(W, A, R, Y, N, K, st);
+    case 3: return launch_gemv_m<QT, 3>(W, A, R, Y, N, K, st);
+    case 4: return launch_gemv_m<QT, 4>(W, A, R, Y, N, K, st);
+    case 5: return launch_gemv_m<QT, 5>(W, A, R, Y, N, K, st);
+    case 6: return launch_gemv_m<QT, 6>(W, A, R, Y, N, K, st);
+    default: return launch_gemv_m<QT, 7>(W, A, R, Y, N, K, st);
+  }
+}
+
+size_t gemv_lds_bytes(int qtype, int M, int K) {
+  return qtype == QT_Q5K ? gemv_layout<QT_Q5K>(M, K).total : gemv_layout<QT_Q6K>(M, K).total;
+}
+
+hipError_t launch_gemv(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, int M,
+                       int N, int K, hipStream_t st) {
+  if (qtype == QT_Q5K) return launch_gemv_q<QT_Q5K>(W, A, R, Y, M, N, K, st);
+  return launch_gemv_q<QT_Q6K>(W, A, R, Y, M, N, K, st);
+}
+
+// --------------------------------------------------------------- debug ----
+
+// The decode path's quantisation routine (the same quant_lane<V> that the
+// GEMV uses for this M, K), written out unswizzled to global memory.
+template <int V>
+__global__ void debug_quantize_kernel(const f16* __restrict__ A, int M, int K, int8_t* qa, float* s,
+                                      int* T) {
+  constexpr int LPG = 4 / V;
+  const int tasks = M * K / (8 * V);
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;   // whole groups per block
+  uint4 raw[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+    raw[i] = t < tasks ? *(const uint4*)(A + (size_t)t * 8 * V + 8 * i) : make_uint4(0, 0, 0, 0);
+  uint32_t q[2 * V];
+  float sc;
+  int tsum, thalf[2];
+  quant_lane<V>(raw, q, sc, tsum, thalf);
+  if (t >= tasks) return;
+#pragma unroll
+  for (int i = 0; i < 2 * V; ++i) ((uint32_t*)qa)[(size_t)t * 2 * V + i] = q[i];
+  if ((t % LPG) == 0) {
+    s[t / LPG] = sc;
+    T[t / LPG] = tsum;
+  }
+}
+
+hipError_t launch_debug_quantize(const f16* A, int M, int K, int8_t* qa, float* s, int* T,
+                                 hipStream_t st) {
+  const int V = gemv_quant_v(M, K);
+  const long long tasks = (long long)M * K / (8 * V);
+  const unsigned grid = (unsigned)((tasks + 255) / 256);
+  if (V == 1) hipLaunchKernelGGL(debug_quantize_kernel<1>, dim3(grid), dim3(256), 0, st, A, M, K, qa, s, T);
+  else if (V == 2) hipLaunchKernelGGL(debug_quantize_kernel<2>, dim3(grid), dim3(256), 0, st, A, M, K, qa, s, T);
+  else hipLaunchKernelGGL(debug_quantize_kernel<4>, dim3(grid), dim3(256), 0, st, A, M, K, qa, s, T);
+  return hipGetLastError();
+}
+
+// Integer sub-block sums with the GEMV's code routines: one thread per block
+// (n, kb), blocks read straight from global memory (Q5_K AoS / Q6_K planes).
+template <int QT>
+__global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ qa,
+                                      int M, int N, int K, int* __restrict__ S) {
+  const int KB = K / QK;
+  const long long gb = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gb >= (long long)N * KB) return;
+  const int n = (int)(gb / KB), kb = (int)(gb % KB);
+  const size_t nblk = (size_t)N * KB;
+  const uint4 ones = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+  if constexpr (QT == QT_Q5K) {
+    uint32_t blk[44];
+    const uint4* src = (const uint4*)(W + (size_t)gb * Q5K_BYTES);
+#pragma unroll
+    for (int c = 0; c < 11; ++c) {
+      const uint4 v = src[c];
+      blk[4 * c] = v.x; blk[4 * c + 1] = v.y; blk[4 * c + 2] = v.z; blk[4 * c + 3] = v.w;
+    }
+    const int ns = K / 32;
+    for (int m = 0; m < M; ++m) {
+      const uint4* a = (const uint4*)(qa + (size_t)m * K + kb * QK);
+      int* out = S + ((size_t)m * N + n) * ns + kb * 8;
+      auto pair = [&](auto cc) {
+        constexpr int C = decltype(cc)::value;
+        uint32_t lo[8], hi[8];
+        q5k_codes<C>(blk + 4, blk + 12, lo, hi);
+        out[2 * C] = dot16u(lo, a[4 * C]) + dot16u(lo + 4, a[4 * C + 1]);
+        out[2 * C + 1] = dot16u(hi, a[4 * C + 2]) + dot16u(hi + 4, a[4 * C + 3]);
+      };
+      pair(std::integral_constant<int, 0>{});
+      pair(std::integral_constant<int, 1>{});
+      pair(std::integral_constant<int, 2>{});
+      pair(std::integral_constant<int, 3>{});
+    }
+  } else {
+    uint32_t ql[32], qh[16];
+    const uint4* pl = (const uint4*)(W + 128 * (size_t)gb);
+    const uint4* ph = (const uint4*)(W + 128 * nblk + 64 * (size_t)gb);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const uint4 v = pl[f];
+      ql[4 * f] = v.x; ql[4 * f + 1] = v.y; ql[4 * f + 2] = v.z; ql[4 * f + 3] = v.w;
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const uint4 v = ph[f];
+      qh[4 * f] = v.x; qh[4 * f + 1] = v.y; qh[4 * f + 2] = v.z; qh[4 * f + 3] = v.w;
+    }
+    const int ns = K / 16;
+    for (int m = 0; m < M; ++m) {
+      const uint4* a = (const uint4*)(qa + (size_t)m * K + kb * QK);
+      int* out = S + ((size_t)m * N + n) * ns + kb * 16;
+      auto unit = [&](auto hh, auto aa) {
+        constexpr int H = decltype(hh)::value, A_ = decltype(aa)::value;
+        constexpr int s0 = 8 * H + 2 * A_;
+        uint32_t lo[8], hi[8];
+        q6k_codes<H, A_>(ql, qh, lo, hi);
+        // 16-value code sums, the quantity the GEMV prologue records
+        const uint32_t* o = (const uint32_t*)&ones;
+        out[s0] = dot16u(lo, a[s0]) - 32 * dot16u(o, a[s0]);
+        out[s0 + 1] = dot16u(lo + 4, a[s0 + 1]) - 32 * dot16u(o, a[s0 + 1]);
+        out[s0 + 4] = dot16u(hi, a[s0 + 4]) - 32 * dot16u(o, a[s0 + 4]);
+        out[s0 + 5] = dot16u(hi + 4, a[s0 + 5]) - 32 * dot16u(o, a[s0 + 5]);
+      };
+      unit(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      unit(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      unit(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+      unit(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    }
+  }
+}
+
+hipError_t launch_debug_int_dots(int qtype, const uint8_t* W, const int8_t* qa, int M, int N, int K,
+                                 int* S, hipStream_t st) {
+  const long long total = (long long)N * (K / QK);
+  const int grid = (int)((total + 255) / 256);
+  if (qtype == QT_Q5K)
+    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q5K>, dim3(grid), dim3(256), 0, st, W, qa, M, N, K, S);
+  else
+    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q6K>, dim3(grid), dim3(256), 0, st, W, qa, M, N, K, S);
+  return hipGetLastError();
+}
+
+}  // namespace fcg

@@ -1,0 +1,34 @@
+// Launchers shared between the kernel translation units and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fcg {
+typedef _Float16 f16;
+
+// Q6_K AoS blocks -> QL | QH | SC | D planes (byte permutation), nblk blocks.
+hipError_t launch_q6k_regroup(const uint8_t* src, uint8_t* dst, size_t nblk, hipStream_t st);
+
+// decode path (M in 1..7)
+size_t gemv_lds_bytes(int qtype, int M, int K);
+hipError_t launch_gemv(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, int M,
+                       int N, int K, hipStream_t st);
+hipError_t launch_debug_quantize(const f16* A, int M, int K, int8_t* qa, float* s, int* T,
+                                 hipStream_t st);
+hipError_t launch_debug_int_dots(int qtype, const uint8_t* W, const int8_t* qa, int M, int N, int K,
+                                 int* S, hipStream_t st);
+
+// prefill path
+void prefill_choose(int qtype, int M, int N, int K, int num_cu, int* mt, int* nt, int* splits);
+size_t prefill_workspace_bytes(int M, int N, int splits);
+hipError_t launch_prefill(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, float* P,
+                          int M, int N, int K, int mt, int nt, int splits, hipStream_t st);
+
+// grouped (MoE) path
+size_t moe_workspace_bytes(int E, int T, int top_k);
+hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, int N, int K,
+                      const f16* A, int T, int a_per_slot, const int32_t* ids, int top_k, f16* Y,
+                      void* ws, int num_cu, hipStream_t st);
+}  // namespace fcg

@@ -1,0 +1,142 @@
+/*
+ * fc_gguf.h -- fully-connected layer computed directly on GGUF K-quant
+ * weight blocks (Q5_K, Q6_K) on an AMD Instinct MI355X (gfx950).
+ *
+ *   Y[M,N] = A[M,K] . W[N,K]^T (+ R[M,N])
+ *
+ * W is never materialised as an f16 matrix: the kernels read the raw
+ * super-blocks.  The operation and its paths follow OpenVINO PR #39119
+ * ("FullyConnectedGGUF"):
+ *   - section "Why a new primitive": GGUF weights are byte rows of
+ *     K/256 * block_bytes, so K must be a multiple of 256;
+ *   - section "Transformation": Q5_K blocks keep their layout; Q6_K blocks
+ *     are regrouped once into the planes QL|QH|SC|D (done on the device at
+ *     create time here);
+ *   - section "Implementation": the path is chosen from the number of
+ *     activation rows M: M < 8 -> per-32 int8 activation quantisation and an
+ *     int8 GEMV; M >= 8 -> each 256-value block decoded once into on-chip
+ *     memory and reused across rows on f16 matrix cores, with a tile that
+ *     grows with M; a same-shape residual Add is fused into the store;
+ *     GPU_GGUF_PREFILL_PATH-style forcing of a path for testing.
+ * The grouped (MoE) entry points follow llama.cpp PR #28301 (Metal
+ * mul_mm_id), section Overview: each expert's routed rows are multiplied by
+ * that expert's weights in one launch, and under-filled row tiles skip their
+ * empty half.
+ *
+ * Conventions for every call:
+ *   - Return value: 0 on success, a negative FC_GGUF_E* code on failure;
+ *     fc_gguf_strerror() describes it.  Nothing is launched on failure.
+ *   - "device" pointers are HIP device memory of the current device;
+ *     "host" pointers are ordinary host memory.
+ *   - f16 is IEEE binary16; all matrices are row-major and contiguous.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  run calls are
+ *     asynchronous and stream-ordered; kernel faults surface at the caller's
+ *     next synchronisation.  A handle owns a workspace, so one handle must not
+ *     be run concurrently on two streams.
+ */
+#ifndef FC_GGUF_H
+#define FC_GGUF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fc_gguf* fc_gguf_t;
+
+/* Quantisation types (this library's own numbering). */
+#define FC_GGUF_Q5_K 5   /* 176 B per 256 values: d, dmin, 12 B scales/mins, qh[32], qs[128] */
+#define FC_GGUF_Q6_K 6   /* 210 B per 256 values: ql[128], qh[64], sc[16] (int8), d */
+
+/* Path override (fc_gguf_set_path; default from env FC_GGUF_PATH=auto|decode|prefill). */
+#define FC_GGUF_PATH_AUTO    0   /* M < 8 -> decode, else prefill */
+#define FC_GGUF_PATH_DECODE  1   /* int8 GEMV for any M (rows taken in chunks of at most 7) */
+#define FC_GGUF_PATH_PREFILL 2   /* f16 matrix-core path for any M >= 1 */
+
+/* Error codes. */
+#define FC_GGUF_OK            0
+#define FC_GGUF_EINVAL       -1  /* NULL handle/pointer, N<=0, K<=0, K%256!=0, M<0, bad top_k ... */
+#define FC_GGUF_EUNSUPPORTED -2  /* unknown qtype or path */
+#define FC_GGUF_ENOMEM       -3  /* device allocation failed */
+#define FC_GGUF_EHIP         -4  /* a HIP runtime call or kernel launch failed */
+#define FC_GGUF_ERANGE       -5  /* a size exceeds an internal limit (e.g. 32-bit indexing) */
+
+/*
+ * Create a handle for one weight matrix W[N,K].
+ *   blocks           u8[N][K/256 * block_bytes] in canonical GGUF AoS order
+ *                    (row n holds its K/256 super-blocks in order).
+ *   blocks_on_device 0: `blocks` is host memory; 1: device memory.
+ * The bytes are copied into library-owned device memory (Q6_K is regrouped
+ * there into QL|QH|SC|D planes), so the caller may free `blocks` as soon as
+ * the call returns.  Synchronous.  *out receives the handle.
+ */
+int fc_gguf_create(int64_t N, int64_t K, int qtype, const void* blocks,
+                   int blocks_on_device, fc_gguf_t* out);
+
+/*
+ * Y = A . W^T (+ R).
+ *   A  device f16[M,K]; R device f16[M,N] or NULL; Y device f16[M,N].
+ *   Y may be the same pointer as R (in-place residual); Y must not overlap A.
+ *   M == 0 is a no-op.  Path per fc_gguf_set_path (default: M<8 -> decode).
+ */
+int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, void* stream);
+
+/* Force a path (FC_GGUF_PATH_*); the testing switch of the FC primitive. */
+int fc_gguf_set_path(fc_gguf_t h, int path);
+
+/* Frees the handle and its device memory; NULL is accepted. Synchronises the device. */
+int fc_gguf_destroy(fc_gguf_t h);
+
+/* N, K, qtype, and the byte size of the device weights of a handle (any may be NULL). */
+int fc_gguf_info(fc_gguf_t h, int64_t* N, int64_t* K, int* qtype, int64_t* weight_bytes);
+
+/*
+ * Grouped (MoE expert) FC: E weight matrices W_e[N,K] of one qtype.
+ *   blocks u8[E][N][K/256 * block_bytes], host or device as in fc_gguf_create.
+ */
+int fc_gguf_create_grouped(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks,
+                           int blocks_on_device, fc_gguf_t* out);
+
+/*
+ * Y[t, j, :] = A_row(t, j) . W_{ids[t,j]}^T for every token t < T and slot j < top_k.
+ *   ids  device i32[T, top_k]: expert ids in [0, E), distinct within a row.
+ *   A    device f16[T, K] when a_per_slot == 0 (row t shared by its slots),
+ *        device f16[T, top_k, K] when a_per_slot == 1 (one row per pair).
+ *   Y    device f16[T, top_k, N], one output row per (token, slot) pair.
+ * No routing weights are applied and nothing is combined.  Ids outside
+ * [0, E) produce zero rows.  T == 0 is a no-op.  Matrix-core numerics
+ * (f16 weights, f32 accumulation) for every expert.
+ */
+int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
+                        const int32_t* ids, int top_k, void* Y, void* stream);
+
+/*
+ * Test exports: they run the same device code as the decode path.
+ *
+ * fc_gguf_debug_quantize: the per-32 int8 activation quantisation of the
+ *   decode path.  A device f16[M,K] (K % 32 == 0); qa device i8[M,K];
+ *   s device f32[M,K/32]; T device i32[M,K/32] (sum of qa per group).
+ *
+ * fc_gguf_debug_int_dots: the integer sub-block dot sums of the decode path,
+ *   from given int8 activations qa device i8[M,K].  S device i32:
+ *   Q5_K [M, N, K/32] (sum of qa*q over each 32-value sub-block, q in [0,31]);
+ *   Q6_K [M, N, K/16] (sum of qa*(q-32) over each 16-value sub-block).
+ *
+ * fc_gguf_debug_weights: copies the handle's device weight bytes (Q5_K AoS
+ *   blocks, or the Q6_K QL|QH|SC|D planes) to device memory `dst`
+ *   (fc_gguf_info's weight_bytes long).
+ */
+int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s,
+                           int32_t* T, void* stream);
+int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S, void* stream);
+int fc_gguf_debug_weights(fc_gguf_t h, void* dst, void* stream);
+
+/* Static description of an error code. */
+const char* fc_gguf_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FC_GGUF_H */

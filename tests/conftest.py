@@ -3,6 +3,11 @@ import sys
 
 import pytest
 
+try:  # import torch at collection time (slow on a cold box), not inside a timed test
+    import torch  # noqa: F401
+except Exception:  # pragma: no cover
+    pass
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

@@ -1,0 +1,150 @@
+"""GPU parity of the decode path (M < 8) against the CPU oracle.
+
+Bit-exact: the int8 activation quantisation (codes, scales, group sums), the
+integer sub-block dot sums, and the device Q6_K plane regroup.  Outputs: max
+relative error <= 1e-3 against the oracle's exact emulation of the int8 path
+(metric max |y-r| / max(|r|, rms(r))).
+"""
+
+import numpy as np
+import pytest
+
+from gguf_quant_block_amd import synth
+from oracle import fc as ofc
+from oracle import kquant as okq
+from helpers import DECODE_TOL, case, maxrel
+
+pytestmark = pytest.mark.gpu
+
+QTYPES = ["q5_k", "q6_k"]
+
+
+def _dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _fc(w, qtype, N, K):
+    from gguf_quant_block_amd.binding import FcGguf
+    return FcGguf(N, K, qtype, w)
+
+
+# ------------------------------------------------------------ quantisation --
+
+def _special_rows(K):
+    g = np.random.default_rng(5)
+    A = g.standard_normal((6, K)).astype(np.float16)
+    A[0, :32] = 0                                                     # zero group
+    A[1, :32] = np.array([(k - 16) / 16 for k in range(32)])           # exact ties
+    A[2, 32:64] = np.float16(6e-8)                                    # f16 subnormals
+    A[3, 64:96] = np.float16(65504) * np.sign(A[3, 64:96])            # largest f16
+    A[4] *= np.float16(1e-3)
+    A[5, 96:128] = np.float16(-1.0)                                   # constant group
+    return A
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 3072), (7, 8192), (6, 512)])
+def test_quantize_bit_exact(gpu_lib, M, K):
+    from gguf_quant_block_amd.binding import debug_quantize
+    A = synth.normal_f16((M, K), synth.rng(50, K, 1))
+    if M == 6:
+        A = _special_rows(K)
+    qa, s, T = (_host(x) for x in debug_quantize(_dev(A)))
+    qa0, s0, T0 = ofc.quantize_act(A)
+    assert np.array_equal(qa, qa0)
+    assert np.array_equal(s.view(np.uint32), s0.view(np.uint32))
+    assert np.array_equal(T, T0)
+
+
+# ---------------------------------------------------------------- regroup --
+
+@pytest.mark.parametrize("N,K", [(3, 768), (512, 2048)])
+def test_device_regroup_bytes(gpu_lib, N, K):
+    w = synth.q6k_blocks(N, K, synth.rng(51, N, 0))
+    fcg = _fc(w, "q6_k", N, K)
+    got = _host(fcg.debug_weights())
+    assert np.array_equal(got, okq.q6k_regroup(w))
+    w5 = synth.q5k_blocks(N, K, synth.rng(51, N + 1, 0))
+    assert np.array_equal(_host(_fc(w5, "q5_k", N, K).debug_weights()), w5.reshape(-1))
+
+
+# --------------------------------------------------------------- int sums --
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M,N,K", [(1, 512, 2048), (7, 37, 768), (4, 16, 8192)])
+def test_int_dots_bit_exact(gpu_lib, qtype, M, N, K):
+    w, A, _ = case(qtype, M, N, K, 52, M * N, with_r=False)
+    qa, _, _ = ofc.quantize_act(A)
+    S = _host(_fc(w, qtype, N, K).debug_int_dots(_dev(qa)))
+    assert np.array_equal(S.astype(np.int64), ofc.int_dots(qa, w, qtype))
+
+
+# ----------------------------------------------------------------- GEMV ----
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("N,K", [(37, 768), (512, 2048), (100, 3072), (24, 8192)])
+def test_gemv_parity(gpu_lib, qtype, M, N, K):
+    with_r = (M + N) % 2 == 0
+    w, A, R = case(qtype, M, N, K, 53, 100 * M + N, with_r=with_r)
+    y = _host(_fc(w, qtype, N, K)(_dev(A), None if R is None else _dev(R))).astype(np.float64)
+    ref = ofc.fc_ref_int8(A, w, qtype, R)
+    assert maxrel(y, ref) <= DECODE_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_gemv_in_place_residual(gpu_lib, qtype):
+    M, N, K = 3, 64, 512
+    w, A, R = case(qtype, M, N, K, 54, 0)
+    Rd = _dev(R)
+    fcg = _fc(w, qtype, N, K)
+    fcg(_dev(A), Rd, out=Rd)
+    assert maxrel(_host(Rd), ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_forced_decode_for_larger_m(gpu_lib, qtype):
+    M, N, K = 16, 40, 512
+    w, A, R = case(qtype, M, N, K, 55, 0)
+    fcg = _fc(w, qtype, N, K)
+    fcg.set_path("decode")
+    y = _host(fcg(_dev(A), _dev(R)))
+    assert maxrel(y, ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
+
+
+def test_m_zero_is_noop(gpu_lib):
+    import torch
+    w, _, _ = case("q6_k", 1, 32, 256, 56, 0)
+    fcg = _fc(w, "q6_k", 32, 256)
+    Y = torch.full((0, 32), 7.0, dtype=torch.float16, device="cuda")
+    fcg(torch.empty((0, 256), dtype=torch.float16, device="cuda"), out=Y)
+    assert Y.shape == (0, 32)
+
+
+# --------------------------------------- full-size layers, sampled outputs --
+# Phi-3.5-mini layer shapes at the decode row counts; the whole matrix runs on
+# the GPU in the benchmark's launch configuration, and a random sample of
+# output columns is checked against the oracle restricted to those W rows.
+
+FULL = [("q5_k", name, M) for name in synth.PHI35_LAYERS for M in (1, 2, 4, 7)]
+FULL += [("q6_k", name, M) for name in synth.PHI35_LAYERS for M in (1, 4)]
+FULL += [("q6_k", "output", M) for M in (1, 4)]
+
+
+@pytest.mark.parametrize("qtype,name,M", FULL)
+def test_gemv_full_size_sampled(gpu_lib, qtype, name, M):
+    N, K = synth.PHI35_OUTPUT if name == "output" else synth.PHI35_LAYERS[name]
+    with_r = name != "output"
+    cfg = 1 if qtype == "q5_k" else 2
+    w, A, R = case(qtype, M, N, K, cfg, list(synth.PHI35_LAYERS).index(name) if with_r else 9, with_r)
+    y = _host(_fc(w, qtype, N, K)(_dev(A), None if R is None else _dev(R)))
+    cols = np.sort(np.random.default_rng(N + M).choice(N, size=min(N, 192), replace=False))
+    cols = np.unique(np.concatenate([cols, [0, N - 1]]))
+    ref = ofc.fc_ref_int8(A, w[cols], qtype, None if R is None else R[:, cols])
+    assert maxrel(y[:, cols], ref) <= DECODE_TOL

@@ -1,0 +1,97 @@
+"""GPU parity of the prefill path (M >= 8) against the float64 oracle.
+
+Relative Frobenius error <= 2e-3 against Y = A.W^T + R with W decoded exactly.
+Covers every tile step of the M ladder, ragged M and N tails, split-K grids,
+the forced prefill path at M < 8, and the full-size prefill shapes at every
+M on sampled output columns.
+"""
+
+import numpy as np
+import pytest
+
+from gguf_quant_block_amd import synth
+from oracle import fc as ofc
+from oracle import kquant as okq
+from helpers import PREFILL_TOL, case, relfro
+
+pytestmark = pytest.mark.gpu
+
+QTYPES = ["q5_k", "q6_k"]
+
+
+def _dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _fc(w, qtype, N, K):
+    from gguf_quant_block_amd.binding import FcGguf
+    return FcGguf(N, K, qtype, w)
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_small_config_m16(gpu_lib, qtype):
+    # single Q6_K/Q5_K FC N=512 K=2048 at M=16, no residual
+    M, N, K = 16, 512, 2048
+    w, A, _ = case(qtype, M, N, K, 0, 1, with_r=False)
+    y = _host(_fc(w, qtype, N, K)(_dev(A)))
+    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype)) <= PREFILL_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M,N,K", [(8, 80, 256), (37, 200, 768), (130, 384, 1024), (300, 64, 512),
+                                   (64, 128, 2048), (17, 1000, 512)])
+def test_prefill_ragged(gpu_lib, qtype, M, N, K):
+    w, A, R = case(qtype, M, N, K, 60, M * 7 + N)
+    y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
+    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M", [1, 3, 7])
+def test_forced_prefill_for_small_m(gpu_lib, qtype, M):
+    N, K = 96, 768
+    w, A, R = case(qtype, M, N, K, 61, M)
+    fcg = _fc(w, qtype, N, K)
+    fcg.set_path("prefill")
+    y = _host(fcg(_dev(A), _dev(R)))
+    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_prefill_in_place_residual(gpu_lib, qtype):
+    M, N, K = 40, 128, 512
+    w, A, R = case(qtype, M, N, K, 62, 0)
+    Rd = _dev(R)
+    _fc(w, qtype, N, K)(_dev(A), Rd, out=Rd)
+    assert relfro(_host(Rd), ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+
+
+def test_prefill_error_is_f16_sized(gpu_lib):
+    # the error is the expected f16-rounding size, far inside the tolerance
+    M, N, K = 256, 256, 2048
+    w, A, R = case("q6_k", M, N, K, 63, 0)
+    err = relfro(_host(_fc(w, "q6_k", N, K)(_dev(A), _dev(R))), ofc.fc_gguf_ref(A, w, "q6_k", R))
+    assert err < 1e-3
+
+
+# full-size prefill sweep: both qtypes, both weight shapes, every M step;
+# sampled output columns against the oracle restricted to those W rows
+SWEEP = [(q, s, M) for q in QTYPES for s in range(2) for M in synth.PREFILL_MS]
+
+
+@pytest.mark.parametrize("qtype,shape,M", SWEEP)
+def test_prefill_full_size_sampled(gpu_lib, qtype, shape, M):
+    N, K = synth.PREFILL_SHAPES[shape]
+    w, A, R = case(qtype, M, N, K, 3, 10 * shape + synth.PREFILL_MS.index(M))
+    y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
+    cols = np.sort(np.random.default_rng(N + M).choice(N, size=160, replace=False))
+    cols = np.unique(np.concatenate([cols, [0, N - 1]]))
+    ref = ofc.fc_ref(A, okq.dequantize(w[cols], qtype), R[:, cols])
+    assert relfro(y[:, cols], ref) <= PREFILL_TOL
