@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Benchmark of the GGUF K-quant FC library on one MI355X.
+
+Metric: decode GEMV weight GB/s at M = 1 (Q5_K, Phi-3.5-mini layer set), with
+the prefill TFLOPS at M = 512 (Q5_K and Q6_K, [8192, 2048] and [2048, 8192])
+reported beside it.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  * decode: a 32-layer decode sweep, each layer running its four FCs (fused
+    qkv [9216, 3072], o_proj [3072, 3072], fused gate_up [16384, 3072], down
+    [3072, 8192]) on M = 1 f16 activations with the f16 residual fused into
+    the store; per-32 int8 activation quantisation + int8 GEMV.  Every layer
+    has its own copy of the weights in HBM (2.49 GB), so the weights stream
+    from HBM rather than from the 256 MB last-level cache.
+  * prefill: the four prefill FCs at M = 512 (f16 matrix-core path).
+Each phase is captured once as a HIP graph and replayed; HIP events on the
+replay stream time the phases.  `value` is the decode phase's weight bytes /
+decode time.  Weights and activations are resident in HBM before timing.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --pmc-target            (counter-collection target)
+       python bench.py --traffic-summary FETCH_CSV WRITE_CSV
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense f16 matrix cores
+LAYERS = 32
+CPU_LAYERS = 6               # oracle sample: about 10-30 s on one core
+
+
+def gemv_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "common.h"):
+        with open(os.path.join(ROOT, "gguf_quant_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per decode-GEMV launch from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "decode_gemv_q5k_m1_traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemv_source_hash") != gemv_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline():
+    """The CPU oracle (int8-emulating decode reference) on a bounded sample:
+    CPU_LAYERS layers of the Q5_K Phi-3.5-mini layer set at M = 1 (the same
+    weights each layer, as in the GPU sweep), single-threaded NumPy."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:          # pragma: no cover
+        threadpool_limits = None
+    import numpy as np  # noqa: F401
+    from gguf_quant_block_amd import synth
+    from oracle import fc as ofc
+
+    import contextlib
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    total_bytes = 0
+    with ctx:
+        inputs = []
+        for i, (name, (N, K)) in enumerate(synth.PHI35_LAYERS.items()):
+            inputs.append((synth.q5k_blocks(N, K, synth.rng(1, i, synth.TAG_BLOCKS)),
+                           synth.normal_f16((1, K), synth.rng(1, i, synth.TAG_A)),
+                           synth.normal_f16((1, N), synth.rng(1, i, synth.TAG_R))))
+        t0 = time.perf_counter()
+        for _ in range(CPU_LAYERS):
+            for w, A, R in inputs:
+                ofc.fc_ref_int8(A, w, "q5_k", R)
+                total_bytes += w.nbytes
+        dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{CPU_LAYERS} layers of the Q5_K Phi-3.5-mini layer set (qkv, o_proj, gate_up, down) at M=1, "
+                      f"int8-emulating float64 oracle, {total_bytes / 1e6:.1f} MB of weights in {dt:.1f} s"}
+
+
+def pmc_target(dev):
+    """Counter-collection target: the decode GEMVs the benchmark times, plus a
+    plain device copy of 256 MiB whose FETCH_SIZE / WRITE_SIZE readings give
+    the counters' scale factors."""
+    import torch
+    from gguf_quant_block_amd import synth
+    from gguf_quant_block_amd.binding import FcGguf
+    fcs = []
+    for i, (name, (N, K)) in enumerate(synth.PHI35_LAYERS.items()):
+        w = torch.from_numpy(synth.q5k_blocks(N, K, synth.rng(1, i, synth.TAG_BLOCKS))).to(dev)
+        A = torch.from_numpy(synth.normal_f16((1, K), synth.rng(1, i, synth.TAG_A))).to(dev)
+        R = torch.from_numpy(synth.normal_f16((1, N), synth.rng(1, i, synth.TAG_R))).to(dev)
+        Y = torch.empty((1, N), dtype=torch.float16, device=dev)
+        for _ in range(4):
+            fcs.append((FcGguf(N, K, "q5_k", w), A, R, Y))
+    for _ in range(3):
+        for fc, A, R, Y in fcs:
+            fc(A, R, out=Y)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("pmc target done", flush=True)
+
+
+CALIB_BYTES = 256 << 20
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """Turn the two counter passes over --pmc-target into HBM bytes per decode
+    GEMV launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled
+    by what they read for the 256 MiB device copy, then averaged over the GEMV
+    dispatches (the same equal mix of the four shapes that the timed sweep runs)."""
+    import csv
+    from gguf_quant_block_amd import synth
+
+    def read(path, counter):
+        gemv, calib = [], []
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        for r in rows:
+            v = float(r["Counter_Value"]) * 1024.0
+            if "gemv_kernel" in r["Kernel_Name"]:
+                gemv.append((int(r["Grid_Size"]), v))
+            elif "copyBuffer" in r["Kernel_Name"]:
+                calib.append(v)
+        return gemv, calib
+
+    fg, fc = read(fetch_csv, "FETCH_SIZE")
+    wg, wc = read(write_csv, "WRITE_SIZE")
+    # the calibration copies are the last three device copies of the run
+    f_factor = CALIB_BYTES / (sum(fc[-3:]) / 3)
+    w_factor = CALIB_BYTES / (sum(wc[-3:]) / 3)
+    fetch = sum(v for _, v in fg) / len(fg) * f_factor
+    write = sum(v for _, v in wg) / len(wg) * w_factor
+    alg = sum(w_bytes + 2 * K + 4 * N for (N, K), w_bytes in
+              (((N, K), N * (K // 256) * 176) for N, K in synth.PHI35_LAYERS.values())) / len(synth.PHI35_LAYERS)
+    per_grid = {}
+    for (g, fv), (_, wv) in zip(fg, wg):
+        per_grid.setdefault(g, []).append(fv * f_factor + wv * w_factor)
+    rec = {
+        "kernel": "gemv_kernel<Q5_K, M=1>",
+        "workload": "Q5_K decode GEMV at M=1 over the Phi-3.5-mini layer set, equal mix of the four shapes",
+        "gemv_source_hash": gemv_source_hash(),
+        "gemv_dispatches": len(fg),
+        "fetch_factor": round(f_factor, 4),
+        "write_factor": round(w_factor, 4),
+        "hbm_fetch_bytes_per_launch": round(fetch),
+        "hbm_write_bytes_per_launch": round(write),
+        "hbm_bytes_per_launch": round(fetch + write),
+        "algorithmic_bytes_per_launch": round(alg),
+        "traffic_over_algorithmic": round((fetch + write) / alg, 4),
+        "hbm_bytes_per_launch_by_grid": {str(g): round(sum(v) / len(v)) for g, v in sorted(per_grid.items())},
+    }
+    out = os.path.join(ROOT, "profiles", "decode_gemv_q5k_m1_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-target", action="store_true",
+                    help="run the decode sweep eagerly (4 shapes x 4 weight copies x 3 passes) and a "
+                         "256 MiB device copy of known size, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic record from the two counter passes over --pmc-target")
+    args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU; the FC shards along N with no exchange "
+              "(see DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from gguf_quant_block_amd import synth
+    from gguf_quant_block_amd.binding import FcGguf
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.pmc_target:
+        pmc_target(dev)
+        return
+
+    # ---- decode workload: 32 layers x 4 FCs, Q5_K, M = 1, residual fused ----
+    shapes = list(synth.PHI35_LAYERS.items())
+    layer_sets = []
+    decode_weight_bytes = 0
+    decode_alg_bytes = 0
+    base = {}
+    for i, (name, (N, K)) in enumerate(shapes):
+        base[name] = torch.from_numpy(synth.q5k_blocks(N, K, synth.rng(1, i, synth.TAG_BLOCKS))).to(dev)
+    acts = {}
+    for i, (name, (N, K)) in enumerate(shapes):
+        A = torch.from_numpy(synth.normal_f16((1, K), synth.rng(1, i, synth.TAG_A))).to(dev)
+        R = torch.from_numpy(synth.normal_f16((1, N), synth.rng(1, i, synth.TAG_R))).to(dev)
+        Y = torch.empty((1, N), dtype=torch.float16, device=dev)
+        acts[name] = (A, R, Y)
+    for layer in range(LAYERS):
+        fcs = {}
+        for name, (N, K) in shapes:
+            fcs[name] = FcGguf(N, K, "q5_k", base[name])
+            decode_weight_bytes += fcs[name].weight_bytes
+            decode_alg_bytes += fcs[name].weight_bytes + 2 * K + 2 * 2 * N   # weights + A + R + Y
+        layer_sets.append(fcs)
+    decode_launches = LAYERS * len(shapes)
+
+    def decode_pass():
+        for fcs in layer_sets:
+            for name, _ in shapes:
+                A, R, Y = acts[name]
+                fcs[name](A, R, out=Y)
+
+    # ---- prefill workload: M = 512, Q5_K and Q6_K, both weight shapes ----
+    Mp = 512
+    prefill = []
+    prefill_flops = 0
+    for qi, q in enumerate(("q5_k", "q6_k")):
+        for si, (N, K) in enumerate(synth.PREFILL_SHAPES):
+            w = torch.from_numpy(synth.blocks(q, N, K, synth.rng(3, 10 * si + 4, synth.TAG_BLOCKS))).to(dev)
+            fc = FcGguf(N, K, q, w)
+            A = torch.from_numpy(synth.normal_f16((Mp, K), synth.rng(3, 10 * si + 4, synth.TAG_A))).to(dev)
+            R = torch.from_numpy(synth.normal_f16((Mp, N), synth.rng(3, 10 * si + 4, synth.TAG_R))).to(dev)
+            Y = torch.empty((Mp, N), dtype=torch.float16, device=dev)
+            prefill.append((fc, A, R, Y))
+            prefill_flops += 2 * Mp * N * K
+
+    def prefill_pass():
+        for fc, A, R, Y in prefill:
+            fc(A, R, out=Y)
+
+    # eager warm-up (sets kernel attributes, allocates split-K workspaces)
+    decode_pass()
+    prefill_pass()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    graphs = {}
+    for key, fn in (("decode", decode_pass), ("prefill", prefill_pass)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                fn()
+        graphs[key] = g
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        graphs["decode"].replay()
+        graphs["prefill"].replay()
+    torch.cuda.synchronize()
+
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for k in ("decode", "prefill")}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for s in range(args.steps):
+            for k in ("decode", "prefill"):
+                e0, e1 = ev[k][s]
+                e0.record(stream)
+                graphs[k].replay()
+                e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    dec_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev["decode"])
+    pre_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev["prefill"])
+    step_ms = (dec_ms + pre_ms) / args.steps
+    dec_s = dec_ms / 1e3 / args.steps
+    pre_s = pre_ms / 1e3 / args.steps
+    value = decode_weight_bytes / dec_s / 1e9
+    achieved = decode_alg_bytes / dec_s / 1e9
+    prefill_tflops = prefill_flops / pre_s / 1e12
+    traffic = traffic_from_profile()
+
+    line = {
+        "metric": "decode GEMV weight GB/s (M=1); prefill TFLOPS at M=512; Q5_K/Q6_K",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 dot products (decode); f16 in, f32 accumulate (prefill)",
+        "data": "synthetic (seeded blocks; 32 device copies of one Q5_K layer set)",
+        "config": {
+            "workload": "Q5_K decode GEMV, Phi-3.5-mini layer set (qkv 9216x3072, o_proj 3072x3072, "
+                        "gate_up 16384x3072, down 3072x8192), M=1, fused f16 residual, 32-layer sweep",
+            "decode_weight_bytes_per_step": decode_weight_bytes,
+            "decode_launches_per_step": decode_launches,
+            "prefill": "Q5_K and Q6_K, [8192,2048] and [2048,8192], M=512, fused residual",
+        },
+        "decode_us_per_launch": round(dec_s * 1e6 / decode_launches, 3),
+        "prefill_tflops_m512": round(prefill_tflops, 1),
+        "prefill_us_per_launch": round(pre_s * 1e6 / len(prefill), 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_kernel (decode, Q5_K, M=1)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "roofline_prefill": {
+            "bound": "mfma",
+            "kernel": "prefill_kernel (M=512)",
+            "achieved": round(prefill_tflops, 1),
+            "peak": F16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(prefill_tflops / F16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

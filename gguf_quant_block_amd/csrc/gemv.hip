@@ -5,23 +5,24 @@
 // activations per 32 values and takes int8 dot products directly against the
 // blocks; the residual Add is fused into the output store.
 //
-// Work layout (one launch, workgroup = 4 waves):
-//   * A wave owns R = 64 / (K/256) whole rows of W (one row per wave when a
-//     row has more than 64 blocks).  Their blocks are one contiguous byte
-//     range (Q5_K rows) or one range per plane (Q6_K), so the wave stages 64
-//     blocks at a time into its LDS slice with fully coalesced 16-byte
-//     global->LDS loads (global_load_lds_dwordx4), then every lane reads back
-//     and decodes ONE whole super-block with compile-time field offsets.
-//   * The activation loads are issued first, the staging loads second, and
-//     the workgroup quantises the M x K activations into LDS while the
-//     weights are in flight: int8 codes (16-byte chunks XOR-swizzled by the
-//     block index so lanes on different blocks hit different banks) and a
-//     per-(row, block) record of the f32 group scales s and the code sums
-//     the scale algebra needs (Q5_K: s*T per 32-group for the min term;
-//     Q6_K: 16-value sums for the -32 offset).
-//   * v_dot4_i32_i8 integer sums per sub-block, the scales applied in f32,
-//     the per-lane partials of a row summed in lane order (deterministic),
-//     plus R, rounded once to f16.
+// Work layout (one launch; workgroup = 4 worker waves + 1..4 quantiser waves):
+//   * A worker wave owns R = 64 / (K/256) whole rows of W (one row per wave
+//     when a row has more than 64 blocks).  Each lane owns ONE whole
+//     super-block: it issues the loads of that block's bytes straight into
+//     registers (Q5_K: 11 x 16 B of the row's contiguous range; Q6_K: the
+//     block's slice of each plane) and goes to the workgroup barrier without
+//     waiting for them.
+//   * The quantiser waves issue no weight loads.  They quantise the M x K
+//     activations into LDS while the weights are in flight: int8 codes
+//     (16-byte chunks XOR-swizzled by the block index so lanes on different
+//     blocks hit different banks) and a per-(row, block) record of the f32
+//     group scales s and the code sums the scale algebra needs (Q5_K: s*T per
+//     32-group for the min term; Q6_K: 16-value sums for the -32 offset).
+//   * After the barrier each worker lane decodes its block with compile-time
+//     field offsets, takes v_dot4_i32_i8 integer sums per sub-block, applies
+//     the scales in f32; the per-lane partials of a row are summed in lane
+//     order (deterministic), R is added, and the result is rounded once to
+//     f16.
 #include <type_traits>
 
 #include "common.h"
@@ -37,29 +38,23 @@ constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23: x + magic rounds x to 
 template <int QT> struct GemvFmt;
 template <> struct GemvFmt<QT_Q5K> {
   static constexpr int REC = 20;           // words per (m, kb) record: s[8], s*T[8], pad[4]
-  static constexpr int STAGE = 64 * 176;   // one round of 64 blocks, AoS
 };
 template <> struct GemvFmt<QT_Q6K> {
   static constexpr int REC = 28;           // s[8], T16[16], pad[4]
-  static constexpr int STAGE = 64 * 192;   // one round: QL (8 KB) | QH (4 KB)
 };
 
 struct GemvLayout {
-  size_t rec, part, dyn, total;   // dyn: dynamic LDS bytes; total: dynamic + static staging
+  size_t rec, part, dyn, total;   // dyn == total: all LDS is dynamic
 };
 
-// Dynamic LDS: qa int8 [MR][K] | rec u32 [MR][KB][REC] | part f32 [WAVES][MR][64].
-// The weight staging slices [WAVES][STAGE] are a separate static array, so
-// the compiler can tell the quantisation's LDS writes from the in-flight
-// global->LDS weight loads and does not wait for the latter before the former.
+// LDS: qa int8 [MR][K] | rec u32 [MR][KB][REC] | part f32 [WAVES][MR][64].
 template <int QT>
 __host__ __device__ constexpr GemvLayout gemv_layout(int MR, int K) {
   const size_t qa = (size_t)MR * K;
   const size_t rec = qa;
   const size_t part = rec + (size_t)MR * (K / QK) * GemvFmt<QT>::REC * 4;
-  const size_t dyn = part + (size_t)GEMV_WAVES * MR * 64 * 4;
-  const size_t total = dyn + (size_t)GEMV_WAVES * GemvFmt<QT>::STAGE;
-  return GemvLayout{rec, part, dyn, total};
+  const size_t total = part + (size_t)GEMV_WAVES * MR * 64 * 4;
+  return GemvLayout{rec, part, total, total};
 }
 
 // byte offset of the 16-byte code chunk t (0..15) of block kb in row m
@@ -351,66 +346,6 @@ __device__ __forceinline__ void q6k_block(const uint32_t* ql, const uint32_t* qh
   for (int m = 0; m < MR; ++m) part[m] += d * X[m];
 }
 
-// ------------------------------------------------------------- staging ----
-// One round = local blocks [64r, 64r + nb) of the wave's range, nb <= 64.
-// Q5_K: the round's bytes are contiguous; chunk c lands in slot c, so lane b
-// reads its block at slots 11b .. 11b+10 (stride 11 is odd: no bank conflict).
-// Q6_K: QL (8 chunks/block) and QH (4 chunks/block) each contiguous; a lane
-// fetches the chunk that belongs in its fixed slot, with the chunks of a
-// block XOR-permuted so that the 16 lanes of a read phase hit 16 distinct
-// 16-byte bank groups.
-
-__device__ __forceinline__ int q6k_ql_slot(int b, int f) {       // b: local block, f: chunk 0..7
-  return 8 * b + (f ^ (((b & 7) >> 1) | (((b >> 3) & 1) << 2)));
-}
-__device__ __forceinline__ int q6k_qh_slot(int b, int f) {       // f: chunk 0..3
-  return 4 * b + (f ^ ((b >> 2) & 3));
-}
-
-__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
-// Every lane issues every load (no branches, so the wait-count bookkeeping
-// after it stays exact): lanes past the round's blocks re-read the round's
-// first chunk into a slot that no lane reads back.  With nb == 0 (a wave
-// without rows) gb0 must point at a valid block (the caller passes 0).
-template <int QT>
-__device__ __forceinline__ void stage_round(const uint8_t* __restrict__ W, size_t nblk, size_t gb0,
-                                            int nb, uint8_t* stage, int lane, uint4& scv,
-                                            uint32_t& dbits) {
-  if constexpr (QT == QT_Q5K) {
-    const uint8_t* src = W + gb0 * Q5K_BYTES;
-    const int nchunks = nb * 11;
-#pragma unroll
-    for (int i = 0; i < 11; ++i) {
-      const int c = 64 * i + lane;
-      lds_dma16(src + 16 * (c < nchunks ? c : 0), stage + 1024 * i);
-    }
-  } else {
-    const uint8_t* ql = W + gb0 * 128;
-    const uint8_t* qh = W + 128 * nblk + gb0 * 64;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {          // QL: 8 blocks per instruction
-      const int slot = 64 * i + lane;      // = 8b + f'
-      const int b = slot >> 3, fp = slot & 7;
-      const int f = fp ^ (((b & 7) >> 1) | (((b >> 3) & 1) << 2));
-      lds_dma16(b < nb ? ql + 128 * b + 16 * f : ql, stage + 1024 * i);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {          // QH: 16 blocks per instruction
-      const int slot = 64 * i + lane;      // = 4b + f'
-      const int b = slot >> 2, fp = slot & 3;
-      const int f = fp ^ ((b >> 2) & 3);
-      lds_dma16(b < nb ? qh + 64 * b + 16 * f : qh, stage + 8192 + 1024 * i);
-    }
-    // the lane's own block scales and d go straight to registers
-    const size_t gb = gb0 + (lane < nb ? lane : 0);
-    scv = *(const uint4*)(W + 192 * nblk + 16 * gb);
-    dbits = *(const uint16_t*)(W + 208 * nblk + 2 * gb);
-  }
-}
-
 // Workgroup barrier for the quantiser waves: their LDS writes complete
 // (lgkmcnt(0)) before they arrive.  (s_waitcnt immediate, gfx9 encoding:
 // vmcnt 63, expcnt 7, lgkmcnt 0.)
@@ -441,12 +376,52 @@ __device__ __forceinline__ void wait_all_and_sync_wave() {
 // issue their weight loads and go straight to the barrier; the quantiser
 // waves issue no weight loads, so their activation loads return from L2 and
 // the quantisation completes while the weights are still in flight.
+// The lane's whole super-block, straight from global memory into registers
+// (Q5_K: 11 x 16 B of its AoS block; Q6_K: its QL, QH, SC and D bytes).
+struct GemvBlock {
+  uint32_t w[48];     // Q5_K: the 176 bytes in w[0..43]; Q6_K: ql in w[0..31], qh in w[32..47]
+  uint4 scv;          // Q6_K scales
+  uint32_t dbits;     // Q6_K d
+};
+
+template <int QT>
+__device__ __forceinline__ void load_block(const uint8_t* __restrict__ W, size_t nblk, size_t gb,
+                                           GemvBlock& b) {
+  if constexpr (QT == QT_Q5K) {
+    const uint4* src = (const uint4*)(W + gb * Q5K_BYTES);
+#pragma unroll
+    for (int c = 0; c < 11; ++c) {
+      const uint4 v = src[c];
+      b.w[4 * c] = v.x; b.w[4 * c + 1] = v.y; b.w[4 * c + 2] = v.z; b.w[4 * c + 3] = v.w;
+    }
+  } else {
+    const uint4* ql = (const uint4*)(W + 128 * gb);
+    const uint4* qh = (const uint4*)(W + 128 * nblk + 64 * gb);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const uint4 v = ql[f];
+      b.w[4 * f] = v.x; b.w[4 * f + 1] = v.y; b.w[4 * f + 2] = v.z; b.w[4 * f + 3] = v.w;
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const uint4 v = qh[f];
+      b.w[32 + 4 * f] = v.x; b.w[33 + 4 * f] = v.y; b.w[34 + 4 * f] = v.z; b.w[35 + 4 * f] = v.w;
+    }
+    b.scv = *(const uint4*)(W + 192 * nblk + 16 * gb);
+    b.dbits = *(const uint16_t*)(W + 208 * nblk + 2 * gb);
+  }
+}
+
+// Workgroup = GEMV_WAVES worker waves + NQ quantiser waves.  A worker lane
+// owns one super-block: it issues that block's loads and goes straight to the
+// barrier; the quantiser waves issue no weight loads, so their activation
+// loads return from L2 and the quantisation completes while the weights are
+// still in flight.
 template <int QT, int MR, int V>
 __global__ void __launch_bounds__(512)
 gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__ R,
             f16* __restrict__ Y, int N, int K, int rows_per_wave) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ __align__(16) uint8_t stage_all[GEMV_WAVES * GemvFmt<QT>::STAGE];
   const GemvLayout L = gemv_layout<QT>(MR, K);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int KB = K / QK;
@@ -465,13 +440,11 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
   rows_w = rows_w < 0 ? 0 : (rows_w > rows_per_wave ? rows_per_wave : rows_w);
   const int nb_w = rows_w * KB;                       // blocks of this wave
   const size_t gb_w = (size_t)n_w * KB;               // its first block
-  uint8_t* stage = stage_all + (size_t)wave * GemvFmt<QT>::STAGE;
   float* part_lds = (float*)(smem + L.part) + (size_t)wave * MR * 64;
 
-  // the first round of this wave's weight blocks -> its LDS slice
-  uint4 scv = make_uint4(0, 0, 0, 0);   // Q6_K: the lane's block scales and d
-  uint32_t dbits = 0;
-  stage_round<QT>(W, nblk, nb_w > 0 ? gb_w : 0, nb_w < 64 ? nb_w : 64, stage, lane, scv, dbits);
+  // the lane's first block (lanes without one re-read block 0; never used)
+  GemvBlock blk;
+  load_block<QT>(W, nblk, lane < nb_w ? gb_w + lane : 0, blk);
   barrier_no_wait();                                  // quantised activations ready
 
   const uint32_t* rec = (const uint32_t*)(smem + L.rec);
@@ -480,39 +453,15 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
   for (int m = 0; m < MR; ++m) part[m] = 0.f;
   const int rounds = (nb_w + 63) / 64;
   for (int r = 0; r < rounds; ++r) {
-    const int nb = nb_w - 64 * r < 64 ? nb_w - 64 * r : 64;
-    if (r > 0) stage_round<QT>(W, nblk, gb_w + 64 * r, nb, stage, lane, scv, dbits);
-    wait_all_and_sync_wave();
     const int j = 64 * r + lane;                      // local block index
-    if (lane < nb) {
+    if (r > 0) load_block<QT>(W, nblk, j < nb_w ? gb_w + j : 0, blk);
+    if (j < nb_w) {
       const int kb = j % KB;
-      if constexpr (QT == QT_Q5K) {
-        uint32_t blk[44];
-        const uint8_t* src = stage + 176 * lane;
-#pragma unroll
-        for (int c = 0; c < 11; ++c) {
-          const uint4 v = *(const uint4*)(src + 16 * c);
-          blk[4 * c] = v.x; blk[4 * c + 1] = v.y; blk[4 * c + 2] = v.z; blk[4 * c + 3] = v.w;
-        }
-        q5k_block<MR>(blk, kb, K, smem, rec, KB, part);
-      } else {
-        uint32_t ql[32], qh[16];
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-          const uint4 v = *(const uint4*)(stage + 16 * q6k_ql_slot(lane, f));
-          ql[4 * f] = v.x; ql[4 * f + 1] = v.y; ql[4 * f + 2] = v.z; ql[4 * f + 3] = v.w;
-        }
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const uint4 v = *(const uint4*)(stage + 8192 + 16 * q6k_qh_slot(lane, f));
-          qh[4 * f] = v.x; qh[4 * f + 1] = v.y; qh[4 * f + 2] = v.z; qh[4 * f + 3] = v.w;
-        }
-        q6k_block<MR>(ql, qh, scv, dbits, kb, K, smem, rec, KB, part);
-      }
+      if constexpr (QT == QT_Q5K)
+        q5k_block<MR>(blk.w, kb, K, smem, rec, KB, part);
+      else
+        q6k_block<MR>(blk.w, blk.w + 32, blk.scv, blk.dbits, kb, K, smem, rec, KB, part);
     }
-    // rows longer than 64 blocks (one row per wave): keep accumulating; the
-    // staging slice is reused only after every lane's reads have returned
-    if (r + 1 < rounds) wait_all_and_sync_wave();
   }
   // row sums in lane order, + R, store
 #pragma unroll
@@ -551,22 +500,19 @@ static int gemv_quant_waves(int M, int K) {
   return nq < 1 ? 1 : (nq > 4 ? 4 : nq);
 }
 
-static constexpr int gemv_static_lds(int qt) {
-  return GEMV_WAVES * (qt == QT_Q5K ? GemvFmt<QT_Q5K>::STAGE : GemvFmt<QT_Q6K>::STAGE);
-}
+
 
 template <int QT, int MR, int V>
 static hipError_t launch_gemv_t(const uint8_t* W, const f16* A, const f16* R, f16* Y, int N, int K,
                                 hipStream_t st) {
-  const size_t lds = gemv_layout<QT>(MR, K).dyn;   // plus the kernel's static staging
-  if (gemv_layout<QT>(MR, K).total > 160 * 1024) return hipErrorInvalidValue;
+  const size_t lds = gemv_layout<QT>(MR, K).total;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = gemv_kernel<QT, MR, V>;
-  // raise the dynamic-LDS limit once per instantiation, to what the CU's
-  // 160 KB leaves beside the kernel's static staging
+  // raise the dynamic-LDS limit once per instantiation (to the CU's 160 KB)
   static bool attr_set = false;
   if (lds > 65536 && !attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024 - gemv_static_lds(QT));
+                                       160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
