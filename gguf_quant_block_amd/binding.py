@@ -162,11 +162,15 @@ class FcGguf:
     def grouped(self, A, ids, a_per_slot: bool, out=None):
         """MoE: Y[t, j] = A_row(t, j) . W_{ids[t, j]}^T; A f16 [T, K] or [T, top_k, K]."""
         torch = _torch()
+        assert self.experts is not None, "grouped() needs a handle made with experts=E"
         T, top_k = ids.shape
+        assert ids.is_cuda and A.is_cuda and A.dtype == torch.float16
+        assert A.shape == ((T, top_k, self.K) if a_per_slot else (T, self.K))
         ids = ids.to(torch.int32).contiguous()
         A = A.contiguous()
         if out is None:
             out = torch.empty((T, top_k, self.N), dtype=torch.float16, device=A.device)
+        assert out.is_contiguous() and out.dtype == torch.float16 and out.shape == (T, top_k, self.N)
         _check(lib().fc_gguf_run_grouped(self._h, _ptr(A), T, 1 if a_per_slot else 0, _ptr(ids), top_k,
                                          _ptr(out), _stream()), "fc_gguf_run_grouped")
         return out

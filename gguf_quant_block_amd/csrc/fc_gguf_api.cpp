@@ -139,6 +139,8 @@ int fc_gguf_create(int64_t N, int64_t K, int qtype, const void* blocks, int bloc
 
 int fc_gguf_create_grouped(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks,
                            int blocks_on_device, fc_gguf_t* out) {
+  if (out) *out = nullptr;
+  if (E > fcg::MOE_MAX_E) return FC_GGUF_ERANGE;
   return create_impl(E, N, K, qtype, blocks, blocks_on_device, out);
 }
 

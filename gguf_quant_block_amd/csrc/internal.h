@@ -27,6 +27,7 @@ hipError_t launch_prefill(int qtype, const uint8_t* W, const f16* A, const f16* 
                           int M, int N, int K, int mt, int nt, int splits, hipStream_t st);
 
 // grouped (MoE) path
+constexpr int MOE_MAX_E = 4096;   // experts per grouped handle (bucketing counts live in LDS)
 size_t moe_workspace_bytes(int E, int T, int top_k);
 hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, int N, int K,
                       const f16* A, int T, int a_per_slot, const int32_t* ids, int top_k, f16* Y,

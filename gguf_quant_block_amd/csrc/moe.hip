@@ -1,18 +1,247 @@
-// Grouped (MoE expert) FC: not yet implemented; run_grouped reports
-// FC_GGUF_EUNSUPPORTED until the grouped kernel lands.
+// Grouped (MoE expert) FC on Q5_K / Q6_K blocks: every expert's routed rows
+// times that expert's weights, all experts in one launch.
+//
+// llama.cpp PR #28301 (Metal mul_mm_id), section Overview: the routed rows are
+// grouped by expert, each expert's rows form row tiles against that expert's
+// weight tiles, and a tile whose rows end early skips its empty 16-row half.
+// Numerics are those of the prefill path (OpenVINO PR #39119, section
+// Implementation): weights decoded exactly to f16 once per workgroup, f16
+// matrix cores, f32 accumulation, one f16 rounding at the store.
+//
+// Two launches on the caller's stream:
+//   1. moe_bucket_kernel (one workgroup): counting sort of the (token, slot)
+//      pairs by expert id -> offsets[E+1] and the pair list, then the tile
+//      list: one entry (expert, first row) per BM routed rows of an expert.
+//      Pairs with an id outside [0, E) get zero output rows.
+//   2. moe_grouped_kernel: one workgroup per (tile, weight-row tile); the
+//      grid is sized for the largest possible tile count (known on the host
+//      without reading the routing) and workgroups past the real count exit
+//      at once.  Rows are gathered through the pair list: token t = p / top_k
+//      reads A[t] (shared rows) or A[p] (one row per pair), and writes Y[p].
+// The order of the pairs inside one expert's range is unspecified (atomic
+// cursors); it never changes a result, because every output row depends only
+// on its own activation row and its expert's weights.
 #include "common.h"
 #include "internal.h"
+#include "mfma_tile.h"
 
 namespace fcg {
 
-size_t moe_workspace_bytes(int E, int T, int top_k) {
-  (void)E; (void)T; (void)top_k;
-  return 0;
+constexpr int MOE_BUCKET_THREADS = 1024;
+constexpr int MOE_NT = 2;                  // BN = 128 weight rows per workgroup
+
+// Row tile: 32 rows (two 16-row halves) for sparse routing, 64 once the
+// average expert holds at least 32 rows.
+static int moe_mt(int E, long long P) { return P >= 32LL * E ? 4 : 2; }
+
+static long long moe_max_tiles(int E, long long P, int BM) {
+  return (P + BM - 1) / BM + (E < P ? E : P);
 }
 
-hipError_t launch_moe(int, const uint8_t*, size_t, int, int, int, const f16*, int, int,
-                      const int32_t*, int, f16*, void*, int, hipStream_t) {
-  return hipErrorNotSupported;
+struct MoeWs {
+  int2* tiles;      // [max_tiles] (expert, first row within the expert)
+  int* offsets;     // [E + 1]
+  int* pairs;       // [P] pair index p = t * top_k + j, grouped by expert
+  int* ntiles;      // [1]
+};
+
+static MoeWs moe_ws(void* ws, int E, long long P, long long max_tiles) {
+  MoeWs w;
+  w.tiles = (int2*)ws;
+  w.offsets = (int*)(w.tiles + max_tiles);
+  w.pairs = w.offsets + (E + 1);
+  w.ntiles = w.pairs + P;
+  return w;
+}
+
+size_t moe_workspace_bytes(int E, int T, int top_k) {
+  const long long P = (long long)T * top_k;
+  const long long mt = moe_max_tiles(E, P, 16 * moe_mt(E, P));
+  return (size_t)mt * sizeof(int2) + (size_t)(E + 1 + P + 1) * sizeof(int);
+}
+
+// exclusive scan of one int per thread over the workgroup; returns the
+// thread's prefix and writes the total to *total
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < nw ? wsum[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(s, d, 64);
+      if (lane >= d) s += y;
+    }
+    if (lane < nw) wsum[lane] = s;          // inclusive wave totals
+  }
+  __syncthreads();
+  const int before = wave > 0 ? wsum[wave - 1] : 0;
+  *total = wsum[nw - 1];
+  return before + x - v;
+}
+
+__global__ void __launch_bounds__(MOE_BUCKET_THREADS)
+moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM, int N,
+                  f16* __restrict__ Y, int2* __restrict__ tiles, int* __restrict__ offsets,
+                  int* __restrict__ pairs, int* __restrict__ ntiles) {
+  __shared__ int cnt[MOE_MAX_E];          // rows per expert, then the scatter cursors
+  __shared__ int wsum[2][MOE_BUCKET_THREADS / 64];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += MOE_BUCKET_THREADS) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += MOE_BUCKET_THREADS) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // each thread owns a contiguous run of experts; scan rows and tiles
+  const int per = (E + MOE_BUCKET_THREADS - 1) / MOE_BUCKET_THREADS;
+  const int e0 = tid * per;
+  int rows = 0, tl = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = e0 + q;
+    if (e < E) {
+      rows += cnt[e];
+      tl += (cnt[e] + BM - 1) / BM;
+    }
+  }
+  int rows_total, tiles_total;
+  int rbase = block_exclusive_scan(rows, wsum[0], &rows_total);
+  int tbase = block_exclusive_scan(tl, wsum[1], &tiles_total);
+  for (int q = 0; q < per; ++q) {
+    const int e = e0 + q;
+    if (e >= E) break;
+    const int c = cnt[e];
+    offsets[e] = rbase;
+    for (int r0 = 0; r0 < c; r0 += BM) tiles[tbase++] = make_int2(e, r0);
+    cnt[e] = rbase;                       // becomes the scatter cursor
+    rbase += c;
+  }
+  if (tid == 0) {
+    offsets[E] = rows_total;
+    *ntiles = tiles_total;
+  }
+  __syncthreads();
+
+  for (int p = tid; p < P; p += MOE_BUCKET_THREADS) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) {
+      pairs[atomicAdd(&cnt[e], 1)] = p;
+    } else {
+      f16* y = Y + (size_t)p * N;
+      for (int n = 0; n < N; ++n) y[n] = (f16)0.f;
+    }
+  }
+}
+
+template <int QT, int MT, int NT>
+__global__ void __launch_bounds__(256)
+moe_grouped_kernel(const uint8_t* __restrict__ W, size_t expert_bytes, const f16* __restrict__ A,
+                   f16* __restrict__ Y, const int2* __restrict__ tiles,
+                   const int* __restrict__ offsets, const int* __restrict__ pairs,
+                   const int* __restrict__ ntiles, int N, int K, int top_k, int a_per_slot,
+                   int max_tiles, int tiles_n) {
+  constexpr int BM = 16 * MT;
+  constexpr int BN = 64 * NT;
+  __shared__ __align__(16) f16 As[2][BM * ASTR];
+
+  // XCD-aware remap (round-robin dispatch over 8 XCDs): each XCD takes a
+  // contiguous run of logical items, row tiles fastest, so the row tiles of
+  // one expert against one weight-row tile share an L2.
+  const int Gt = max_tiles * tiles_n;
+  int bid = blockIdx.x;
+  {
+    const int per = Gt / 8, rem = Gt % 8, x = bid % 8, j = bid / 8;
+    bid = x * per + (x < rem ? x : rem) + j;
+  }
+  const int ti = bid % max_tiles;
+  const int nt = bid / max_tiles;
+  if (ti >= *ntiles) return;               // whole workgroup: past the real tile count
+
+  const int2 t = tiles[ti];
+  const int e = t.x;
+  const int base = offsets[e] + t.y;
+  int cnt = offsets[e + 1] - base;
+  if (cnt > BM) cnt = BM;
+  const int mt_act = (cnt + 15) / 16;
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int kq = lane >> 4;
+
+  TileRows<MT> rows;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int r = (tid + 256 * i) >> 4;
+    if (r < cnt) {
+      const int p = pairs[base + r];
+      rows.a_ld[i] = A + (size_t)(a_per_slot ? p : p / top_k) * K;
+    } else {
+      rows.a_ld[i] = nullptr;
+    }
+  }
+
+  floatx4 acc[MT][NT];
+  tile_mainloop<QT, MT, NT>(W + (size_t)e * expert_bytes, (size_t)N * (K >> 8), N, K, n0, 0,
+                            K / KSTAGE, mt_act, rows, As, acc);
+
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int r = 16 * i + (lane & 15);
+    if (r >= cnt) continue;
+    f16* y = Y + (size_t)pairs[base + r] * N;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = n0 + wave * 16 * NT + 16 * j + 4 * kq;
+      if (n < N) store4_f16(y, nullptr, n, N, acc[i][j]);
+    }
+  }
+}
+
+template <int QT, int MT>
+static hipError_t launch_grouped_t(const uint8_t* W, size_t expert_bytes, const f16* A, f16* Y,
+                                   const MoeWs& w, int N, int K, int top_k, int a_per_slot,
+                                   int max_tiles, hipStream_t st) {
+  constexpr int BN = 64 * MOE_NT;
+  const int tiles_n = (N + BN - 1) / BN;
+  const long long grid = (long long)max_tiles * tiles_n;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((moe_grouped_kernel<QT, MT, MOE_NT>), dim3((unsigned)grid), dim3(256), 0, st,
+                     W, expert_bytes, A, Y, w.tiles, w.offsets, w.pairs, w.ntiles, N, K, top_k,
+                     a_per_slot, max_tiles, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, int N, int K,
+                      const f16* A, int T, int a_per_slot, const int32_t* ids, int top_k, f16* Y,
+                      void* ws, int num_cu, hipStream_t st) {
+  (void)num_cu;
+  if (E > MOE_MAX_E) return hipErrorInvalidValue;
+  const long long P = (long long)T * top_k;
+  const int mt = moe_mt(E, P);
+  const int BM = 16 * mt;
+  const long long max_tiles = moe_max_tiles(E, P, BM);
+  const MoeWs w = moe_ws(ws, E, P, max_tiles);
+  hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(MOE_BUCKET_THREADS), 0, st, ids, (int)P, E,
+                     BM, N, Y, w.tiles, w.offsets, w.pairs, w.ntiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (qtype == QT_Q5K) {
+    if (mt == 2) return launch_grouped_t<QT_Q5K, 2>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
+    return launch_grouped_t<QT_Q5K, 4>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
+  }
+  if (mt == 2) return launch_grouped_t<QT_Q6K, 2>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
+  return launch_grouped_t<QT_Q6K, 4>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
 }
 
 }  // namespace fcg

@@ -94,6 +94,7 @@ int fc_gguf_info(fc_gguf_t h, int64_t* N, int64_t* K, int* qtype, int64_t* weigh
 /*
  * Grouped (MoE expert) FC: E weight matrices W_e[N,K] of one qtype.
  *   blocks u8[E][N][K/256 * block_bytes], host or device as in fc_gguf_create.
+ *   1 <= E <= 4096, else FC_GGUF_ERANGE.
  */
 int fc_gguf_create_grouped(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks,
                            int blocks_on_device, fc_gguf_t* out);
@@ -106,7 +107,10 @@ int fc_gguf_create_grouped(int64_t E, int64_t N, int64_t K, int qtype, const voi
  *   Y    device f16[T, top_k, N], one output row per (token, slot) pair.
  * No routing weights are applied and nothing is combined.  Ids outside
  * [0, E) produce zero rows.  T == 0 is a no-op.  Matrix-core numerics
- * (f16 weights, f32 accumulation) for every expert.
+ * (f16 weights, f32 accumulation) for every expert, whatever its row count.
+ * Two kernels on `stream`: the bucketing of the pairs by expert (into the
+ * handle's workspace, grown on first use with hipMalloc) and the grouped FC.
+ * T * top_k <= 2^24.
  */
 int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
                         const int32_t* ids, int top_k, void* Y, void* stream);

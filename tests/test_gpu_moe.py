@@ -1,0 +1,148 @@
+"""GPU parity of the grouped (MoE expert) FC against the float64 oracle.
+
+Relative Frobenius error <= 2e-3, over the whole output and per expert, so a
+bug in a 1-row expert is not hidden by the hot experts.  Covers the 32-row and
+64-row tile variants, experts spanning several ragged tiles, N tails, shared
+and per-pair activation rows, ids outside [0, E), empty experts, T = 0,
+repeat calls (the pair order inside an expert is free, the result must not
+depend on it), and the full-size routed Q6_K expert FCs (128 experts, top-8,
+256 tokens, Zipf 1.1 routing) on sampled experts.
+"""
+
+import numpy as np
+import pytest
+
+from gguf_quant_block_amd import synth
+from oracle import fc as ofc
+from oracle import kquant as okq
+from helpers import PREFILL_TOL, relfro
+
+pytestmark = pytest.mark.gpu
+
+QTYPES = ["q5_k", "q6_k"]
+
+
+def _dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _moe_case(qtype, E, N, K, T, top_k, a_per_slot, cfg, idx, s=1.1):
+    w = synth.blocks(qtype, E * N, K, synth.rng(cfg, idx, synth.TAG_BLOCKS)).reshape(E, N, -1)
+    shape = (T, top_k, K) if a_per_slot else (T, K)
+    A = synth.normal_f16(shape, synth.rng(cfg, idx, synth.TAG_A))
+    ids = synth.moe_routing(T, E, top_k, synth.rng(cfg, idx, synth.TAG_ROUTING), s=s)
+    return w, A, ids
+
+
+def _run(w, qtype, A, ids, a_per_slot, out=None):
+    from gguf_quant_block_amd.binding import FcGguf
+    E, N = w.shape[:2]
+    K = A.shape[-1]
+    fc = FcGguf(N, K, qtype, w, experts=E)
+    return fc, fc.grouped(_dev(A), _dev(ids), a_per_slot, out=out)
+
+
+def _check_experts(y, w, qtype, A, ids, a_per_slot, experts):
+    """Per-expert relative Frobenius error against the oracle on `experts`."""
+    worst = 0.0
+    for e in experts:
+        tt, jj = np.nonzero(ids == e)
+        if tt.size == 0:
+            continue
+        W = okq.dequantize(w[e], qtype)
+        rows = A[tt, jj] if a_per_slot else A[tt]
+        err = relfro(y[tt, jj], ofc.fc_ref(rows, W))
+        assert err <= PREFILL_TOL, f"expert {e} ({tt.size} rows): {err:.3e}"
+        worst = max(worst, err)
+    return worst
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("a_per_slot", [False, True])
+@pytest.mark.parametrize("E,N,K,T,top_k", [
+    (8, 200, 512, 37, 2),      # 32-row tiles, N tail, sparse experts
+    (4, 128, 768, 64, 2),      # 128 pairs over 4 experts: 64-row tiles
+    (16, 96, 256, 90, 4),      # several ragged tiles per hot expert
+    (32, 256, 512, 5, 3),      # more experts than pairs: most experts empty
+])
+def test_moe_small(gpu_lib, qtype, a_per_slot, E, N, K, T, top_k):
+    w, A, ids = _moe_case(qtype, E, N, K, T, top_k, a_per_slot, 40, E * 1000 + T)
+    _, y = _run(w, qtype, A, ids, a_per_slot)
+    y = _host(y)
+    ref = ofc.moe_ref(A, w, qtype, ids, a_per_slot)
+    assert relfro(y, ref) <= PREFILL_TOL
+    _check_experts(y, w, qtype, A, ids, a_per_slot, range(E))
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_moe_single_hot_expert(gpu_lib, qtype):
+    # every token routed to expert 2 in slot 0: one expert spans many tiles
+    E, N, K, T, top_k = 6, 160, 512, 150, 2
+    w, A, ids = _moe_case(qtype, E, N, K, T, top_k, False, 41, 0)
+    ids[:, 0] = 2
+    ids[:, 1] = np.where(ids[:, 1] == 2, 3, ids[:, 1])
+    _, y = _run(w, qtype, A, ids, False)
+    y = _host(y)
+    _check_experts(y, w, qtype, A, ids, False, range(E))
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_moe_invalid_ids_give_zero_rows(gpu_lib, qtype):
+    import torch
+    E, N, K, T, top_k = 8, 64, 256, 20, 2
+    w, A, ids = _moe_case(qtype, E, N, K, T, top_k, False, 42, 0)
+    ids[3, 1] = -1
+    ids[7, 0] = E
+    ids[11, 1] = 1 << 30
+    out = torch.full((T, top_k, N), float("nan"), dtype=torch.float16, device="cuda")
+    _, y = _run(w, qtype, A, ids, False, out=out)
+    y = _host(y)
+    for t, j in [(3, 1), (7, 0), (11, 1)]:
+        assert np.all(y[t, j] == 0)
+    assert np.all(np.isfinite(y))
+    _check_experts(y, w, qtype, A, ids, False, range(E))
+
+
+def test_moe_empty_and_repeat(gpu_lib):
+    import torch
+    qtype = "q6_k"
+    E, N, K, T, top_k = 16, 128, 512, 48, 4
+    w, A, ids = _moe_case(qtype, E, N, K, T, top_k, True, 43, 0)
+    fc, y1 = _run(w, qtype, A, ids, True)
+    y2 = fc.grouped(_dev(A), _dev(ids), True)
+    assert torch.equal(y1, y2)                 # bit-identical whatever the pair order
+    out = torch.zeros((0, top_k, N), dtype=torch.float16, device="cuda")
+    fc.grouped(torch.zeros((0, top_k, K), dtype=torch.float16, device="cuda"),
+               torch.zeros((0, top_k), dtype=torch.int32, device="cuda"), True, out=out)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("which,a_per_slot", [("gate_up", False), ("down", True)])
+def test_moe_full_size_q6k(gpu_lib, which, a_per_slot):
+    """128 experts, top-8, 256 tokens, Zipf(1.1): gate/up [768, 2048] on shared
+    token rows, down [2048, 768] on per-pair rows.  Checked per expert on every
+    multi-tile expert, the 8 smallest non-empty ones and 8 random others."""
+    m = synth.MOE
+    N, K = m[which]
+    E, T, top_k = m["E"], m["T"], m["top_k"]
+    w, A, ids = _moe_case("q6_k", E, N, K, T, top_k, a_per_slot, 4, 0 if which == "gate_up" else 1,
+                          s=m["zipf_s"])
+    _, y = _run(w, "q6_k", A, ids, a_per_slot)
+    y = _host(y)
+    assert np.all(np.isfinite(y))
+    counts = np.bincount(ids.ravel(), minlength=E)
+    nonempty = np.nonzero(counts)[0]
+    hot = nonempty[counts[nonempty] > 32]
+    cold = nonempty[np.argsort(counts[nonempty], kind="stable")[:8]]
+    g = np.random.default_rng(7)
+    rest = np.setdiff1d(nonempty, np.concatenate([hot, cold]))
+    sample = np.unique(np.concatenate([hot, cold, g.choice(rest, size=min(8, rest.size), replace=False)]))
+    assert hot.size >= 4
+    _check_experts(y, w, "q6_k", A, ids, a_per_slot, sample)
