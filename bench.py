@@ -3,7 +3,7 @@
 
 Metric: decode GEMV weight GB/s at M = 1 (Q5_K, Phi-3.5-mini layer set), with
 the prefill TFLOPS at M = 512 (Q5_K and Q6_K, [8192, 2048] and [2048, 8192])
-reported beside it.
+and the MoE grouped-FC rates reported beside it.
 
 One step = one pass of the hot path over one batch of synthetic input:
   * decode: a 32-layer decode sweep, each layer running its four FCs (fused
@@ -13,6 +13,10 @@ One step = one pass of the hot path over one batch of synthetic input:
     has its own copy of the weights in HBM (2.49 GB), so the weights stream
     from HBM rather than from the 256 MB last-level cache.
   * prefill: the four prefill FCs at M = 512 (f16 matrix-core path).
+  * moe: the routed Q6_K expert FCs (128 experts, top-8, 256 tokens, Zipf 1.1
+    routing): expert bucketing + one grouped launch for gate/up [768, 2048]
+    and for down [2048, 768], over 7 weight copies with 7 routings so that
+    the touched expert weights stream from HBM.
 Each phase is captured once as a HIP graph and replayed; HIP events on the
 replay stream time the phases.  `value` is the decode phase's weight bytes /
 decode time.  Weights and activations are resident in HBM before timing.
@@ -38,6 +42,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense f16 matrix cores
 LAYERS = 32
+MOE_COPIES = 7               # 7 x 165 MB per expert FC: the weights stream from HBM
 CPU_LAYERS = 6               # oracle sample: about 10-30 s on one core
 
 
@@ -198,6 +203,7 @@ def main():
               "(see DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -229,8 +235,9 @@ def main():
         fcs = {}
         for name, (N, K) in shapes:
             fcs[name] = FcGguf(N, K, "q5_k", base[name])
-            decode_weight_bytes += fcs[name].weight_bytes
-            decode_alg_bytes += fcs[name].weight_bytes + 2 * K + 2 * 2 * N   # weights + A + R + Y
+            w_bytes = N * (K // 256) * 176                                    # the Q5_K blocks
+            decode_weight_bytes += w_bytes
+            decode_alg_bytes += w_bytes + 2 * K + 2 * 2 * N                   # weights + A + R + Y
         layer_sets.append(fcs)
     decode_launches = LAYERS * len(shapes)
 
@@ -258,14 +265,43 @@ def main():
         for fc, A, R, Y in prefill:
             fc(A, R, out=Y)
 
+    # ---- MoE workload: Q6_K experts, 128 experts, top-8, 256 tokens, Zipf 1.1 ----
+    m = synth.MOE
+    E, T, top_k = m["E"], m["T"], m["top_k"]
+    moe = []
+    moe_touched = moe_alg = moe_flops = 0
+    for c in range(MOE_COPIES):
+        ids_np = synth.moe_routing(T, E, top_k, synth.rng(5, c, synth.TAG_ROUTING), s=m["zipf_s"])
+        ids = torch.from_numpy(ids_np).to(dev)
+        nonempty = int((np.bincount(ids_np.ravel(), minlength=E) > 0).sum())
+        for fi, (which, per_slot) in enumerate((("gate_up", False), ("down", True))):
+            N, K = m[which]
+            w = torch.from_numpy(synth.q6k_blocks(E * N, K, synth.rng(5, 10 * c + fi, synth.TAG_BLOCKS))).to(dev)
+            fc = FcGguf(N, K, "q6_k", w, experts=E)
+            del w
+            shape = (T, top_k, K) if per_slot else (T, K)
+            A = torch.from_numpy(synth.normal_f16(shape, synth.rng(5, 10 * c + fi, synth.TAG_A))).to(dev)
+            Y = torch.empty((T, top_k, N), dtype=torch.float16, device=dev)
+            moe.append((fc, A, ids, per_slot, Y))
+            expert_bytes = N * (K // 256) * 210
+            moe_touched += nonempty * expert_bytes
+            moe_alg += nonempty * expert_bytes + A.numel() * 2 + Y.numel() * 2
+            moe_flops += 2 * T * top_k * N * K
+
+    def moe_pass():
+        for fc, A, ids, per_slot, Y in moe:
+            fc.grouped(A, ids, per_slot, out=Y)
+
     # eager warm-up (sets kernel attributes, allocates split-K workspaces)
     decode_pass()
     prefill_pass()
+    moe_pass()
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
     graphs = {}
-    for key, fn in (("decode", decode_pass), ("prefill", prefill_pass)):
+    phases = (("decode", decode_pass), ("prefill", prefill_pass), ("moe", moe_pass))
+    for key, fn in phases:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             with torch.cuda.graph(g, stream=stream):
@@ -274,17 +310,17 @@ def main():
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        graphs["decode"].replay()
-        graphs["prefill"].replay()
+        for key, _ in phases:
+            graphs[key].replay()
     torch.cuda.synchronize()
 
     ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for k in ("decode", "prefill")}
+              for _ in range(args.steps)] for k, _ in phases}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     with torch.cuda.stream(stream):
         for s in range(args.steps):
-            for k in ("decode", "prefill"):
+            for k, _ in phases:
                 e0, e1 = ev[k][s]
                 e0.record(stream)
                 graphs[k].replay()
@@ -294,7 +330,9 @@ def main():
 
     dec_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev["decode"])
     pre_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev["prefill"])
-    step_ms = (dec_ms + pre_ms) / args.steps
+    moe_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev["moe"])
+    step_ms = (dec_ms + pre_ms + moe_ms) / args.steps
+    moe_s = moe_ms / 1e3 / args.steps
     dec_s = dec_ms / 1e3 / args.steps
     pre_s = pre_ms / 1e3 / args.steps
     value = decode_weight_bytes / dec_s / 1e9
@@ -333,6 +371,23 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+        },
+        "moe": {
+            "workload": "Q6_K experts, 128 experts, top-8, 256 tokens, Zipf(1.1) routing: gate/up [768,2048] "
+                        f"on token rows + down [2048,768] on pair rows, {MOE_COPIES} weight copies and routings "
+                        "in rotation",
+            "touched_weight_gbps": round(moe_touched / moe_s / 1e9, 1),
+            "tflops": round(moe_flops / moe_s / 1e12, 2),
+            "us_per_call": round(moe_s * 1e6 / len(moe), 2),
+        },
+        "roofline_moe": {
+            "bound": "hbm",
+            "kernel": "moe_bucket_kernel + moe_grouped_kernel (Q6_K)",
+            "achieved": round(moe_alg / moe_s / 1e9, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(moe_alg / moe_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": None,
         },
         "roofline_prefill": {
             "bound": "mfma",

@@ -29,7 +29,7 @@ CFLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["fc_gguf_api.cpp", "regroup.hip", "gemv.hip", "prefill.hip", "moe.hip"]
+SOURCES = ["fc_gguf_api.cpp", "layout.hip", "gemv.hip", "prefill.hip", "moe.hip"]
 
 
 def _compile(src: str) -> str:

@@ -10,6 +10,7 @@ typedef _Float16 f16;
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte register chunk
 
 constexpr int QK = 256;          // values per super-block
 constexpr int Q5K_BYTES = 176;   // d, dmin, scales[12], qh[32], qs[128]

@@ -77,8 +77,9 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
   if (!bb) return FC_GGUF_EUNSUPPORTED;
   if (N > kMaxDim || K > kMaxDim || E > 65536) return FC_GGUF_ERANGE;
   const size_t nblk = (size_t)N * (size_t)(K / 256);
-  const size_t expert_bytes = nblk * (size_t)bb;
   if (nblk > ((size_t)1 << 31) / 256) return FC_GGUF_ERANGE;
+  const size_t src_bytes = nblk * (size_t)bb;                        // one canonical matrix
+  const size_t expert_bytes = fcg::layout_bytes(qtype, nblk);        // one device matrix
 
   fc_gguf* h = new (std::nothrow) fc_gguf();
   if (!h) return FC_GGUF_ENOMEM;
@@ -101,23 +102,21 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
     delete h;
     return FC_GGUF_ENOMEM;
   }
-  const hipMemcpyKind kind = on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
-  if (qtype == FC_GGUF_Q5_K) {
-    e = hipMemcpy(h->w, blocks, total, kind);
-  } else {
-    // Q6_K: regroup every expert's blocks into its own QL|QH|SC|D planes.
-    const uint8_t* src = (const uint8_t*)blocks;
-    uint8_t* staging = nullptr;
-    if (!on_device) {
-      e = hipMalloc(&staging, total);
-      if (e == hipSuccess) e = hipMemcpy(staging, blocks, total, hipMemcpyHostToDevice);
-      src = staging;
-    }
-    for (int64_t x = 0; e == hipSuccess && x < E; ++x)
-      e = fcg::launch_q6k_regroup(src + x * expert_bytes, h->w + x * expert_bytes, nblk, nullptr);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (staging) hipFree(staging);
+  // canonical blocks (staged on the device when they come from the host) ->
+  // the device layout, one matrix at a time
+  const uint8_t* src = (const uint8_t*)blocks;
+  uint8_t* staging = nullptr;
+  if (!on_device) {
+    e = hipMalloc(&staging, src_bytes * (size_t)E);
+    if (e == hipSuccess)
+      e = hipMemcpy(staging, blocks, src_bytes * (size_t)E, hipMemcpyHostToDevice);
+    src = staging;
   }
+  for (int64_t x = 0; e == hipSuccess && x < E; ++x)
+    e = fcg::launch_weight_layout(qtype, src + x * src_bytes, h->w + x * expert_bytes, nblk,
+                                  nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (staging) hipFree(staging);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     hipFree(h->w);

@@ -5,28 +5,28 @@
 // activations per 32 values and takes int8 dot products directly against the
 // blocks; the residual Add is fused into the output store.
 //
-// Work layout (one launch; workgroup = 4 worker waves + 1..4 quantiser waves):
-//   * A worker wave owns R = 64 / (K/256) whole rows of W (one row per wave
-//     when a row has more than 64 blocks).  Each lane owns ONE whole
-//     super-block: it issues the loads of that block's bytes straight into
-//     registers (Q5_K: 11 x 16 B of the row's contiguous range; Q6_K: the
-//     block's slice of each plane) and goes to the workgroup barrier without
-//     waiting for them.
-//   * The quantiser waves issue no weight loads.  They quantise the M x K
-//     activations into LDS while the weights are in flight: int8 codes
+// Work layout (one launch; workgroup = 4 waves):
+//   * A wave owns R = 64 / (K/256) whole rows of W (one row per wave when a
+//     row has more than 64 blocks).  Each lane owns ONE whole super-block; in
+//     the device layout (layout.h) the wave's blocks are piece-interleaved,
+//     so each of its 16-byte piece loads is one coalesced access.
+//   * Every thread first issues the activation loads of its quantisation
+//     groups, then its block's weight loads, then quantises (waiting only
+//     for the activation loads, which complete first) into LDS: int8 codes
 //     (16-byte chunks XOR-swizzled by the block index so lanes on different
 //     blocks hit different banks) and a per-(row, block) record of the f32
 //     group scales s and the code sums the scale algebra needs (Q5_K: s*T per
 //     32-group for the min term; Q6_K: 16-value sums for the -32 offset).
-//   * After the barrier each worker lane decodes its block with compile-time
-//     field offsets, takes v_dot4_i32_i8 integer sums per sub-block, applies
-//     the scales in f32; the per-lane partials of a row are summed in lane
-//     order (deterministic), R is added, and the result is rounded once to
-//     f16.
+//     The weights arrive meanwhile.
+//   * After the barrier each lane decodes its block with compile-time field
+//     offsets, takes v_dot4_i32_i8 integer sums per sub-block and applies the
+//     scales in f32; the per-lane partials of a row are summed in lane order
+//     (deterministic), R is added, and the result is rounded once to f16.
 #include <type_traits>
 
 #include "common.h"
 #include "internal.h"
+#include "layout.h"
 
 namespace fcg {
 
@@ -150,11 +150,13 @@ __device__ __forceinline__ void quant_lane(const uint4* raw, uint32_t* q, float&
   tsum = thalf[0] + thalf[1];
 }
 
-// Quantise MR rows of A into the LDS layout, on the workgroup's quantiser
-// waves only: lane ql of nlanes takes tasks ql, ql + nlanes, ... (one 32-value
-// group per task).  The activation loads of the first QPRE rounds are all
-// issued before any is used, so their latencies overlap.
-constexpr int QPRE = 4;
+// Quantisation of MR rows of A into the LDS layout by the whole workgroup:
+// thread tid takes the 32-value groups (tasks) tid, tid + 256, ...  The
+// activation loads of the first QPRE rounds are issued before the weight
+// loads, so the quantisation waits only for them (loads complete in order)
+// while the weights are still in flight.
+constexpr int QPRE = 2;
+constexpr int GEMV_THREADS = 64 * GEMV_WAVES;
 
 template <int QT, int MR>
 __device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4 raw[4], uint8_t* smem,
@@ -184,24 +186,31 @@ __device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4 raw
   }
 }
 
-template <int QT, int MR>
-__device__ __forceinline__ void quantise_to_lds(const f16* A, int K, uint8_t* smem, int ql,
-                                                int nlanes) {
+template <int MR>
+__device__ __forceinline__ void quant_issue(const f16* A, int K, int tid, uint4 (&raw)[QPRE][4]) {
   const int tasks = MR * K / 32;
-  uint32_t* rec = (uint32_t*)(smem + gemv_layout<QT>(MR, K).rec);
-  uint4 raw[QPRE][4];
 #pragma unroll
   for (int r = 0; r < QPRE; ++r) {
-    const int t = r * nlanes + ql;
+    const int t = r * GEMV_THREADS + tid;
     const int tc = t < tasks ? t : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) raw[r][i] = *(const uint4*)(A + (size_t)tc * 32 + 8 * i);
   }
+}
+
+template <int QT, int MR>
+__device__ __forceinline__ void quant_finish(const f16* A, int K, uint8_t* smem, int tid,
+                                             uint4 (&raw)[QPRE][4]) {
+  const int tasks = MR * K / 32;
+  const int wbase = tid & ~63;                        // wave-uniform skip of idle waves
+  uint32_t* rec = (uint32_t*)(smem + gemv_layout<QT>(MR, K).rec);
 #pragma unroll
   for (int r = 0; r < QPRE; ++r)
-    if (r * nlanes < tasks) quantise_task<QT, MR>(r * nlanes + ql, tasks, K, raw[r], smem, rec);
-  for (int t0 = QPRE * nlanes; t0 < tasks; t0 += nlanes) {
-    const int t = t0 + ql;
+    if (r * GEMV_THREADS + wbase < tasks)
+      quantise_task<QT, MR>(r * GEMV_THREADS + tid, tasks, K, raw[r], smem, rec);
+  for (int t0 = QPRE * GEMV_THREADS; t0 < tasks; t0 += GEMV_THREADS) {
+    if (t0 + wbase >= tasks) break;
+    const int t = t0 + tid;
     const int tc = t < tasks ? t : 0;
     uint4 v[4];
 #pragma unroll
@@ -346,21 +355,12 @@ __device__ __forceinline__ void q6k_block(const uint32_t* ql, const uint32_t* qh
   for (int m = 0; m < MR; ++m) part[m] += d * X[m];
 }
 
-// Workgroup barrier for the quantiser waves: their LDS writes complete
-// (lgkmcnt(0)) before they arrive.  (s_waitcnt immediate, gfx9 encoding:
-// vmcnt 63, expcnt 7, lgkmcnt 0.)
+// Workgroup barrier after the quantisation: every wave's LDS writes complete
+// (lgkmcnt(0)) before it arrives, while its weight loads stay in flight.
+// (s_waitcnt immediate, gfx9 encoding: vmcnt 63, expcnt 7, lgkmcnt 0.)
 __device__ __forceinline__ void barrier_after_lds_writes() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier for the worker waves: they have written nothing that
-// other waves read, so they arrive without waiting for their own in-flight
-// global->LDS weight loads (those land in the wave's private staging slice).
-__device__ __forceinline__ void barrier_no_wait() {
-  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -377,63 +377,67 @@ __device__ __forceinline__ void wait_all_and_sync_wave() {
 // waves issue no weight loads, so their activation loads return from L2 and
 // the quantisation completes while the weights are still in flight.
 // The lane's whole super-block, straight from global memory into registers
-// (Q5_K: 11 x 16 B of its AoS block; Q6_K: its QL, QH, SC and D bytes).
+// (Q5_K: its 11 pieces; Q6_K: its QL, QH, SC and D bytes).  In the device
+// layout the lanes of a wave own consecutive blocks, so every piece load of
+// the wave is one or two contiguous runs.
 struct GemvBlock {
   uint32_t w[48];     // Q5_K: the 176 bytes in w[0..43]; Q6_K: ql in w[0..31], qh in w[32..47]
   uint4 scv;          // Q6_K scales
   uint32_t dbits;     // Q6_K d
 };
 
+// The loads are issued in the order the block is consumed (header and fifth
+// bits / scales first, then the code pieces sub-block by sub-block): loads
+// complete in order, so the arithmetic on the first sub-blocks starts while
+// the later pieces are still in flight.  The empty asm statements keep the
+// compiler from reordering the loads.
+#define FCG_KEEP_ORDER() asm volatile("" ::: "memory")
+
 template <int QT>
-__device__ __forceinline__ void load_block(const uint8_t* __restrict__ W, size_t nblk, size_t gb,
-                                           GemvBlock& b) {
+__device__ __forceinline__ void load_block(const uint8_t* W, size_t nbp, size_t gb, GemvBlock& b) {
   if constexpr (QT == QT_Q5K) {
-    const uint4* src = (const uint4*)(W + gb * Q5K_BYTES);
 #pragma unroll
     for (int c = 0; c < 11; ++c) {
-      const uint4 v = src[c];
+      const uint4 v = *(const uint4*)(W + piece_off(gb, 11, c));
       b.w[4 * c] = v.x; b.w[4 * c + 1] = v.y; b.w[4 * c + 2] = v.z; b.w[4 * c + 3] = v.w;
+      FCG_KEEP_ORDER();
     }
   } else {
-    const uint4* ql = (const uint4*)(W + 128 * gb);
-    const uint4* qh = (const uint4*)(W + 128 * nblk + 64 * gb);
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const uint4 v = ql[f];
+    b.scv = *(const uint4*)(W + q6k_sc_base(nbp) + 16 * gb);
+    b.dbits = *(const uint16_t*)(W + q6k_d_base(nbp) + 2 * gb);
+    FCG_KEEP_ORDER();
+    const uint8_t* qh = W + q6k_qh_base(nbp);
+    auto ql_piece = [&](int f) {
+      const uint4 v = *(const uint4*)(W + piece_off(gb, 8, f));
       b.w[4 * f] = v.x; b.w[4 * f + 1] = v.y; b.w[4 * f + 2] = v.z; b.w[4 * f + 3] = v.w;
-    }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint4 v = qh[f];
+      FCG_KEEP_ORDER();
+    };
+    auto qh_piece = [&](int f) {
+      const uint4 v = *(const uint4*)(qh + piece_off(gb, 4, f));
       b.w[32 + 4 * f] = v.x; b.w[33 + 4 * f] = v.y; b.w[34 + 4 * f] = v.z; b.w[35 + 4 * f] = v.w;
-    }
-    b.scv = *(const uint4*)(W + 192 * nblk + 16 * gb);
-    b.dbits = *(const uint16_t*)(W + 208 * nblk + 2 * gb);
+      FCG_KEEP_ORDER();
+    };
+    // consumption order: units (h, a) = (0,0) (0,1) (1,0) (1,1)
+    ql_piece(0); ql_piece(1); qh_piece(0); qh_piece(1);
+    ql_piece(2); ql_piece(3);
+    ql_piece(4); ql_piece(5); qh_piece(2); qh_piece(3);
+    ql_piece(6); ql_piece(7);
   }
 }
 
-// Workgroup = GEMV_WAVES worker waves + NQ quantiser waves.  A worker lane
-// owns one super-block: it issues that block's loads and goes straight to the
-// barrier; the quantiser waves issue no weight loads, so their activation
-// loads return from L2 and the quantisation completes while the weights are
-// still in flight.
+// Workgroup = 4 waves.  Each thread issues its activation loads, then the
+// loads of its lane's super-block, quantises its activation groups into LDS
+// (waiting only for the activation loads) and meets the others at the
+// barrier; the weights arrive while this happens.
 template <int QT, int MR, int V>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(GEMV_THREADS)
 gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__ R,
             f16* __restrict__ Y, int N, int K, int rows_per_wave) {
   extern __shared__ __align__(16) uint8_t smem[];
   const GemvLayout L = gemv_layout<QT>(MR, K);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KB = K / QK;
-  const size_t nblk = (size_t)N * KB;
-
-  if (wave >= GEMV_WAVES) {
-    // quantiser waves
-    quantise_to_lds<QT, MR>(A, K, smem, (int)threadIdx.x - 64 * GEMV_WAVES,
-                            (int)blockDim.x - 64 * GEMV_WAVES);
-    barrier_after_lds_writes();
-    return;
-  }
+  const size_t nbp = padded_blocks((size_t)N * KB);
 
   const int n_w = (blockIdx.x * GEMV_WAVES + wave) * rows_per_wave;
   int rows_w = N - n_w;
@@ -442,10 +446,28 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
   const size_t gb_w = (size_t)n_w * KB;               // its first block
   float* part_lds = (float*)(smem + L.part) + (size_t)wave * MR * 64;
 
+  uint4 araw[QPRE][4];
+  quant_issue<MR>(A, K, tid, araw);
+  // the residual of the row this lane stores (lanes < rows_w), fetched now so
+  // that its latency hides under the weight stream
+  // (unconditional loads from a valid address, so that nothing waits on them
+  // before the weight loads are issued; without R they read A and are unused)
+  f16 rres[MR];
+  {
+    int nr = n_w + lane;
+    nr = nr < N ? nr : N - 1;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) rres[m] = *(R ? R + (size_t)m * N + nr : A);
+  }
+  asm volatile("" ::: "memory");                    // activation and residual loads first
+
   // the lane's first block (lanes without one re-read block 0; never used)
   GemvBlock blk;
-  load_block<QT>(W, nblk, lane < nb_w ? gb_w + lane : 0, blk);
-  barrier_no_wait();                                  // quantised activations ready
+  load_block<QT>(W, nbp, lane < nb_w ? gb_w + lane : 0, blk);
+  asm volatile("" ::: "memory");                    // ... then the weight loads
+
+  quant_finish<QT, MR>(A, K, smem, tid, araw);
+  barrier_after_lds_writes();                         // quantised activations ready
 
   const uint32_t* rec = (const uint32_t*)(smem + L.rec);
   float part[MR];
@@ -454,7 +476,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
   const int rounds = (nb_w + 63) / 64;
   for (int r = 0; r < rounds; ++r) {
     const int j = 64 * r + lane;                      // local block index
-    if (r > 0) load_block<QT>(W, nblk, j < nb_w ? gb_w + j : 0, blk);
+    if (r > 0) load_block<QT>(W, nbp, j < nb_w ? gb_w + j : 0, blk);
     if (j < nb_w) {
       const int kb = j % KB;
       if constexpr (QT == QT_Q5K)
@@ -475,7 +497,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
       float y = 0.f;
       for (int i = 0; i < per; ++i) y += part_lds[m * 64 + first + i];
       const int n = n_w + lane;
-      if (R) y += (float)R[(size_t)m * N + n];
+      if (R) y += (float)rres[m];
       Y[(size_t)m * N + n] = (f16)y;
     }
   }
@@ -492,15 +514,6 @@ static int gemv_quant_v(int M, int K) {
   (void)M; (void)K;
   return 4;      // 32 values (one group) per quantising lane
 }
-
-// quantiser waves per workgroup: one or two rounds of 32-value tasks per lane
-static int gemv_quant_waves(int M, int K) {
-  const int tasks = M * K / 32;
-  int nq = (tasks + 127) / 128;
-  return nq < 1 ? 1 : (nq > 4 ? 4 : nq);
-}
-
-
 
 template <int QT, int MR, int V>
 static hipError_t launch_gemv_t(const uint8_t* W, const f16* A, const f16* R, f16* Y, int N, int K,
@@ -519,8 +532,7 @@ static hipError_t launch_gemv_t(const uint8_t* W, const f16* A, const f16* R, f1
   const int rpw = gemv_rows_per_wave(K);
   const int rows_wg = GEMV_WAVES * rpw;
   const int grid = (N + rows_wg - 1) / rows_wg;
-  const int threads = 64 * (GEMV_WAVES + gemv_quant_waves(MR, K));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, W, A, R, Y, N, K, rpw);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(GEMV_THREADS), lds, st, W, A, R, Y, N, K, rpw);
   return hipGetLastError();
 }
 
@@ -605,14 +617,13 @@ __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_
   const long long gb = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gb >= (long long)N * KB) return;
   const int n = (int)(gb / KB), kb = (int)(gb % KB);
-  const size_t nblk = (size_t)N * KB;
+  const size_t nbp = padded_blocks((size_t)N * KB);
   const uint4 ones = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
   if constexpr (QT == QT_Q5K) {
     uint32_t blk[44];
-    const uint4* src = (const uint4*)(W + (size_t)gb * Q5K_BYTES);
 #pragma unroll
     for (int c = 0; c < 11; ++c) {
-      const uint4 v = src[c];
+      const uint4 v = *(const uint4*)(W + piece_off((size_t)gb, 11, c));
       blk[4 * c] = v.x; blk[4 * c + 1] = v.y; blk[4 * c + 2] = v.z; blk[4 * c + 3] = v.w;
     }
     const int ns = K / 32;
@@ -633,16 +644,14 @@ __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_
     }
   } else {
     uint32_t ql[32], qh[16];
-    const uint4* pl = (const uint4*)(W + 128 * (size_t)gb);
-    const uint4* ph = (const uint4*)(W + 128 * nblk + 64 * (size_t)gb);
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      const uint4 v = pl[f];
+      const uint4 v = *(const uint4*)(W + piece_off((size_t)gb, 8, f));
       ql[4 * f] = v.x; ql[4 * f + 1] = v.y; ql[4 * f + 2] = v.z; ql[4 * f + 3] = v.w;
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const uint4 v = ph[f];
+      const uint4 v = *(const uint4*)(W + q6k_qh_base(nbp) + piece_off((size_t)gb, 4, f));
       qh[4 * f] = v.x; qh[4 * f + 1] = v.y; qh[4 * f + 2] = v.z; qh[4 * f + 3] = v.w;
     }
     const int ns = K / 16;

@@ -19,15 +19,16 @@
 //       magic f16 (1024 + q) from a byte permute, t = fma(1024+q, sc, -1024*sc
 //       [Q6_K: -1056*sc]) = sc*q [sc*(q-32)] exactly, then w = t*d - dmin*m
 //       [Q6_K: t*d] with a single rounding.
-//   * Only the first `mt_act` 16-row halves of the tile run on the matrix
-//     cores: a tile whose rows end early skips its empty halves (llama.cpp
-//     PR #28301, section Overview, skips the empty upper half of under-filled
-//     expert tiles the same way).
+//   * Only the first MTA 16-row halves of the tile are staged and run on the
+//     matrix cores: a tile whose rows end early skips its empty halves
+//     (llama.cpp PR #28301, section Overview, skips the empty upper half of
+//     under-filled expert tiles the same way).
 #pragma once
 
 #include <type_traits>
 
 #include "common.h"
+#include "layout.h"
 
 namespace fcg {
 
@@ -134,22 +135,28 @@ __device__ __forceinline__ void decode_q6k_half(const RawQ6& r, int kq, half8v o
 
 
 // Per-thread view of the tile rows.  Thread tid stages the 16-byte chunks
-// c = tid + 256*i (i < MT) of the activation tile: tile row c >> 4, column
-// chunk c & 15.  a_ld[i] points at that row of A (nullptr: a zero row).
+// c = tid + 256*i (i < MT) of the activation tile: tile row c >> 4 (inside
+// half i), column chunk c & 15.  a_ld[i] points at that row of A; rows past
+// the end of the tile point at any valid row (their outputs are never
+// stored, and an output row depends only on its own activation row).
 template <int MT>
 struct TileRows {
   const f16* a_ld[MT];
 };
 
-// Main loop of one tile over the stages [s_begin, s_end) of K.  W is one
-// weight matrix ([N, K]: Q5_K AoS bytes or Q6_K planes over nblk = N*K/256
-// blocks); n0 its first weight row; acc[i][j] holds C[n][m] of the 16x16
-// sub-tile (activation half i, weight sub-tile j).
-template <int QT, int MT, int NT>
-__device__ __forceinline__ void tile_mainloop(const uint8_t* __restrict__ W, size_t nblk, int N,
-                                              int K, int n0, int s_begin, int s_end, int mt_act,
+// Main loop of one tile over the stages [s_begin, s_end) of K, walked from
+// stage s_begin + rot (wrapping), for the first
+// MTA (<= MT) 16-row halves of the tile.  W is one weight matrix [N, K] in
+// the device layout of layout.h over nbp (padded) blocks; n0 its first
+// weight row (rows past N are clamped to N - 1: loaded, never stored).
+// acc[i][j] receives C[n][m] of the 16x16 sub-tile (half i < MTA, weight
+// sub-tile j).  The loop body has no data-dependent branches.
+template <int QT, int MT, int NT, int MTA>
+__device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int N,
+                                              int K, int n0, int s_begin, int s_end, int rot,
                                               const TileRows<MT>& rows, f16 (*As)[16 * MT * ASTR],
                                               floatx4 (&acc)[MT][NT]) {
+  static_assert(MTA >= 1 && MTA <= MT, "active halves");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4;
@@ -158,85 +165,93 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* __restrict__ W, siz
   // rows of this lane's weight fragments
   int nrow[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) nrow[j] = n0 + wave * 16 * NT + 16 * j + (lane & 15);
+  for (int j = 0; j < NT; ++j) {
+    const int n = n0 + wave * 16 * NT + 16 * j + (lane & 15);
+    nrow[j] = n < N ? n : N - 1;
+  }
 
+  // raw bytes of the lane's rows for stage s (half-block hb of block kb):
+  // 8-byte slices of the 16-byte pieces of the device layout
   auto load_raw_q5 = [&](int s, RawQ5* raw) {
     const int kb = s >> 1, hb = s & 1;
+    const int sub = 8 * (kq & 1), pq = kq >> 1;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      if (nrow[j] < N) {
-        const uint8_t* blk = W + ((size_t)nrow[j] * KB + kb) * Q5K_BYTES;
-        raw[j].hdr = *(const uint4*)blk;
-        raw[j].qsA = *(const uint2*)(blk + 48 + 64 * hb + 8 * kq);
-        raw[j].qsB = *(const uint2*)(blk + 80 + 64 * hb + 8 * kq);
-        raw[j].qh = *(const uint2*)(blk + 16 + 8 * kq);
-      } else {
-        raw[j].hdr = make_uint4(0, 0, 0, 0);
-        raw[j].qsA = raw[j].qsB = raw[j].qh = make_uint2(0, 0);
-      }
+      const size_t b = (size_t)nrow[j] * KB + kb;
+      raw[j].hdr = *(const uint4*)(W + piece_off(b, 11, 0));
+      raw[j].qsA = *(const uint2*)(W + piece_off(b, 11, 3 + 4 * hb + pq) + sub);
+      raw[j].qsB = *(const uint2*)(W + piece_off(b, 11, 5 + 4 * hb + pq) + sub);
+      raw[j].qh = *(const uint2*)(W + piece_off(b, 11, 1 + pq) + sub);
     }
   };
   auto load_raw_q6 = [&](int s, RawQ6* raw) {
     const int kb = s >> 1, hb = s & 1;
+    const int sub = 8 * (kq & 1), pq = kq >> 1;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      if (nrow[j] < N) {
-        const size_t b = (size_t)nrow[j] * KB + kb;
-        raw[j].qlA = *(const uint2*)(W + 128 * b + 64 * hb + 8 * kq);
-        raw[j].qlB = *(const uint2*)(W + 128 * b + 64 * hb + 32 + 8 * kq);
-        raw[j].qh = *(const uint2*)(W + 128 * nblk + 64 * b + 32 * hb + 8 * kq);
-        raw[j].sc = *(const uint2*)(W + 192 * nblk + 16 * b + 8 * hb);
-        raw[j].d = *(const uint16_t*)(W + 208 * nblk + 2 * b);
-      } else {
-        raw[j].qlA = raw[j].qlB = raw[j].qh = raw[j].sc = make_uint2(0, 0);
-        raw[j].d = 0;
-      }
+      const size_t b = (size_t)nrow[j] * KB + kb;
+      raw[j].qlA = *(const uint2*)(W + piece_off(b, 8, 4 * hb + pq) + sub);
+      raw[j].qlB = *(const uint2*)(W + piece_off(b, 8, 4 * hb + 2 + pq) + sub);
+      raw[j].qh = *(const uint2*)(W + q6k_qh_base(nbp) + piece_off(b, 4, 2 * hb + pq) + sub);
+      raw[j].sc = *(const uint2*)(W + q6k_sc_base(nbp) + 16 * b + 8 * hb);
+      raw[j].d = *(const uint16_t*)(W + q6k_d_base(nbp) + 2 * b);
     }
   };
 
-  // activation stage: BM rows x 128 halves = BM*16 chunks of 16 B, MT per thread
-  uint4 areg[MT];
+  // activation stage: 16*MTA rows x 128 halves, MTA chunks of 16 B per thread
+  u32x4 areg[MTA];
   auto load_a = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int col = (tid + 256 * i) & 15;
-      if (rows.a_ld[i])
-        areg[i] = *(const uint4*)(rows.a_ld[i] + (size_t)s * KSTAGE + 8 * col);
-      else
-        areg[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < MTA; ++i)
+      areg[i] = *(const u32x4*)(rows.a_ld[i] + (size_t)s * KSTAGE + 8 * (tid & 15));
   };
   auto store_a = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+    for (int i = 0; i < MTA; ++i) {
       const int c = tid + 256 * i;
-      const int row = c >> 4, col = c & 15;
-      *(uint4*)(&As[buf][row * ASTR + 8 * col]) = areg[i];
+      *(u32x4*)(&As[buf][(c >> 4) * ASTR + 8 * (c & 15)]) = areg[i];
     }
   };
 
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < MTA; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   using Raw = typename std::conditional<QT == QT_Q5K, RawQ5, RawQ6>::type;
   Raw rawc[NT], rawn[NT];
 
-  if (s_begin < s_end) {
-    load_a(s_begin);
-    if constexpr (QT == QT_Q5K) load_raw_q5(s_begin, rawc); else load_raw_q6(s_begin, rawc);
+  // stage t of the loop is stage s_begin + (t + rot) mod nst of K
+  const int nst = s_end - s_begin;
+  auto stage = [&](int t) {
+    int u = t + rot;
+    if (u >= nst) u -= nst;
+    return s_begin + u;
+  };
+  if (nst > 0) {
+    const int s0 = stage(0);
+    load_a(s0);
+    if constexpr (QT == QT_Q5K) load_raw_q5(s0, rawc); else load_raw_q6(s0, rawc);
     store_a(0);
   }
+  // drain the prologue: the loop then starts with no load in flight, and the
+  // waits of its body cover only the loads of the body itself
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int s = s_begin; s < s_end; ++s) {
-    const int buf = (s - s_begin) & 1;
-    const bool more = s + 1 < s_end;
+  for (int t = 0; t < nst; ++t) {
+    const int s = stage(t);
+    const int buf = t & 1;
+    const bool more = t + 1 < nst;
     if (more) {
-      load_a(s + 1);
-      if constexpr (QT == QT_Q5K) load_raw_q5(s + 1, rawn); else load_raw_q6(s + 1, rawn);
+      const int sn = stage(t + 1);
+      load_a(sn);
+      if constexpr (QT == QT_Q5K) load_raw_q5(sn, rawn); else load_raw_q6(sn, rawn);
     }
+    // keep the next stage's loads here, ahead of this stage's work: without
+    // the fence the compiler sinks them to their first use and the prefetch
+    // is lost
+    asm volatile("" ::: "memory");
     // decode this stage's weight fragments: wf[j][g]
     half8v wf[NT][4];
 #pragma unroll
@@ -246,17 +261,15 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* __restrict__ W, siz
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      half8v af[MT];
+      half8v af[MTA];
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        if (i < mt_act)
-          af[i] = *(const half8v*)(&As[buf][(16 * i + (lane & 15)) * ASTR + 32 * g + 8 * kq]);
+      for (int i = 0; i < MTA; ++i)
+        af[i] = *(const half8v*)(&As[buf][(16 * i + (lane & 15)) * ASTR + 32 * g + 8 * kq]);
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        if (i < mt_act)
+      for (int i = 0; i < MTA; ++i)
 #pragma unroll
-          for (int j = 0; j < NT; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j][g], af[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j][g], af[i], acc[i][j], 0, 0, 0);
     }
     if (more) {
       store_a(buf ^ 1);

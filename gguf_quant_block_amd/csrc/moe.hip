@@ -145,7 +145,7 @@ moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM, int N,
 
 template <int QT, int MT, int NT>
 __global__ void __launch_bounds__(256)
-moe_grouped_kernel(const uint8_t* __restrict__ W, size_t expert_bytes, const f16* __restrict__ A,
+moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
                    f16* __restrict__ Y, const int2* __restrict__ tiles,
                    const int* __restrict__ offsets, const int* __restrict__ pairs,
                    const int* __restrict__ ntiles, int N, int K, int top_k, int a_per_slot,
@@ -183,17 +183,21 @@ moe_grouped_kernel(const uint8_t* __restrict__ W, size_t expert_bytes, const f16
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int r = (tid + 256 * i) >> 4;
-    if (r < cnt) {
-      const int p = pairs[base + r];
-      rows.a_ld[i] = A + (size_t)(a_per_slot ? p : p / top_k) * K;
-    } else {
-      rows.a_ld[i] = nullptr;
-    }
+    const int p = pairs[base + (r < cnt ? r : 0)];
+    rows.a_ld[i] = A + (size_t)(a_per_slot ? p : p / top_k) * K;
   }
 
+  // only the halves that hold routed rows run (mt_act is uniform per workgroup)
   floatx4 acc[MT][NT];
-  tile_mainloop<QT, MT, NT>(W + (size_t)e * expert_bytes, (size_t)N * (K >> 8), N, K, n0, 0,
-                            K / KSTAGE, mt_act, rows, As, acc);
+  const uint8_t* We = W + (size_t)e * expert_bytes;
+  const size_t nbp = padded_blocks((size_t)N * (K >> 8));
+  const int S = K / KSTAGE;
+  const int rot = (ti + nt) % S;           // spread concurrent loads over K
+  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else if constexpr (MT == 2) tile_mainloop<QT, MT, NT, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act == 2) tile_mainloop<QT, MT, NT, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act == 3) tile_mainloop<QT, MT, NT, 3>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else tile_mainloop<QT, MT, NT, MT>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
 
 #pragma unroll
   for (int i = 0; i < MT; ++i) {

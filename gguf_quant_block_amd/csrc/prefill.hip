@@ -18,7 +18,7 @@ namespace fcg {
 
 template <int QT, int MT, int NT>
 __global__ void __launch_bounds__(256)
-prefill_kernel(const uint8_t* __restrict__ W, const f16* __restrict__ A, const f16* __restrict__ R,
+prefill_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
                f16* __restrict__ Y, float* __restrict__ P, int M, int N, int K, int tiles_m,
                int tiles_n, int splits, int stages_per_split) {
   constexpr int BM = 16 * MT;
@@ -51,15 +51,19 @@ prefill_kernel(const uint8_t* __restrict__ W, const f16* __restrict__ A, const f
   TileRows<MT> rows;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int m = m0 + ((tid + 256 * i) >> 4);
-    rows.a_ld[i] = m < M ? A + (size_t)m * K : nullptr;
+    int m = m0 + ((tid + 256 * i) >> 4);
+    m = m < M ? m : M - 1;
+    rows.a_ld[i] = A + (size_t)m * K;
   }
-  const int left = M - m0;
-  const int mt_act = left >= BM ? MT : (left + 15) / 16;
 
   floatx4 acc[MT][NT];
-  tile_mainloop<QT, MT, NT>(W, (size_t)N * (K >> 8), N, K, n0, s_begin, s_end, mt_act, rows, As,
-                            acc);
+  // workgroups that share activation rows (or weight rows) start at
+  // different stages of K, so their concurrent loads spread over the memory
+  // channels instead of hitting the same addresses together
+  const int nst = s_end - s_begin;
+  const int rot = nst > 0 ? (nt + mt) % nst : 0;
+  tile_mainloop<QT, MT, NT, MT>(W, padded_blocks((size_t)N * (K >> 8)), N, K, n0, s_begin, s_end, rot, rows, As,
+                                acc);
 
   // epilogue: lane holds C[n = 4*(lane>>4) + r][m = lane & 15] of each 16x16 tile
 #pragma unroll

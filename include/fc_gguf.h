@@ -9,9 +9,10 @@
  * ("FullyConnectedGGUF"):
  *   - section "Why a new primitive": GGUF weights are byte rows of
  *     K/256 * block_bytes, so K must be a multiple of 256;
- *   - section "Transformation": Q5_K blocks keep their layout; Q6_K blocks
- *     are regrouped once into the planes QL|QH|SC|D (done on the device at
- *     create time here);
+ *   - section "Transformation": the weights are converted once; Q6_K blocks
+ *     are regrouped into the planes QL|QH|SC|D (done on the device at create
+ *     time here, where every plane, and the Q5_K blocks, are also
+ *     piece-interleaved over groups of 64 blocks for coalesced wave64 loads);
  *   - section "Implementation": the path is chosen from the number of
  *     activation rows M: M < 8 -> per-32 int8 activation quantisation and an
  *     int8 GEMV; M >= 8 -> each 256-value block decoded once into on-chip
@@ -67,9 +68,10 @@ typedef struct fc_gguf* fc_gguf_t;
  *   blocks           u8[N][K/256 * block_bytes] in canonical GGUF AoS order
  *                    (row n holds its K/256 super-blocks in order).
  *   blocks_on_device 0: `blocks` is host memory; 1: device memory.
- * The bytes are copied into library-owned device memory (Q6_K is regrouped
- * there into QL|QH|SC|D planes), so the caller may free `blocks` as soon as
- * the call returns.  Synchronous.  *out receives the handle.
+ * The bytes are copied into library-owned device memory and converted there
+ * to the device layout (see fc_gguf_debug_weights), so the caller may free
+ * `blocks` as soon as the call returns.  Synchronous.  *out receives the
+ * handle.
  */
 int fc_gguf_create(int64_t N, int64_t K, int qtype, const void* blocks,
                    int blocks_on_device, fc_gguf_t* out);
@@ -88,7 +90,9 @@ int fc_gguf_set_path(fc_gguf_t h, int path);
 /* Frees the handle and its device memory; NULL is accepted. Synchronises the device. */
 int fc_gguf_destroy(fc_gguf_t h);
 
-/* N, K, qtype, and the byte size of the device weights of a handle (any may be NULL). */
+/* N, K, qtype, and the byte size of the device weights of a handle (any may be
+ * NULL); the size includes the padding of the device layout (see
+ * fc_gguf_debug_weights). */
 int fc_gguf_info(fc_gguf_t h, int64_t* N, int64_t* K, int* qtype, int64_t* weight_bytes);
 
 /*
@@ -127,9 +131,15 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
  *   Q5_K [M, N, K/32] (sum of qa*q over each 32-value sub-block, q in [0,31]);
  *   Q6_K [M, N, K/16] (sum of qa*(q-32) over each 16-value sub-block).
  *
- * fc_gguf_debug_weights: copies the handle's device weight bytes (Q5_K AoS
- *   blocks, or the Q6_K QL|QH|SC|D planes) to device memory `dst`
- *   (fc_gguf_info's weight_bytes long).
+ * fc_gguf_debug_weights: copies the handle's device weight bytes to device
+ *   memory `dst` (fc_gguf_info's weight_bytes long).  Device layout, per
+ *   matrix (experts one after another): blocks b = n*(K/256) + kb, padded
+ *   with zero bytes to a multiple of 64; groups of 64 consecutive blocks
+ *   stored piece-major, piece p (16 bytes) of block b at
+ *   ((b/64)*P + p)*1024 + (b%64)*16 within its plane.  Q5_K: one plane,
+ *   P = 11.  Q6_K: planes QL (P = 8) | QH (P = 4) | SC (16 B per block, in
+ *   block order) | D (2 B per block, in block order), each over the padded
+ *   block count.
  */
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s,
                            int32_t* T, void* stream);

@@ -1,7 +1,8 @@
 """GPU parity of the decode path (M < 8) against the CPU oracle.
 
 Bit-exact: the int8 activation quantisation (codes, scales, group sums), the
-integer sub-block dot sums, and the device Q6_K plane regroup.  Outputs: max
+integer sub-block dot sums, and the device weight layout (Q6_K plane regroup
+plus the 64-block piece interleave).  Outputs: max
 relative error <= 1e-3 against the oracle's exact emulation of the int8 path
 (metric max |y-r| / max(|r|, rms(r))).
 """
@@ -64,14 +65,60 @@ def test_quantize_bit_exact(gpu_lib, M, K):
 
 # ---------------------------------------------------------------- regroup --
 
-@pytest.mark.parametrize("N,K", [(3, 768), (512, 2048)])
-def test_device_regroup_bytes(gpu_lib, N, K):
+def _pad_blocks(plane, fill=0):
+    nblk = plane.shape[0]
+    nbp = -(-nblk // 64) * 64
+    out = np.full((nbp, plane.shape[1]), fill, dtype=plane.dtype)
+    out[:nblk] = plane
+    return out
+
+
+def _interleave(plane, P):
+    """[nblk, 16P] bytes -> groups of 64 blocks stored piece-major: [g][p][lane][16]."""
+    x = _pad_blocks(plane).reshape(-1, 64, P, 16)
+    return x.transpose(0, 2, 1, 3).reshape(-1)
+
+
+def expected_device_bytes(w, qtype):
+    """The library's device copy of canonical blocks w: Q5_K pieces interleaved
+    over groups of 64 blocks; Q6_K planes QL | QH | SC | D (the oracle's
+    regroup) with QL and QH interleaved the same way, zero-padded to 64 blocks."""
+    if qtype == "q5_k":
+        return _interleave(w.reshape(-1, 176), 11)
+    planes = okq.q6k_regroup(w)
+    nblk = w.reshape(-1, 210).shape[0]
+    ql = planes[:128 * nblk].reshape(nblk, 128)
+    qh = planes[128 * nblk:192 * nblk].reshape(nblk, 64)
+    sc = planes[192 * nblk:208 * nblk].reshape(nblk, 16)
+    d = planes[208 * nblk:].reshape(nblk, 2)
+    return np.concatenate([_interleave(ql, 8), _interleave(qh, 4),
+                           _pad_blocks(sc).reshape(-1), _pad_blocks(d).reshape(-1)])
+
+
+@pytest.mark.parametrize("N,K", [(3, 768), (512, 2048), (77, 1280)])
+def test_device_layout_bytes(gpu_lib, N, K):
     w = synth.q6k_blocks(N, K, synth.rng(51, N, 0))
-    fcg = _fc(w, "q6_k", N, K)
-    got = _host(fcg.debug_weights())
-    assert np.array_equal(got, okq.q6k_regroup(w))
+    got = _host(_fc(w, "q6_k", N, K).debug_weights())
+    assert np.array_equal(got, expected_device_bytes(w, "q6_k"))
     w5 = synth.q5k_blocks(N, K, synth.rng(51, N + 1, 0))
-    assert np.array_equal(_host(_fc(w5, "q5_k", N, K).debug_weights()), w5.reshape(-1))
+    got5 = _host(_fc(w5, "q5_k", N, K).debug_weights())
+    assert np.array_equal(got5, expected_device_bytes(w5, "q5_k"))
+
+
+def test_layout_helper_is_a_permutation():
+    # the expected-bytes helper itself: every canonical byte appears exactly
+    # once, and block 64g + l's piece p lands at ((g*P + p)*64 + l)*16
+    nblk = 70
+    idx = np.arange(nblk * 176, dtype=np.int64).reshape(nblk, 176)
+    x = _pad_blocks(idx, fill=-1).reshape(-1, 64, 11, 16).transpose(0, 2, 1, 3).reshape(-1)
+    assert x.size == 128 * 176
+    assert np.array_equal(np.sort(x[x >= 0]), np.arange(nblk * 176))
+    for b, p in [(0, 0), (5, 3), (63, 10), (64, 0), (69, 7)]:
+        g, l = divmod(b, 64)
+        o = ((g * 11 + p) * 64 + l) * 16
+        assert np.array_equal(x[o:o + 16], idx[b, 16 * p:16 * p + 16])
+    w = synth.q5k_blocks(nblk, 256, synth.rng(51, 0, 1))
+    assert np.array_equal(expected_device_bytes(w, "q5_k")[x >= 0], w.reshape(-1)[x[x >= 0]])
 
 
 # --------------------------------------------------------------- int sums --
