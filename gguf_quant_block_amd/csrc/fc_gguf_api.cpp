@@ -69,7 +69,7 @@ int ensure_ws(fc_gguf* h, size_t bytes) {
 }
 
 int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, int on_device,
-                fc_gguf_t* out) {
+                int grouped, fc_gguf_t* out) {
   if (!out) return FC_GGUF_EINVAL;
   *out = nullptr;
   if (!blocks || E <= 0 || N <= 0 || K <= 0 || (K % 256) != 0) return FC_GGUF_EINVAL;
@@ -113,8 +113,8 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
     src = staging;
   }
   for (int64_t x = 0; e == hipSuccess && x < E; ++x)
-    e = fcg::launch_weight_layout(qtype, src + x * src_bytes, h->w + x * expert_bytes, nblk,
-                                  nullptr);
+    e = fcg::launch_weight_layout(qtype, grouped == 0, src + x * src_bytes,
+                                  h->w + x * expert_bytes, nblk, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (staging) hipFree(staging);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -133,14 +133,14 @@ extern "C" {
 
 int fc_gguf_create(int64_t N, int64_t K, int qtype, const void* blocks, int blocks_on_device,
                    fc_gguf_t* out) {
-  return create_impl(1, N, K, qtype, blocks, blocks_on_device, out);
+  return create_impl(1, N, K, qtype, blocks, blocks_on_device, 0, out);
 }
 
 int fc_gguf_create_grouped(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks,
                            int blocks_on_device, fc_gguf_t* out) {
   if (out) *out = nullptr;
   if (E > fcg::MOE_MAX_E) return FC_GGUF_ERANGE;
-  return create_impl(E, N, K, qtype, blocks, blocks_on_device, out);
+  return create_impl(E, N, K, qtype, blocks, blocks_on_device, 1, out);
 }
 
 int fc_gguf_destroy(fc_gguf_t h) {

@@ -145,18 +145,23 @@ struct TileRows {
 };
 
 // Main loop of one tile over the stages [s_begin, s_end) of K, walked from
-// stage s_begin + rot (wrapping), for the first
-// MTA (<= MT) 16-row halves of the tile.  W is one weight matrix [N, K] in
-// the device layout of layout.h over nbp (padded) blocks; n0 its first
-// weight row (rows past N are clamped to N - 1: loaded, never stored).
+// stage s_begin + rot (wrapping), for the first MTA (<= MT) 16-row halves of
+// the tile.  W is one weight matrix [N, K] over nbp (padded) blocks, in the
+// piece-interleaved device layout of layout.h (IL) or in the canonical one
+// (Q5_K blocks in order; Q6_K row-major QL | QH | SC | D planes).  n0 is its
+// first weight row (rows past N are clamped to N - 1: loaded, never stored).
 // acc[i][j] receives C[n][m] of the 16x16 sub-tile (half i < MTA, weight
-// sub-tile j).  The loop body has no data-dependent branches.
-template <int QT, int MT, int NT, int MTA>
+// sub-tile j).  PD = 1: the next stage's loads are in flight while a stage
+// computes; PD = 2: the next two stages' (three register sets; for the small
+// row tiles of the streaming-bound grouped FC).  The loop body has no
+// data-dependent branches.
+template <int QT, int MT, int NT, int MTA, bool IL, int PD>
 __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int N,
                                               int K, int n0, int s_begin, int s_end, int rot,
                                               const TileRows<MT>& rows, f16 (*As)[16 * MT * ASTR],
                                               floatx4 (&acc)[MT][NT]) {
   static_assert(MTA >= 1 && MTA <= MT, "active halves");
+  static_assert(PD == 1 || PD == 2, "prefetch depth");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4;
@@ -170,18 +175,23 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
     nrow[j] = n < N ? n : N - 1;
   }
 
+  // byte offset of 16-byte piece p of block b in a plane of P pieces per block
+  auto piece = [&](size_t b, int P, int p) -> size_t {
+    if constexpr (IL) return piece_off(b, P, p);
+    else return b * (size_t)(16 * P) + (size_t)(16 * p);
+  };
   // raw bytes of the lane's rows for stage s (half-block hb of block kb):
-  // 8-byte slices of the 16-byte pieces of the device layout
+  // 8-byte slices of the 16-byte pieces
   auto load_raw_q5 = [&](int s, RawQ5* raw) {
     const int kb = s >> 1, hb = s & 1;
     const int sub = 8 * (kq & 1), pq = kq >> 1;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const size_t b = (size_t)nrow[j] * KB + kb;
-      raw[j].hdr = *(const uint4*)(W + piece_off(b, 11, 0));
-      raw[j].qsA = *(const uint2*)(W + piece_off(b, 11, 3 + 4 * hb + pq) + sub);
-      raw[j].qsB = *(const uint2*)(W + piece_off(b, 11, 5 + 4 * hb + pq) + sub);
-      raw[j].qh = *(const uint2*)(W + piece_off(b, 11, 1 + pq) + sub);
+      raw[j].hdr = *(const uint4*)(W + piece(b, 11, 0));
+      raw[j].qsA = *(const uint2*)(W + piece(b, 11, 3 + 4 * hb + pq) + sub);
+      raw[j].qsB = *(const uint2*)(W + piece(b, 11, 5 + 4 * hb + pq) + sub);
+      raw[j].qh = *(const uint2*)(W + piece(b, 11, 1 + pq) + sub);
     }
   };
   auto load_raw_q6 = [&](int s, RawQ6* raw) {
@@ -190,74 +200,39 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const size_t b = (size_t)nrow[j] * KB + kb;
-      raw[j].qlA = *(const uint2*)(W + piece_off(b, 8, 4 * hb + pq) + sub);
-      raw[j].qlB = *(const uint2*)(W + piece_off(b, 8, 4 * hb + 2 + pq) + sub);
-      raw[j].qh = *(const uint2*)(W + q6k_qh_base(nbp) + piece_off(b, 4, 2 * hb + pq) + sub);
+      raw[j].qlA = *(const uint2*)(W + piece(b, 8, 4 * hb + pq) + sub);
+      raw[j].qlB = *(const uint2*)(W + piece(b, 8, 4 * hb + 2 + pq) + sub);
+      raw[j].qh = *(const uint2*)(W + q6k_qh_base(nbp) + piece(b, 4, 2 * hb + pq) + sub);
       raw[j].sc = *(const uint2*)(W + q6k_sc_base(nbp) + 16 * b + 8 * hb);
       raw[j].d = *(const uint16_t*)(W + q6k_d_base(nbp) + 2 * b);
     }
   };
+  using Raw = typename std::conditional<QT == QT_Q5K, RawQ5, RawQ6>::type;
+  auto load_raw = [&](int s, Raw* raw) {
+    if constexpr (QT == QT_Q5K) load_raw_q5(s, raw); else load_raw_q6(s, raw);
+  };
 
   // activation stage: 16*MTA rows x 128 halves, MTA chunks of 16 B per thread
-  u32x4 areg[MTA];
-  auto load_a = [&](int s) {
+  auto load_a = [&](int s, u32x4* areg) {
 #pragma unroll
     for (int i = 0; i < MTA; ++i)
       areg[i] = *(const u32x4*)(rows.a_ld[i] + (size_t)s * KSTAGE + 8 * (tid & 15));
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int buf, const u32x4* areg) {
 #pragma unroll
     for (int i = 0; i < MTA; ++i) {
       const int c = tid + 256 * i;
       *(u32x4*)(&As[buf][(c >> 4) * ASTR + 8 * (c & 15)]) = areg[i];
     }
   };
-
-#pragma unroll
-  for (int i = 0; i < MTA; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  using Raw = typename std::conditional<QT == QT_Q5K, RawQ5, RawQ6>::type;
-  Raw rawc[NT], rawn[NT];
-
-  // stage t of the loop is stage s_begin + (t + rot) mod nst of K
-  const int nst = s_end - s_begin;
-  auto stage = [&](int t) {
-    int u = t + rot;
-    if (u >= nst) u -= nst;
-    return s_begin + u;
-  };
-  if (nst > 0) {
-    const int s0 = stage(0);
-    load_a(s0);
-    if constexpr (QT == QT_Q5K) load_raw_q5(s0, rawc); else load_raw_q6(s0, rawc);
-    store_a(0);
-  }
-  // drain the prologue: the loop then starts with no load in flight, and the
-  // waits of its body cover only the loads of the body itself
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = 0; t < nst; ++t) {
-    const int s = stage(t);
-    const int buf = t & 1;
-    const bool more = t + 1 < nst;
-    if (more) {
-      const int sn = stage(t + 1);
-      load_a(sn);
-      if constexpr (QT == QT_Q5K) load_raw_q5(sn, rawn); else load_raw_q6(sn, rawn);
-    }
-    // keep the next stage's loads here, ahead of this stage's work: without
-    // the fence the compiler sinks them to their first use and the prefetch
-    // is lost
-    asm volatile("" ::: "memory");
-    // decode this stage's weight fragments: wf[j][g]
+  // one stage on the matrix cores: decode the lane's weight fragments, then
+  // C += W_frag x A_frag over the four 32-value k-steps
+  auto compute = [&](int s, int buf, const Raw* raw) {
     half8v wf[NT][4];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      if constexpr (QT == QT_Q5K) decode_q5k_half(rawc[j], s & 1, wf[j]);
-      else decode_q6k_half(rawc[j], kq, wf[j]);
+      if constexpr (QT == QT_Q5K) decode_q5k_half(raw[j], s & 1, wf[j]);
+      else decode_q6k_half(raw[j], kq, wf[j]);
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -271,12 +246,84 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
         for (int j = 0; j < NT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j][g], af[i], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      store_a(buf ^ 1);
+  };
+
 #pragma unroll
-      for (int j = 0; j < NT; ++j) rawc[j] = rawn[j];
+  for (int i = 0; i < MTA; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // stage t of the loop is stage s_begin + (t + rot) mod nst of K
+  const int nst = s_end - s_begin;
+  auto stage = [&](int t) {
+    int u = t + rot;
+    if (u >= nst) u -= nst;
+    return s_begin + u;
+  };
+
+  if constexpr (PD == 1) {
+    Raw rawc[NT], rawn[NT];
+    u32x4 areg[MTA];
+    if (nst > 0) {
+      load_a(stage(0), areg);
+      load_raw(stage(0), rawc);
+      store_a(0, areg);
+    }
+    // drain the prologue: the loop then starts with no load in flight, and
+    // the waits of its body cover only the loads of the body itself
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < nst; ++t) {
+      const bool more = t + 1 < nst;
+      if (more) {
+        load_a(stage(t + 1), areg);
+        load_raw(stage(t + 1), rawn);
+      }
+      // keep the next stage's loads here, ahead of this stage's work:
+      // without the fence the compiler sinks them to their first use and
+      // the prefetch is lost
+      asm volatile("" ::: "memory");
+      compute(stage(t), t & 1, rawc);
+      if (more) {
+        store_a((t + 1) & 1, areg);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) rawc[j] = rawn[j];
+      }
+      __syncthreads();
+    }
+  } else {
+    // three register sets, rotated by unrolling the loop three times: stage
+    // t computes from set t % 3 while the sets of t + 1 and t + 2 fill
+    Raw raw[3][NT];
+    u32x4 areg[3][MTA];
+    if (nst > 0) {
+      load_a(stage(0), areg[0]);
+      load_raw(stage(0), raw[0]);
+      store_a(0, areg[0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (nst > 1) {
+      load_a(stage(1), areg[1]);
+      load_raw(stage(1), raw[1]);
     }
     __syncthreads();
+    auto step = [&](int t, auto cc) {
+      constexpr int C = decltype(cc)::value;
+      constexpr int C1 = (C + 1) % 3, C2 = (C + 2) % 3;
+      if (t + 2 < nst) {
+        load_a(stage(t + 2), areg[C2]);
+        load_raw(stage(t + 2), raw[C2]);
+      }
+      asm volatile("" ::: "memory");
+      compute(stage(t), t & 1, raw[C]);
+      if (t + 1 < nst) store_a((t + 1) & 1, areg[C1]);
+      __syncthreads();
+    };
+    for (int t = 0; t < nst; t += 3) {
+      step(t, std::integral_constant<int, 0>{});
+      if (t + 1 < nst) step(t + 1, std::integral_constant<int, 1>{});
+      if (t + 2 < nst) step(t + 2, std::integral_constant<int, 2>{});
+    }
   }
 }
 

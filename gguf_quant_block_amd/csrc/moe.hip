@@ -193,11 +193,11 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
   const size_t nbp = padded_blocks((size_t)N * (K >> 8));
   const int S = K / KSTAGE;
   const int rot = (ti + nt) % S;           // spread concurrent loads over K
-  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else if constexpr (MT == 2) tile_mainloop<QT, MT, NT, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act == 2) tile_mainloop<QT, MT, NT, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act == 3) tile_mainloop<QT, MT, NT, 3>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else tile_mainloop<QT, MT, NT, MT>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else if constexpr (MT == 2) tile_mainloop<QT, MT, NT, 2, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act == 2) tile_mainloop<QT, MT, NT, 2, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act == 3) tile_mainloop<QT, MT, NT, 3, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else tile_mainloop<QT, MT, NT, MT, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
 
 #pragma unroll
   for (int i = 0; i < MT; ++i) {

@@ -62,7 +62,7 @@ prefill_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   // channels instead of hitting the same addresses together
   const int nst = s_end - s_begin;
   const int rot = nst > 0 ? (nt + mt) % nst : 0;
-  tile_mainloop<QT, MT, NT, MT>(W, padded_blocks((size_t)N * (K >> 8)), N, K, n0, s_begin, s_end, rot, rows, As,
+  tile_mainloop<QT, MT, NT, MT, true, 1>(W, padded_blocks((size_t)N * (K >> 8)), N, K, n0, s_begin, s_end, rot, rows, As,
                                 acc);
 
   // epilogue: lane holds C[n = 4*(lane>>4) + r][m = lane & 15] of each 16x16 tile

@@ -134,12 +134,14 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
  * fc_gguf_debug_weights: copies the handle's device weight bytes to device
  *   memory `dst` (fc_gguf_info's weight_bytes long).  Device layout, per
  *   matrix (experts one after another): blocks b = n*(K/256) + kb, padded
- *   with zero bytes to a multiple of 64; groups of 64 consecutive blocks
- *   stored piece-major, piece p (16 bytes) of block b at
- *   ((b/64)*P + p)*1024 + (b%64)*16 within its plane.  Q5_K: one plane,
- *   P = 11.  Q6_K: planes QL (P = 8) | QH (P = 4) | SC (16 B per block, in
- *   block order) | D (2 B per block, in block order), each over the padded
- *   block count.
+ *   with zero bytes to a multiple of 64.  Q5_K: one plane of P = 11 pieces
+ *   (16 bytes) per block.  Q6_K: planes QL (P = 8) | QH (P = 4) | SC (16 B
+ *   per block, in block order) | D (2 B per block, in block order), each over
+ *   the padded block count.  Single-matrix handles store the QL, QH and Q5_K
+ *   planes piece-interleaved: groups of 64 consecutive blocks piece-major,
+ *   piece p of block b at ((b/64)*P + p)*1024 + (b%64)*16 within its plane.
+ *   Grouped handles store every plane in block order (piece p of block b at
+ *   b*16*P + 16*p).
  */
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s,
                            int32_t* T, void* stream);

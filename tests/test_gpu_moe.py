@@ -110,6 +110,33 @@ def test_moe_invalid_ids_give_zero_rows(gpu_lib, qtype):
     _check_experts(y, w, qtype, A, ids, False, range(E))
 
 
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_grouped_device_layout_bytes(gpu_lib, qtype):
+    # grouped handles keep every plane in block order, per expert, padded to
+    # a multiple of 64 blocks
+    from gguf_quant_block_amd.binding import FcGguf
+    E, N, K = 3, 5, 512
+    bb = 176 if qtype == "q5_k" else 210
+    w = synth.blocks(qtype, E * N, K, synth.rng(44, 0, 0)).reshape(E, N, -1)
+    got = _host(FcGguf(N, K, qtype, w, experts=E).debug_weights())
+    nblk = N * K // 256
+    per = 64 * bb
+    assert got.size == E * per
+    for e in range(E):
+        blocks = w[e].reshape(nblk, bb)
+        pad = np.zeros((64, bb), dtype=np.uint8)
+        pad[:nblk] = blocks
+        if qtype == "q5_k":
+            exp = pad.reshape(-1)
+        else:
+            exp = np.concatenate([pad[:, :128].reshape(-1), pad[:, 128:192].reshape(-1),
+                                  pad[:, 192:208].reshape(-1), pad[:, 208:].reshape(-1)])
+            # the plane split agrees with the oracle's regroup on the real blocks
+            planes = okq.q6k_regroup(w[e])
+            assert np.array_equal(exp[:128 * nblk], planes[:128 * nblk])
+        assert np.array_equal(got[e * per:(e + 1) * per], exp)
+
+
 def test_moe_empty_and_repeat(gpu_lib):
     import torch
     qtype = "q6_k"
