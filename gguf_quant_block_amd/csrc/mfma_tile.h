@@ -32,8 +32,11 @@
 
 namespace fcg {
 
-constexpr int KSTAGE = 128;          // values of K per stage (half super-block)
-constexpr int ASTR = KSTAGE + 8;     // LDS row stride in halves (pad 16 B)
+constexpr int KSTAGE = 128;          // values of K per half super-block
+// A stage covers SH half super-blocks (SH = 1 or 2); its LDS activation
+// tile has a row stride of astr(SH) halves (16 bytes of padding per row).
+__host__ __device__ constexpr int astr(int SH) { return KSTAGE * SH + 8; }
+constexpr int ASTR = astr(1);
 
 struct RawQ5 {  // one lane, one row, one half-block
   uint4 hdr;    // d | dmin, scales[0..3], scales[4..7], scales[8..11]
@@ -151,17 +154,20 @@ struct TileRows {
 // (Q5_K blocks in order; Q6_K row-major QL | QH | SC | D planes).  n0 is its
 // first weight row (rows past N are clamped to N - 1: loaded, never stored).
 // acc[i][j] receives C[n][m] of the 16x16 sub-tile (half i < MTA, weight
-// sub-tile j).  PD = 1: the next stage's loads are in flight while a stage
-// computes; PD = 2: the next two stages' (three register sets; for the small
-// row tiles of the streaming-bound grouped FC).  The loop body has no
-// data-dependent branches.
-template <int QT, int MT, int NT, int MTA, bool IL, int PD>
+// sub-tile j).  A stage is SH half super-blocks (128*SH values of K; stages
+// are numbered in those units).  PD = 1: the next stage's loads are in flight
+// while a stage computes; PD = 2: the next two stages' (three register sets).
+// The loop body has no data-dependent branches.
+template <int QT, int MT, int NT, int MTA, bool IL, int PD, int SH = 1>
 __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int N,
                                               int K, int n0, int s_begin, int s_end, int rot,
-                                              const TileRows<MT>& rows, f16 (*As)[16 * MT * ASTR],
+                                              const TileRows<MT>& rows,
+                                              f16 (*As)[16 * MT * astr(SH)],
                                               floatx4 (&acc)[MT][NT]) {
   static_assert(MTA >= 1 && MTA <= MT, "active halves");
   static_assert(PD == 1 || PD == 2, "prefetch depth");
+  static_assert(SH == 1 || SH == 2, "halves per stage");
+  constexpr int AS = astr(SH);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4;
@@ -208,43 +214,54 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
     }
   };
   using Raw = typename std::conditional<QT == QT_Q5K, RawQ5, RawQ6>::type;
-  auto load_raw = [&](int s, Raw* raw) {
-    if constexpr (QT == QT_Q5K) load_raw_q5(s, raw); else load_raw_q6(s, raw);
+  // the raw bytes of stage s: its SH half-blocks (half index SH*s + x)
+  auto load_raw = [&](int s, Raw (*raw)[NT]) {
+#pragma unroll
+    for (int x = 0; x < SH; ++x) {
+      if constexpr (QT == QT_Q5K) load_raw_q5(SH * s + x, raw[x]); else load_raw_q6(SH * s + x, raw[x]);
+    }
   };
 
-  // activation stage: 16*MTA rows x 128 halves, MTA chunks of 16 B per thread
-  auto load_a = [&](int s, u32x4* areg) {
+  // activation stage: 16*MTA rows x 128*SH halves, MTA*SH chunks of 16 B per thread
+  auto load_a = [&](int s, u32x4 (*areg)[SH]) {
 #pragma unroll
     for (int i = 0; i < MTA; ++i)
-      areg[i] = *(const u32x4*)(rows.a_ld[i] + (size_t)s * KSTAGE + 8 * (tid & 15));
+#pragma unroll
+      for (int x = 0; x < SH; ++x)
+        areg[i][x] = *(const u32x4*)(rows.a_ld[i] + (size_t)(SH * s + x) * KSTAGE + 8 * (tid & 15));
   };
-  auto store_a = [&](int buf, const u32x4* areg) {
+  auto store_a = [&](int buf, u32x4 (*areg)[SH]) {
 #pragma unroll
     for (int i = 0; i < MTA; ++i) {
       const int c = tid + 256 * i;
-      *(u32x4*)(&As[buf][(c >> 4) * ASTR + 8 * (c & 15)]) = areg[i];
+#pragma unroll
+      for (int x = 0; x < SH; ++x)
+        *(u32x4*)(&As[buf][(c >> 4) * AS + KSTAGE * x + 8 * (c & 15)]) = areg[i][x];
     }
   };
   // one stage on the matrix cores: decode the lane's weight fragments, then
-  // C += W_frag x A_frag over the four 32-value k-steps
-  auto compute = [&](int s, int buf, const Raw* raw) {
-    half8v wf[NT][4];
+  // C += W_frag x A_frag over the four 32-value k-steps of each half
+  auto compute = [&](int s, int buf, Raw (*raw)[NT]) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if constexpr (QT == QT_Q5K) decode_q5k_half(raw[j], s & 1, wf[j]);
-      else decode_q6k_half(raw[j], kq, wf[j]);
-    }
+    for (int x = 0; x < SH; ++x) {
+      half8v wf[NT][4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      half8v af[MTA];
+      for (int j = 0; j < NT; ++j) {
+        if constexpr (QT == QT_Q5K) decode_q5k_half(raw[x][j], (SH * s + x) & 1, wf[j]);
+        else decode_q6k_half(raw[x][j], kq, wf[j]);
+      }
 #pragma unroll
-      for (int i = 0; i < MTA; ++i)
-        af[i] = *(const half8v*)(&As[buf][(16 * i + (lane & 15)) * ASTR + 32 * g + 8 * kq]);
+      for (int g = 0; g < 4; ++g) {
+        half8v af[MTA];
 #pragma unroll
-      for (int i = 0; i < MTA; ++i)
+        for (int i = 0; i < MTA; ++i)
+          af[i] = *(const half8v*)(&As[buf][(16 * i + (lane & 15)) * AS + KSTAGE * x + 32 * g + 8 * kq]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j][g], af[i], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < MTA; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j][g], af[i], acc[i][j], 0, 0, 0);
+      }
     }
   };
 
@@ -262,8 +279,8 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
   };
 
   if constexpr (PD == 1) {
-    Raw rawc[NT], rawn[NT];
-    u32x4 areg[MTA];
+    Raw rawc[SH][NT], rawn[SH][NT];
+    u32x4 areg[MTA][SH];
     if (nst > 0) {
       load_a(stage(0), areg);
       load_raw(stage(0), rawc);
@@ -287,15 +304,17 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
       if (more) {
         store_a((t + 1) & 1, areg);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) rawc[j] = rawn[j];
+        for (int x = 0; x < SH; ++x)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) rawc[x][j] = rawn[x][j];
       }
       __syncthreads();
     }
   } else {
     // three register sets, rotated by unrolling the loop three times: stage
     // t computes from set t % 3 while the sets of t + 1 and t + 2 fill
-    Raw raw[3][NT];
-    u32x4 areg[3][MTA];
+    Raw raw[3][SH][NT];
+    u32x4 areg[3][MTA][SH];
     if (nst > 0) {
       load_a(stage(0), areg[0]);
       load_raw(stage(0), raw[0]);

@@ -29,10 +29,22 @@ namespace fcg {
 
 constexpr int MOE_BUCKET_THREADS = 1024;
 constexpr int MOE_NT = 2;                  // BN = 128 weight rows per workgroup
+#ifndef MOE_PD
+#define MOE_PD 1                           // stages of prefetch in the tile main loop
+#endif
+#ifndef MOE_SH
+#define MOE_SH 2                           // half super-blocks per stage
+#endif
 
-// Row tile: 32 rows (two 16-row halves) for sparse routing, 64 once the
-// average expert holds at least 32 rows.
-static int moe_mt(int E, long long P) { return P >= 32LL * E ? 4 : 2; }
+// Row tile: 16-row halves, 2 per tile when the routing is very sparse (fewer
+// than 8 pairs per expert on average), 8 when it is dense (64 or more), else 4.
+// Empty halves of a tile are skipped, so a tall tile costs a short expert
+// nothing, while a tall expert decodes its weights fewer times.
+#ifndef MOE_MT_FIXED
+static int moe_mt(int E, long long P) { return P < 8LL * E ? 2 : (P >= 64LL * E ? 8 : 4); }
+#else
+static int moe_mt(int, long long) { return MOE_MT_FIXED; }
+#endif
 
 static long long moe_max_tiles(int E, long long P, int BM) {
   return (P + BM - 1) / BM + (E < P ? E : P);
@@ -152,7 +164,7 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
                    int max_tiles, int tiles_n) {
   constexpr int BM = 16 * MT;
   constexpr int BN = 64 * NT;
-  __shared__ __align__(16) f16 As[2][BM * ASTR];
+  __shared__ __align__(16) f16 As[2][BM * astr(MOE_SH)];
 
   // XCD-aware remap (round-robin dispatch over 8 XCDs): each XCD takes a
   // contiguous run of logical items, row tiles fastest, so the row tiles of
@@ -191,13 +203,13 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
   floatx4 acc[MT][NT];
   const uint8_t* We = W + (size_t)e * expert_bytes;
   const size_t nbp = padded_blocks((size_t)N * (K >> 8));
-  const int S = K / KSTAGE;
+  const int S = K / (KSTAGE * MOE_SH);
   const int rot = (ti + nt) % S;           // spread concurrent loads over K
-  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else if constexpr (MT == 2) tile_mainloop<QT, MT, NT, 2, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act == 2) tile_mainloop<QT, MT, NT, 2, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act == 3) tile_mainloop<QT, MT, NT, 3, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else tile_mainloop<QT, MT, NT, MT, false, 2>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  // (active halves rounded up to 1, 2, 4 or MT)
+  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, false, MOE_PD, MOE_SH>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act == 2 || MT == 2) tile_mainloop<QT, MT, NT, (MT < 2 ? MT : 2), false, MOE_PD, MOE_SH>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act <= 4 || MT == 4) tile_mainloop<QT, MT, NT, (MT < 4 ? MT : 4), false, MOE_PD, MOE_SH>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  else tile_mainloop<QT, MT, NT, MT, false, MOE_PD, MOE_SH>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
 
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
@@ -240,12 +252,15 @@ hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, i
                      BM, N, Y, w.tiles, w.offsets, w.pairs, w.ntiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+#define FCG_MOE(QT_, MT_) \
+  if (mt == MT_) return launch_grouped_t<QT_, MT_>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
   if (qtype == QT_Q5K) {
-    if (mt == 2) return launch_grouped_t<QT_Q5K, 2>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
-    return launch_grouped_t<QT_Q5K, 4>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
+    FCG_MOE(QT_Q5K, 2) FCG_MOE(QT_Q5K, 4) FCG_MOE(QT_Q5K, 8)
+  } else {
+    FCG_MOE(QT_Q6K, 2) FCG_MOE(QT_Q6K, 4) FCG_MOE(QT_Q6K, 8)
   }
-  if (mt == 2) return launch_grouped_t<QT_Q6K, 2>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
-  return launch_grouped_t<QT_Q6K, 4>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
+#undef FCG_MOE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fcg

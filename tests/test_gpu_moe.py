@@ -1,11 +1,11 @@
 """GPU parity of the grouped (MoE expert) FC against the float64 oracle.
 
 Relative Frobenius error <= 2e-3, over the whole output and per expert, so a
-bug in a 1-row expert is not hidden by the hot experts.  Covers the 32-row and
-64-row tile variants, experts spanning several ragged tiles, N tails, shared
+bug in a 1-row expert is not hidden by the hot experts.  Covers experts
+spanning several ragged tiles, N tails, shared
 and per-pair activation rows, ids outside [0, E), empty experts, T = 0,
 repeat calls (the pair order inside an expert is free, the result must not
-depend on it), and the full-size routed Q6_K expert FCs (128 experts, top-8,
+depend on it), the 32-, 64- and 128-row tile variants, and the full-size routed Q6_K expert FCs (128 experts, top-8,
 256 tokens, Zipf 1.1 routing) on sampled experts.
 """
 
@@ -71,6 +71,7 @@ def _check_experts(y, w, qtype, A, ids, a_per_slot, experts):
     (4, 128, 768, 64, 2),      # 128 pairs over 4 experts: 64-row tiles
     (16, 96, 256, 90, 4),      # several ragged tiles per hot expert
     (32, 256, 512, 5, 3),      # more experts than pairs: most experts empty
+    (2, 96, 1024, 100, 2),     # dense routing: 128-row tiles
 ])
 def test_moe_small(gpu_lib, qtype, a_per_slot, E, N, K, T, top_k):
     w, A, ids = _moe_case(qtype, E, N, K, T, top_k, a_per_slot, 40, E * 1000 + T)
