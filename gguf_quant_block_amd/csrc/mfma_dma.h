@@ -1,0 +1,261 @@
+// Matrix-core tile with decoupled loads: loader waves stream the activation
+// tile and the raw weight pieces straight into a ring of LDS stages with
+// global_load_lds_dwordx4; compute waves only read LDS, decode the weights
+// into MFMA operands and run the matrix cores.
+//
+// OpenVINO PR #39119, section Implementation: every weight value is decoded
+// once per workgroup and reused across all the activation rows of the tile,
+// with loads and decode double-buffered.  Here the buffering is a ring of
+// three stages, so two stages of loads are in flight while one computes, and
+// no register holds data in flight.
+//
+// Workgroup: 384 threads.  Waves 0-3 compute (wave w owns weight rows
+// 32w .. 32w+31 of the 128-row tile); wave 4 loads the activation tile, wave
+// 5 the weight pieces.  A stage is half a super-block (128 values of K).
+// LDS stage slot:
+//   A: BM rows x 16 chunks of 16 B; chunk c of row r sits at position
+//      c ^ (r & 15) of the row, so that the 16 rows of an MFMA operand read
+//      hit 16 distinct bank groups;
+//   W: 7 pieces x 128 rows x 16 B (the 16-byte pieces of the half-block
+//      that the decode reads: Q5_K header, the two fifth-bit pieces, four
+//      code pieces; Q6_K four QL pieces, two QH pieces, the scales), then for
+//      Q6_K the 4-byte word holding each row's d.
+// One barrier per stage: a compute wave reaches it after reading its slot,
+// a loader wave after its loads for the next stage have landed.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+#include "layout.h"
+#include "mfma_tile.h"
+
+namespace fcg {
+
+#ifndef FCG_DMA_SLOTS
+#define FCG_DMA_SLOTS 3
+#endif
+#ifndef FCG_DMA_ALOADERS
+#define FCG_DMA_ALOADERS 1
+#endif
+constexpr int DMA_SLOTS = FCG_DMA_SLOTS;          // LDS ring depth (stages)
+constexpr int DMA_ALOADERS = FCG_DMA_ALOADERS;    // waves loading the activation tile
+constexpr int DMA_THREADS = 64 * (4 + DMA_ALOADERS + 1);
+constexpr int DMA_WP = 7;                 // weight pieces per row per stage
+
+template <int QT, int MT>
+struct DmaCfg {
+  static constexpr int BM = 16 * MT;
+  static constexpr int BN = 128;
+  static constexpr int A_BYTES = BM * 256;
+  static constexpr int W_BYTES = DMA_WP * BN * 16 + (QT == QT_Q6K ? BN * 4 : 0);
+  static constexpr int SLOT = A_BYTES + W_BYTES;
+  static constexpr int LDS = DMA_SLOTS * SLOT;
+};
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// stage t of the loop -> stage of K (rotated start, wrapping)
+__device__ __forceinline__ int dma_stage(int t, int s_begin, int nst, int rot) {
+  int u = t + rot;
+  if (u >= nst) u -= nst;
+  return s_begin + u;
+}
+
+// Loader wave 4: the activation tile.  arow(r) points at the activation row
+// of tile row r (any valid row for rows past the tile's end).  Only the
+// first MTA halves are loaded.
+template <int QT, int MT, int MTA, class ARow>
+__device__ __forceinline__ void dma_load_a(ARow arow, uint8_t* smem, int s_begin, int s_end,
+                                           int rot, int which) {
+  using C = DmaCfg<QT, MT>;
+  static_assert((4 * MTA) % DMA_ALOADERS == 0 || 4 * MTA < DMA_ALOADERS, "split");
+  constexpr int NI = (4 * MTA + DMA_ALOADERS - 1) / DMA_ALOADERS;   // instructions per stage
+  const int lane = threadIdx.x & 63;
+  const int nst = s_end - s_begin;
+  const int k0 = which * NI;                        // this wave's first instruction
+  const f16* rp[NI];
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int kk = k0 + k < 4 * MTA ? k0 + k : 4 * MTA - 1;
+    rp[k] = arow(4 * kk + (lane >> 4));
+  }
+  auto issue = [&](int t) {
+    const int s = dma_stage(t, s_begin, nst, rot);
+    uint8_t* base = smem + (t % DMA_SLOTS) * C::SLOT;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int kk = k0 + k < 4 * MTA ? k0 + k : 4 * MTA - 1;   // (a duplicate is harmless)
+      const int r = 4 * kk + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      dma16(rp[k] + (size_t)s * KSTAGE + 8 * c, base + 1024 * kk);
+    }
+  };
+  constexpr int AHEAD = DMA_SLOTS - 1;              // stages in flight beyond the current one
+  for (int t = 0; t < AHEAD && t < nst; ++t) issue(t);
+  // stage 0 landed: at most the later prologue stages still in flight
+  if (nst >= AHEAD) wait_vmcnt<NI * (AHEAD - 1)>(); else wait_vmcnt<0>();
+  stage_barrier();
+  for (int t = 0; t < nst; ++t) {
+    if (t + AHEAD < nst) { issue(t + AHEAD); wait_vmcnt<NI * (AHEAD - 1)>(); }
+    else if (t + AHEAD - 1 < nst && AHEAD > 1) { wait_vmcnt<NI * (AHEAD - 2)>(); }
+    else { wait_vmcnt<0>(); }
+    stage_barrier();
+  }
+}
+
+// Loader wave 5: the weight pieces of the tile's 128 rows (rows past N are
+// clamped to N - 1: loaded, never stored).
+template <int QT, int MT, bool IL>
+__device__ __forceinline__ void dma_load_w(const uint8_t* W, size_t nbp, int N, int K, int n0,
+                                           uint8_t* smem, int s_begin, int s_end, int rot) {
+  using C = DmaCfg<QT, MT>;
+  constexpr int NI = 2 * DMA_WP + (QT == QT_Q6K ? 2 : 0);
+  const int lane = threadIdx.x & 63;
+  const int nst = s_end - s_begin;
+  const int KB = K >> 8;
+  size_t rb[2];                                     // first block of each of the lane's two rows
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int n = n0 + 64 * h + lane;
+    n = n < N ? n : N - 1;
+    rb[h] = (size_t)n * KB;
+  }
+  auto piece = [&](size_t b, int P, int p) -> size_t {
+    if constexpr (IL) return piece_off(b, P, p);
+    else return b * (size_t)(16 * P) + (size_t)(16 * p);
+  };
+  auto issue = [&](int t) {
+    const int s = dma_stage(t, s_begin, nst, rot);
+    const int kb = s >> 1, hb = s & 1;
+    uint8_t* base = smem + (t % DMA_SLOTS) * C::SLOT + C::A_BYTES;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t b = rb[h] + kb;
+#pragma unroll
+      for (int q = 0; q < DMA_WP; ++q) {
+        size_t off;
+        if constexpr (QT == QT_Q5K) {
+          off = piece(b, 11, q < 3 ? q : q + 4 * hb);
+        } else {
+          if (q < 4) off = piece(b, 8, 4 * hb + q);
+          else if (q < 6) off = q6k_qh_base(nbp) + piece(b, 4, 2 * hb + (q - 4));
+          else off = q6k_sc_base(nbp) + 16 * b;
+        }
+        dma16(W + off, base + (q * 128 + 64 * h) * 16);
+      }
+      if constexpr (QT == QT_Q6K)
+        dma4(W + q6k_d_base(nbp) + ((2 * b) & ~(size_t)3), base + DMA_WP * 128 * 16 + 64 * h * 4);
+    }
+  };
+  constexpr int AHEAD = DMA_SLOTS - 1;
+  for (int t = 0; t < AHEAD && t < nst; ++t) issue(t);
+  if (nst >= AHEAD) wait_vmcnt<NI * (AHEAD - 1)>(); else wait_vmcnt<0>();
+  stage_barrier();
+  for (int t = 0; t < nst; ++t) {
+    if (t + AHEAD < nst) { issue(t + AHEAD); wait_vmcnt<NI * (AHEAD - 1)>(); }
+    else if (t + AHEAD - 1 < nst && AHEAD > 1) { wait_vmcnt<NI * (AHEAD - 2)>(); }
+    else { wait_vmcnt<0>(); }
+    stage_barrier();
+  }
+}
+
+// Compute waves 0-3: acc[i][j] += C[n][m] of the 16x16 sub-tiles (half
+// i < MTA, weight sub-tile j of the wave's 32 rows) over the stages.
+template <int QT, int MT, int MTA>
+__device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t* smem, int s_begin,
+                                            int s_end, int rot, floatx4 (&acc)[MT][2]) {
+  using C = DmaCfg<QT, MT>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kq = lane >> 4, sub = 8 * (kq & 1), pq = kq >> 1;
+  const int nst = s_end - s_begin;
+  const int KB = K >> 8;
+  int nloc[2];
+  size_t rb[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    nloc[j] = wave * 32 + 16 * j + (lane & 15);
+    int n = n0 + nloc[j];
+    n = n < N ? n : N - 1;
+    rb[j] = (size_t)n * KB;
+  }
+#pragma unroll
+  for (int i = 0; i < MTA; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  stage_barrier();                                  // stage 0 has landed
+  for (int t = 0; t < nst; ++t) {
+    const int s = dma_stage(t, s_begin, nst, rot);
+    const int hb = s & 1, kb = s >> 1;
+    const uint8_t* As = smem + (t % DMA_SLOTS) * C::SLOT;
+    const uint8_t* Ws = As + C::A_BYTES;
+    // activation operands of k-step g, read one k-step ahead of their MFMAs
+    // (the first k-step's before the weight decode, to overlap its latency)
+    auto lda = [&](int g, half8v* af) {
+#pragma unroll
+      for (int i = 0; i < MTA; ++i) {
+        const int r = 16 * i + (lane & 15);
+        af[i] = *(const half8v*)(As + (r * 16 + ((4 * g + kq) ^ (r & 15))) * 16);
+      }
+    };
+    half8v afc[MTA], afn[MTA];
+    lda(0, afc);
+    asm volatile("" ::: "memory");                  // keep the reads ahead of their use
+    half8v wf[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      auto pc = [&](int q) { return Ws + (q * 128 + nloc[j]) * 16; };
+      if constexpr (QT == QT_Q5K) {
+        RawQ5 r;
+        r.hdr = *(const uint4*)pc(0);
+        r.qh = *(const uint2*)(pc(1 + pq) + sub);
+        r.qsA = *(const uint2*)(pc(3 + pq) + sub);
+        r.qsB = *(const uint2*)(pc(5 + pq) + sub);
+        decode_q5k_half(r, hb, wf[j]);
+      } else {
+        RawQ6 r;
+        r.qlA = *(const uint2*)(pc(pq) + sub);
+        r.qlB = *(const uint2*)(pc(2 + pq) + sub);
+        r.qh = *(const uint2*)(pc(4 + pq) + sub);
+        r.sc = *(const uint2*)(pc(6) + 8 * hb);
+        const uint32_t dw = *(const uint32_t*)(Ws + DMA_WP * 128 * 16 + 4 * nloc[j]);
+        r.d = dw >> (16 * (int)((rb[j] + kb) & 1));
+        decode_q6k_half(r, kq, wf[j]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g + 1 < 4) lda(g + 1, afn);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j][g], afc[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < MTA; ++i) afc[i] = afn[i];
+    }
+    stage_barrier();                                // done reading this slot; next one landed
+  }
+}
+
+}  // namespace fcg

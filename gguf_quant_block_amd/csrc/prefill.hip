@@ -13,8 +13,61 @@
 #include "common.h"
 #include "internal.h"
 #include "mfma_tile.h"
+#include "mfma_dma.h"
+
+#ifndef FCG_PREFILL_DMA
+#define FCG_PREFILL_DMA 1
+#endif
 
 namespace fcg {
+
+// Epilogue of a tile: lane holds C[n = 4*(lane>>4) + r][m = lane & 15] of each
+// 16x16 sub-tile; + R and one f16 rounding, or f32 split-K partials.
+template <int MT, int NT>
+__device__ __forceinline__ void prefill_epilogue(const floatx4 (&acc)[MT][NT],
+                                                 const f16* __restrict__ R, f16* __restrict__ Y,
+                                                 float* __restrict__ P, int M, int N, int m0,
+                                                 int n0, int sp, int splits) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kq = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int m = m0 + 16 * i + (lane & 15);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = n0 + wave * 16 * NT + 16 * j + 4 * kq;
+      if (n >= N) continue;
+      const floatx4 v = acc[i][j];
+      if (splits > 1) {
+        float* dst = P + ((size_t)sp * M + m) * N + n;
+        if (n + 3 < N && ((N & 3) == 0)) {
+          *(floatx4*)dst = v;
+        } else {
+          for (int r = 0; r < 4 && n + r < N; ++r) dst[r] = v[r];
+        }
+      } else {
+        store4_f16(Y + (size_t)m * N, R ? R + (size_t)m * N : nullptr, n, N, v);
+      }
+    }
+  }
+}
+
+// Tile index of this workgroup.  XCD-aware remap: the hardware deals
+// workgroups round-robin over 8 XCDs; give each XCD a contiguous run of
+// logical tiles (m fastest, then split, then n) so tiles sharing weight
+// columns share an L2.
+__device__ __forceinline__ void prefill_tile_id(int tiles_m, int tiles_n, int splits, int& mt,
+                                                int& sp, int& nt) {
+  const int Gt = tiles_m * tiles_n * splits;
+  int bid = blockIdx.x;
+  const int per = Gt / 8, rem = Gt % 8, x = bid % 8, j = bid / 8;
+  bid = x * per + (x < rem ? x : rem) + j;
+  mt = bid % tiles_m;
+  const int rest = bid / tiles_m;
+  sp = rest % splits;
+  nt = rest / splits;
+}
 
 template <int QT, int MT, int NT>
 __global__ void __launch_bounds__(256)
@@ -25,19 +78,8 @@ prefill_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   constexpr int BN = 64 * NT;
   __shared__ __align__(16) f16 As[2][BM * ASTR];
 
-  // XCD-aware remap: the hardware deals workgroups round-robin over 8 XCDs;
-  // give each XCD a contiguous run of logical tiles (m fastest, then split,
-  // then n) so tiles sharing weight columns share an L2.
-  const int Gt = tiles_m * tiles_n * splits;
-  int bid = blockIdx.x;
-  {
-    const int per = Gt / 8, rem = Gt % 8, x = bid % 8, j = bid / 8;
-    bid = x * per + (x < rem ? x : rem) + j;
-  }
-  const int mt = bid % tiles_m;
-  const int rest = bid / tiles_m;
-  const int sp = rest % splits;
-  const int nt = rest / splits;
+  int mt, sp, nt;
+  prefill_tile_id(tiles_m, tiles_n, splits, mt, sp, nt);
   const int m0 = mt * BM, n0 = nt * BN;
   const int S_total = K / KSTAGE;
   const int s_begin = sp * stages_per_split;
@@ -65,28 +107,46 @@ prefill_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   tile_mainloop<QT, MT, NT, MT, true, 1>(W, padded_blocks((size_t)N * (K >> 8)), N, K, n0, s_begin, s_end, rot, rows, As,
                                 acc);
 
-  // epilogue: lane holds C[n = 4*(lane>>4) + r][m = lane & 15] of each 16x16 tile
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int m = m0 + 16 * i + (lane & 15);
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int n = n0 + wave * 16 * NT + 16 * j + 4 * kq;
-      if (n >= N) continue;
-      const floatx4 v = acc[i][j];
-      if (splits > 1) {
-        float* dst = P + ((size_t)sp * M + m) * N + n;
-        if (n + 3 < N && ((N & 3) == 0)) {
-          *(floatx4*)dst = v;
-        } else {
-          for (int r = 0; r < 4 && n + r < N; ++r) dst[r] = v[r];
-        }
-      } else {
-        store4_f16(Y + (size_t)m * N, R ? R + (size_t)m * N : nullptr, n, N, v);
-      }
-    }
+  prefill_epilogue<MT, NT>(acc, R, Y, P, M, N, m0, n0, sp, splits);
+}
+
+// The same tile with loader waves and an LDS ring (mfma_dma.h).
+template <int QT, int MT>
+__global__ void __launch_bounds__(DMA_THREADS)
+prefill_dma_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
+                   f16* __restrict__ Y, float* __restrict__ P, int M, int N, int K, int tiles_m,
+                   int tiles_n, int splits, int stages_per_split) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int BM = 16 * MT, BN = 128;
+  int mt, sp, nt;
+  prefill_tile_id(tiles_m, tiles_n, splits, mt, sp, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int S_total = K / KSTAGE;
+  const int s_begin = sp * stages_per_split;
+  int s_end = s_begin + stages_per_split;
+  if (s_end > S_total) s_end = S_total;
+  if (s_end < s_begin) s_end = s_begin;
+  const int nst = s_end - s_begin;
+  // workgroups sharing activation or weight rows start at different stages
+  const int rot = nst > 0 ? (nt + mt) % nst : 0;
+  const int wave = threadIdx.x >> 6;
+  if (wave >= 4 && wave < 4 + DMA_ALOADERS) {
+    auto arow = [&](int r) {
+      int m = m0 + r;
+      m = m < M ? m : M - 1;
+      return A + (size_t)m * K;
+    };
+    dma_load_a<QT, MT, MT>(arow, smem, s_begin, s_end, rot, wave - 4);
+    return;
   }
+  if (wave == 4 + DMA_ALOADERS) {
+    dma_load_w<QT, MT, true>(W, padded_blocks((size_t)N * (K >> 8)), N, K, n0, smem, s_begin,
+                             s_end, rot);
+    return;
+  }
+  floatx4 acc[MT][2];
+  dma_compute<QT, MT, MT>(N, K, n0, smem, s_begin, s_end, rot, acc);
+  prefill_epilogue<MT, 2>(acc, R, Y, P, M, N, m0, n0, sp, splits);
 }
 
 // Y = sum over splits of P + R, rounded once to f16.
@@ -109,8 +169,22 @@ static hipError_t launch_prefill_t(const uint8_t* W, const f16* A, const f16* R,
   const int S_total = K / KSTAGE;
   const int per = (S_total + splits - 1) / splits;
   const int grid = tiles_m * tiles_n * splits;
+#if FCG_PREFILL_DMA
+  static_assert(NT == 2, "the loader-wave tile is 128 weight rows wide");
+  constexpr int lds = DmaCfg<QT, MT>::LDS;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t ea = hipFuncSetAttribute((const void*)prefill_dma_kernel<QT, MT>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (ea != hipSuccess) return ea;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((prefill_dma_kernel<QT, MT>), dim3(grid), dim3(DMA_THREADS), lds, st, W, A, R,
+                     Y, P, M, N, K, tiles_m, tiles_n, splits, per);
+#else
   hipLaunchKernelGGL((prefill_kernel<QT, MT, NT>), dim3(grid), dim3(256), 0, st, W, A, R, Y, P, M,
                      N, K, tiles_m, tiles_n, splits, per);
+#endif
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const long long MN = (long long)M * N;
