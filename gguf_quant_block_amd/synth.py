@@ -6,6 +6,9 @@ no matmul).  It is the one module that both the CPU oracle tests and the HIP
 path's tests and benchmark use, so that both sides see identical inputs.
 
 Block byte slots used here (GGUF super-block structs, 256 values per block):
+  Q4_K, 144 B: d f16 @0, dmin f16 @2, 12 packed scale/min bytes @4,
+               qs[128] @16 (the struct printed in the onnxruntime-mobius
+               GGUF proposal, section 7.3).
   Q5_K, 176 B: d f16 @0, dmin f16 @2, 12 packed scale/min bytes @4,
                qh[32] @16, qs[128] @48
                (field order as in the onnxruntime-mobius GGUF proposal,
@@ -17,6 +20,8 @@ Block byte slots used here (GGUF super-block structs, 256 values per block):
 Value distributions (all uniform unless stated):
   Q5_K: d in [1e-3, 1e-2], dmin in [0, 5e-3] (f64 draws rounded to f16 with
         round-to-nearest-even); scale/min bytes, qh and qs uniform bytes.
+  Q4_K: as Q5_K, with d in [2e-3, 2e-2] (4-bit codes need twice the step
+        for a similar weight range).
   Q6_K: ql, qh uniform bytes; sc uniform integers in [-32, 31]; d as Q5_K.
   Activations and residuals: f32 N(0,1) draws rounded to f16.
   MoE routing: Zipf(s) popularity over a seeded permutation of the experts,
@@ -32,6 +37,7 @@ from __future__ import annotations
 import numpy as np
 
 QK = 256
+Q4K_BYTES = 144
 Q5K_BYTES = 176
 Q6K_BYTES = 210
 
@@ -44,6 +50,18 @@ def rng(cfg: int, case: int, tag: int) -> np.random.Generator:
 
 def _f16_uniform(g: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
     return g.uniform(lo, hi, size=shape).astype(np.float16)
+
+
+def q4k_blocks(N: int, K: int, g: np.random.Generator) -> np.ndarray:
+    """u8[N, K/256*144]: row-major (n, kb) AoS Q4_K super-blocks."""
+    assert K % QK == 0
+    nb = K // QK
+    raw = g.integers(0, 256, size=(N, nb, Q4K_BYTES), dtype=np.uint8)
+    d = _f16_uniform(g, (N, nb), 2e-3, 2e-2)
+    dmin = _f16_uniform(g, (N, nb), 0.0, 5e-3)
+    raw[:, :, 0:2] = d.view(np.uint8).reshape(N, nb, 2)
+    raw[:, :, 2:4] = dmin.view(np.uint8).reshape(N, nb, 2)
+    return raw.reshape(N, nb * Q4K_BYTES)
 
 
 def q5k_blocks(N: int, K: int, g: np.random.Generator) -> np.ndarray:
@@ -71,6 +89,8 @@ def q6k_blocks(N: int, K: int, g: np.random.Generator) -> np.ndarray:
 
 
 def blocks(qtype: str, N: int, K: int, g: np.random.Generator) -> np.ndarray:
+    if qtype == "q4_k":
+        return q4k_blocks(N, K, g)
     if qtype == "q5_k":
         return q5k_blocks(N, K, g)
     if qtype == "q6_k":
@@ -79,7 +99,7 @@ def blocks(qtype: str, N: int, K: int, g: np.random.Generator) -> np.ndarray:
 
 
 def block_bytes(qtype: str) -> int:
-    return {"q5_k": Q5K_BYTES, "q6_k": Q6K_BYTES}[qtype]
+    return {"q4_k": Q4K_BYTES, "q5_k": Q5K_BYTES, "q6_k": Q6K_BYTES}[qtype]
 
 
 def normal_f16(shape, g: np.random.Generator) -> np.ndarray:

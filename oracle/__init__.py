@@ -1,4 +1,4 @@
-"""CPU oracle for the fully-connected layer on GGUF Q5_K / Q6_K blocks.
+"""CPU oracle for the fully-connected layer on GGUF Q4_K / Q5_K / Q6_K blocks.
 
 TEST INFRASTRUCTURE ONLY.  Plain, slow, obviously correct NumPy code in
 float64 (integer sums in int64), written from the method's description and

@@ -1,4 +1,4 @@
-"""Fully-connected reference: Y = A.W^T (+R) on GGUF Q5_K / Q6_K blocks.
+"""Fully-connected reference: Y = A.W^T (+R) on GGUF Q4_K / Q5_K / Q6_K blocks.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -36,8 +36,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .kquant import (QK, as_blocks, dequantize, q5k_codes, q5k_scale_min,
-                     q6k_codes, q6k_scales, _f16_at)
+from .kquant import (QK, as_blocks, dequantize, q4k_codes, q4k_scale_min, q5k_codes,
+                     q5k_scale_min, q6k_codes, q6k_scales, _f16_at)
 
 GROUP = 32
 
@@ -106,8 +106,8 @@ def dequant_act(qa: np.ndarray, s: np.ndarray) -> np.ndarray:
 def int_dots(qa: np.ndarray, w_bytes: np.ndarray, qtype: str) -> np.ndarray:
     """Exact integer dot sums per (m, n, sub-block).
 
-    Q5_K: S[m,n,j] = sum over the 32 values of sub-block j of qa*q, q in [0,31];
-          shape [M, N, K/32].
+    Q4_K, Q5_K: S[m,n,j] = sum over the 32 values of sub-block j of qa*q,
+          q in [0,15] / [0,31]; shape [M, N, K/32].
     Q6_K: S[m,n,s] = sum over the 16 values of sub-block s of qa*(q-32);
           shape [M, N, K/16].
     """
@@ -115,8 +115,9 @@ def int_dots(qa: np.ndarray, w_bytes: np.ndarray, qtype: str) -> np.ndarray:
     N, nb = blk.shape[:2]
     K = nb * QK
     M = qa.shape[0]
-    if qtype == "q5_k":
-        q = q5k_codes(blk).reshape(N, K)
+    if qtype in ("q4_k", "q5_k"):
+        codes = q4k_codes if qtype == "q4_k" else q5k_codes
+        q = codes(blk).reshape(N, K)
         width = 32
     else:
         q = q6k_codes(blk).reshape(N, K) - 32
@@ -129,7 +130,7 @@ def int_dots(qa: np.ndarray, w_bytes: np.ndarray, qtype: str) -> np.ndarray:
 def fc_ref_int8(A, w_bytes, qtype, R=None):
     """float64[M, N]: the decode path's result, combined explicitly.
 
-    Q5_K: y = sum_j s_j * (d*sc_j*S_j - dmin*m_j*T_j) + R
+    Q4_K, Q5_K: y = sum_j s_j * (d*sc_j*S_j - dmin*m_j*T_j) + R
     Q6_K: y = sum_s s_{s//2} * d*sc_s*S_s + R
     """
     qa, s, T = quantize_act(A)
@@ -138,10 +139,11 @@ def fc_ref_int8(A, w_bytes, qtype, R=None):
     N, nb = blk.shape[:2]
     M = A.shape[0]
     s64 = s.astype(np.float64)
-    if qtype == "q5_k":
+    if qtype in ("q4_k", "q5_k"):
         d = _f16_at(blk, 0)                      # [N, nb]
         dmin = _f16_at(blk, 2)
-        sc, mn = q5k_scale_min(blk)              # [N, nb, 8]
+        scale_min = q4k_scale_min if qtype == "q4_k" else q5k_scale_min
+        sc, mn = scale_min(blk)                  # [N, nb, 8]
         dsc = (d[..., None] * sc).reshape(N, nb * 8)
         dmm = (dmin[..., None] * mn).reshape(N, nb * 8)
         term = (S * dsc[None]) - dmm[None] * T.astype(np.float64)[:, None, :]

@@ -1,4 +1,4 @@
-"""GGUF Q5_K / Q6_K super-block formats, decoded exactly to float64.
+"""GGUF Q4_K / Q5_K / Q6_K super-block formats, decoded exactly to float64.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -12,8 +12,12 @@ Sources.
     section 7.3 (the K-quant header d | dmin | 12 packed 6-bit scale/min
     bytes, and the roles sub_scale = sc*d, sub_min = m*dmin, value =
     q*sub_scale - sub_min).
-  Q5_K weights are w = d*sc_j*q - dmin*m_j with q in [0,31]; Q6_K weights are
-  w = d*sc_s*(q - 32) with q in [0,63] and a signed 8-bit scale per 16 values.
+  * onnxruntime-mobius "GGUF Support Proposal", section 7.3 (Q4_K): the
+    144-byte struct d | dmin | scales[12] | qs[128], 32-value sub-blocks with
+    a 6-bit scale and a 6-bit min each, value = q*sc*d - m*dmin.
+  Q5_K weights are w = d*sc_j*q - dmin*m_j with q in [0,31]; Q4_K weights
+  have the same form with q in [0,15]; Q6_K weights are w = d*sc_s*(q - 32)
+  with q in [0,63] and a signed 8-bit scale per 16 values.
 
 Readings where the pages are silent (bit positions are not printed; these
 follow the GGUF on-disk convention of the reference runtime the pages name):
@@ -24,6 +28,9 @@ follow the GGUF on-disk convention of the reference runtime the pages name):
           j < 4 : sc_j = b[j] & 63,  m_j = b[j+4] & 63
           j >= 4: sc_j = (b[j+4] & 15) | (b[j-4] >> 6) << 4
                   m_j  = (b[j+4] >> 4) | (b[j]   >> 6) << 4
+  Q4_K  bytes 0-1 d, 2-3 dmin, 4-15 scales (packed as for Q5_K), 16-143 qs.
+        Code of value i: qs[16 + 32*(i//64) + i%32] (block byte offset), low
+        half if (i%64) < 32 else high half; sub-block j = i//32.
   Q6_K  bytes 0-127 ql, 128-191 qh, 192-207 sc (int8), 208-209 d.
         Value i: h = i//128, r = i%128, g = r//32, l = r%32.
         Low nibble: ql[64h + 32*(g%2) + l] >> 4*(g//2) & 15.
@@ -37,6 +44,7 @@ from __future__ import annotations
 import numpy as np
 
 QK = 256
+Q4K_BYTES = 144
 Q5K_BYTES = 176
 Q6K_BYTES = 210
 
@@ -89,6 +97,35 @@ def decode_q5k(blk: np.ndarray) -> np.ndarray:
     return d * sc[..., j].astype(np.float64) * q - dmin * m[..., j].astype(np.float64)
 
 
+# ----------------------------------------------------------------- Q4_K ----
+
+def q4k_scale_min(blk: np.ndarray):
+    """(sc[..., 8], m[..., 8]) int64 of a Q4_K block: the header (d, dmin,
+    12 scale bytes) is laid out exactly as Q5_K's, so the fields are too."""
+    return q5k_scale_min(blk)
+
+
+def q4k_codes(blk: np.ndarray) -> np.ndarray:
+    """int64[..., 256]: the 4-bit code q_i in [0, 15] of every value."""
+    qs = blk[..., 16:144].astype(np.int64)
+    q = np.empty(blk.shape[:-1] + (QK,), dtype=np.int64)
+    for i in range(QK):
+        byte = qs[..., 32 * (i // 64) + i % 32]
+        q[..., i] = (byte & 15) if (i % 64) < 32 else (byte >> 4)
+    return q
+
+
+def decode_q4k(blk: np.ndarray) -> np.ndarray:
+    """float64[..., 256]: w_i = q_i*(sc_j*d) - m_j*dmin, j = i//32 (exact)."""
+    assert blk.shape[-1] == Q4K_BYTES
+    d = _f16_at(blk, 0)[..., None]
+    dmin = _f16_at(blk, 2)[..., None]
+    sc, m = q4k_scale_min(blk)
+    q = q4k_codes(blk).astype(np.float64)
+    j = np.arange(QK) // 32
+    return q * (sc[..., j].astype(np.float64) * d) - m[..., j].astype(np.float64) * dmin
+
+
 # ----------------------------------------------------------------- Q6_K ----
 
 def q6k_codes(blk: np.ndarray) -> np.ndarray:
@@ -123,7 +160,7 @@ def decode_q6k(blk: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------ matrices ----
 
 def block_bytes(qtype: str) -> int:
-    return {"q5_k": Q5K_BYTES, "q6_k": Q6K_BYTES}[qtype]
+    return {"q4_k": Q4K_BYTES, "q5_k": Q5K_BYTES, "q6_k": Q6K_BYTES}[qtype]
 
 
 def as_blocks(w_bytes: np.ndarray, qtype: str) -> np.ndarray:
@@ -137,7 +174,7 @@ def as_blocks(w_bytes: np.ndarray, qtype: str) -> np.ndarray:
 def dequantize(w_bytes: np.ndarray, qtype: str) -> np.ndarray:
     """u8[N, K/256*B] -> float64[N, K], exact."""
     blk = as_blocks(w_bytes, qtype)
-    dec = decode_q5k if qtype == "q5_k" else decode_q6k
+    dec = {"q4_k": decode_q4k, "q5_k": decode_q5k, "q6_k": decode_q6k}[qtype]
     N, nb = blk.shape[:2]
     return dec(blk).reshape(N, nb * QK)
 
@@ -175,6 +212,22 @@ def q6k_ungroup(planes: np.ndarray, N: int, K: int) -> np.ndarray:
 
 # --------------------------------------------- encoders (hand-built blocks) --
 
+def _pack_scale_min(sc, m) -> list:
+    """The 12 scale bytes of a Q4_K / Q5_K header from 8 scales and 8 mins
+    (6 bits each): low 6 bits of sc_0..3 and m_0..3 in bytes 0-3 and 4-7,
+    the low nibbles of sc_4..7 | m_4..7 << 4 in bytes 8-11, and the top two
+    bits of sc_4..7 / m_4..7 in bits 6-7 of bytes 0-3 / 4-7."""
+    b = [0] * 12
+    for j in range(4):
+        b[j] |= sc[j] & 63
+        b[j + 4] |= m[j] & 63
+    for j in range(4, 8):
+        b[j + 4] |= (sc[j] & 15) | ((m[j] & 15) << 4)
+        b[j - 4] |= (sc[j] >> 4) << 6
+        b[j] |= (m[j] >> 4) << 6
+    return b
+
+
 def encode_q5k(d: float, dmin: float, sc, m, q) -> np.ndarray:
     """Build one Q5_K block from fields: d, dmin (f16), sc/m (8 x 6-bit),
     q (256 x 5-bit codes).  Inverse of the decoder's field extraction."""
@@ -186,21 +239,31 @@ def encode_q5k(d: float, dmin: float, sc, m, q) -> np.ndarray:
     out = np.zeros(Q5K_BYTES, dtype=np.uint8)
     out[0:2] = np.array([d], dtype=np.float16).view(np.uint8)
     out[2:4] = np.array([dmin], dtype=np.float16).view(np.uint8)
-    b = [0] * 12
-    for j in range(4):
-        b[j] |= sc[j] & 63
-        b[j + 4] |= m[j] & 63
-    for j in range(4, 8):
-        b[j + 4] |= (sc[j] & 15) | ((m[j] & 15) << 4)
-        b[j - 4] |= (sc[j] >> 4) << 6
-        b[j] |= (m[j] >> 4) << 6
-    out[4:16] = b
+    out[4:16] = _pack_scale_min(sc, m)
     for i in range(QK):
         j, l = i // 32, i % 32
         low, high = q[i] & 15, q[i] >> 4
         k = 48 + 32 * (i // 64) + l
         out[k] |= low if (i % 64) < 32 else (low << 4)
         out[16 + l] |= high << j
+    return out
+
+
+def encode_q4k(d: float, dmin: float, sc, m, q) -> np.ndarray:
+    """Build one Q4_K block from d, dmin (f16), sc/m (8 x 6-bit) and q
+    (256 x 4-bit codes), field by field."""
+    sc = [int(x) for x in sc]
+    m = [int(x) for x in m]
+    q = [int(x) for x in q]
+    assert len(sc) == 8 and len(m) == 8 and len(q) == QK
+    assert all(0 <= x < 64 for x in sc + m) and all(0 <= x < 16 for x in q)
+    out = np.zeros(Q4K_BYTES, dtype=np.uint8)
+    out[0:2] = np.array([d], dtype=np.float16).view(np.uint8)
+    out[2:4] = np.array([dmin], dtype=np.float16).view(np.uint8)
+    out[4:16] = _pack_scale_min(sc, m)
+    for c in range(4):                 # 64-value chunk c: qs[32c + l]
+        for l in range(32):
+            out[16 + 32 * c + l] = q[64 * c + l] | (q[64 * c + 32 + l] << 4)
     return out
 
 

@@ -30,7 +30,7 @@ def _inputs(qtype, M, N, K, seed, with_r=True):
     return w, A, R
 
 
-@pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
+@pytest.mark.parametrize("qtype", ["q4_k", "q5_k", "q6_k"])
 def test_decode_equals_exact_fraction_formula(qtype):
     w = synth.blocks(qtype, 2, 512, synth.rng(97, 11, 0))
     blk = kq.as_blocks(w, qtype)
@@ -39,11 +39,11 @@ def test_decode_equals_exact_fraction_formula(qtype):
         for kb in range(2):
             b = blk[n, kb]
             for i in range(0, 256, 7):
-                if qtype == "q5_k":
+                if qtype in ("q4_k", "q5_k"):
                     d = Fraction(float(b[0:2].view(np.float16)[0]))
                     dmin = Fraction(float(b[2:4].view(np.float16)[0]))
                     sc, m = kq.q5k_scale_min(b)
-                    q = kq.q5k_codes(b)[i]
+                    q = (kq.q4k_codes if qtype == "q4_k" else kq.q5k_codes)(b)[i]
                     exact = d * int(sc[i // 32]) * int(q) - dmin * int(m[i // 32])
                 else:
                     d = Fraction(float(b[208:210].view(np.float16)[0]))
@@ -51,7 +51,7 @@ def test_decode_equals_exact_fraction_formula(qtype):
                 assert Fraction(float(W[n, 256 * kb + i])) == exact
 
 
-@pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
+@pytest.mark.parametrize("qtype", ["q4_k", "q5_k", "q6_k"])
 def test_fc_ref_matches_exact_rational(qtype):
     M, N, K = 2, 3, 256
     w, A, R = _inputs(qtype, M, N, K, 12)
@@ -116,21 +116,23 @@ def test_quantize_zero_group_and_invariants():
 
 # ------------------------------------------------------------ int dots ----
 
-@pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
+@pytest.mark.parametrize("qtype", ["q4_k", "q5_k", "q6_k"])
 def test_int_dots_brute_force(qtype):
     M, N, K = 2, 3, 512
     w, A, _ = _inputs(qtype, M, N, K, 14, with_r=False)
     qa, _, _ = fc.quantize_act(A)
     S = fc.int_dots(qa, w, qtype)
     blk = kq.as_blocks(w, qtype)
-    width = 32 if qtype == "q5_k" else 16
+    width = 16 if qtype == "q6_k" else 32
     for m in range(M):
         for n in range(N):
             for sb in range(K // width):
                 acc = 0
                 for k in range(sb * width, sb * width + width):
                     b = blk[n, k // 256]
-                    if qtype == "q5_k":
+                    if qtype == "q4_k":
+                        q = int(kq.q4k_codes(b)[k % 256])
+                    elif qtype == "q5_k":
                         q = int(kq.q5k_codes(b)[k % 256])
                     else:
                         q = int(kq.q6k_codes(b)[k % 256]) - 32
@@ -140,7 +142,7 @@ def test_int_dots_brute_force(qtype):
 
 # ------------------------------------------------------- int8 emulation ----
 
-@pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
+@pytest.mark.parametrize("qtype", ["q4_k", "q5_k", "q6_k"])
 @pytest.mark.parametrize("with_r", [False, True])
 def test_int8_emulation_identity(qtype, with_r):
     M, N, K = 3, 8, 1024

@@ -1,4 +1,4 @@
-"""Pins for the oracle's block decoders (CPU only).
+"""Pins for the oracle's Q4_K / Q5_K / Q6_K block decoders (CPU only).
 
 The decoders are checked against (a) blocks whose bytes are written out by
 hand with the expected weights derived by hand from the layout reading, (b) a
@@ -145,6 +145,64 @@ def test_q5k_subnormal_dmin_is_exact():
     assert np.array_equal(w, np.full(256, -63 * dmin))
 
 
+# ------------------------------------------------------------ Q4_K pins ----
+
+def q4k_block(d=1.0, dmin=0.0, scale_bytes=None, qs=0):
+    b = np.zeros(144, dtype=np.uint8)
+    b[0:2] = f16_bytes(d)
+    b[2:4] = f16_bytes(dmin)
+    if scale_bytes is not None:
+        b[4:16] = scale_bytes
+    b[16:144] = qs
+    return b
+
+
+def test_q4k_hand_placed_bytes():
+    g = _golden("q4k_hand_block.txt")
+    b = q4k_block(d=1.0, dmin=1.0, scale_bytes=[int(x, 16) for x in g["scales"][0]])
+    for field, idx, val in g["set"]:
+        assert field == "qs"
+        b[16 + int(idx)] = int(val, 16)
+    expect = np.zeros(256)
+    for lo, hi, v in g["fill"]:
+        expect[int(lo):int(hi) + 1] = float(v)
+    for i, v in g["w"]:
+        expect[int(i)] = float(v)
+    assert np.array_equal(kq.decode_q4k(b), expect)
+
+
+def test_q4k_header_matches_q5k_header():
+    # the same 12 scale bytes give the same fields in both formats
+    sc4, m4 = kq.q4k_scale_min(q4k_block(scale_bytes=GOLD_SCALE_BYTES))
+    assert list(sc4) == GOLD_SC and list(m4) == GOLD_M
+
+
+def test_q4k_d_sc_q_closed_form():
+    # d=1, dmin=0, qs = 0xFF -> q = 15 everywhere, w = sc_j * 15
+    w = kq.decode_q4k(q4k_block(d=1.0, dmin=0.0, scale_bytes=GOLD_SCALE_BYTES, qs=0xFF))
+    assert np.array_equal(w, np.array([GOLD_SC[i // 32] * 15.0 for i in range(256)]))
+
+
+def test_q4k_dmin_closed_form():
+    # d=0, dmin=1 -> w = -m_j, whatever the codes
+    w = kq.decode_q4k(q4k_block(d=0.0, dmin=1.0, scale_bytes=GOLD_SCALE_BYTES, qs=0x3C))
+    assert np.array_equal(w, np.array([-float(GOLD_M[i // 32]) for i in range(256)]))
+
+
+def test_q4k_nibble_halves():
+    # qs = 0x21: every low nibble 1, every high nibble 2 -> values 0-31 of
+    # each 64-value chunk have q = 1, values 32-63 have q = 2
+    w = kq.decode_q4k(q4k_block(d=1.0, dmin=0.0, scale_bytes=[1, 1, 1, 1, 0, 0, 0, 0, 1, 1, 1, 1],
+                                qs=0x21))
+    assert np.array_equal(w, np.array([1.0 if (i % 64) < 32 else 2.0 for i in range(256)]))
+
+
+def test_q4k_subnormal_d_is_exact():
+    d = float(np.float16(2.0 ** -21))
+    w = kq.decode_q4k(q4k_block(d=d, dmin=0.0, scale_bytes=[0xFF] * 12, qs=0x77))
+    assert np.array_equal(w, np.full(256, 7 * 63 * d))
+
+
 # --------------------------------------------------------------- bit probe --
 # Forward tables: (byte, bit) -> which value/field changes.  They are written
 # from the layout reading in the byte->field direction, the opposite of the
@@ -171,18 +229,40 @@ def _q5k_probe_prediction(base, byte, bit):
         i = 32 * bit + l
         dw[i] = d * sc[bit] * 16 * sign
     elif 4 <= byte < 16:                      # packed 6-bit scale/min
-        p = byte - 4
-        if p < 4:
-            field, j, pos = ("sc", p, bit) if bit < 6 else ("sc", p + 4, 4 + bit - 6)
-        elif p < 8:
-            field, j, pos = ("m", p - 4, bit) if bit < 6 else ("m", p, 4 + bit - 6)
-        else:
-            field, j, pos = ("sc", p - 4, bit) if bit < 4 else ("m", p - 4, bit - 4)
-        delta = sign * (1 << pos)
-        for i in range(32 * j, 32 * j + 32):
-            dw[i] = d * delta * q[i] if field == "sc" else -dmin * delta
+        _scale_byte_prediction(dw, byte - 4, bit, sign, d, dmin, q)
     else:
         return None                           # d / dmin: checked separately
+    return dw
+
+
+def _scale_byte_prediction(dw, p, bit, sign, d, dmin, q):
+    """Weights changed by flipping `bit` of scale byte p (Q4_K and Q5_K)."""
+    if p < 4:
+        field, j, pos = ("sc", p, bit) if bit < 6 else ("sc", p + 4, 4 + bit - 6)
+    elif p < 8:
+        field, j, pos = ("m", p - 4, bit) if bit < 6 else ("m", p, 4 + bit - 6)
+    else:
+        field, j, pos = ("sc", p - 4, bit) if bit < 4 else ("m", p - 4, bit - 4)
+    delta = sign * (1 << pos)
+    for i in range(32 * j, 32 * j + 32):
+        dw[i] = d * delta * q[i] if field == "sc" else -dmin * delta
+
+
+def _q4k_probe_prediction(base, byte, bit):
+    d = float(base[0:2].view(np.float16)[0])
+    dmin = float(base[2:4].view(np.float16)[0])
+    sc, _ = kq.q4k_scale_min(base)
+    q = kq.q4k_codes(base)
+    sign = -1 if (int(base[byte]) >> bit) & 1 else 1
+    dw = np.zeros(256)
+    if 16 <= byte < 144:                      # qs: byte 16 + 32c + l
+        c, l = (byte - 16) // 32, (byte - 16) % 32
+        i = 64 * c + l + (32 if bit >= 4 else 0)
+        dw[i] = d * sc[i // 32] * sign * (1 << (bit % 4))
+    elif 4 <= byte < 16:
+        _scale_byte_prediction(dw, byte - 4, bit, sign, d, dmin, q)
+    else:
+        return None
     return dw
 
 
@@ -213,13 +293,14 @@ def _q6k_probe_prediction(base, byte, bit):
     return dw
 
 
-@pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
+@pytest.mark.parametrize("qtype", ["q4_k", "q5_k", "q6_k"])
 def test_bit_probe_every_bit(qtype):
     from gguf_quant_block_amd import synth
     g = synth.rng(99, 0, 0)
     base = synth.blocks(qtype, 1, 256, g)[0]
-    dec = kq.decode_q5k if qtype == "q5_k" else kq.decode_q6k
-    pred = _q5k_probe_prediction if qtype == "q5_k" else _q6k_probe_prediction
+    dec = {"q4_k": kq.decode_q4k, "q5_k": kq.decode_q5k, "q6_k": kq.decode_q6k}[qtype]
+    pred = {"q4_k": _q4k_probe_prediction, "q5_k": _q5k_probe_prediction,
+            "q6_k": _q6k_probe_prediction}[qtype]
     w0 = dec(base)
     nbits = 0
     for byte in range(base.size):
@@ -234,7 +315,7 @@ def test_bit_probe_every_bit(qtype):
             assert np.allclose(got, dw, rtol=0, atol=1e-12 * max(1.0, np.abs(w0).max())), (byte, bit)
             nbits += 1
     # every bit except the f16 header words is probed
-    assert nbits == 8 * (base.size - (4 if qtype == "q5_k" else 2))
+    assert nbits == 8 * (base.size - (2 if qtype == "q6_k" else 4))
 
 
 def test_header_words_scale_all_weights():
@@ -243,6 +324,15 @@ def test_header_words_scale_all_weights():
     b5 = synth.q5k_blocks(1, 256, synth.rng(99, 1, 0))[0]
     sc, m = kq.q5k_scale_min(b5)
     q = kq.q5k_codes(b5)
+    b4 = synth.q4k_blocks(1, 256, synth.rng(99, 6, 0))[0]
+    sc4, m4 = kq.q4k_scale_min(b4)
+    q4 = kq.q4k_codes(b4)
+    for d, dmin in ((1.0, 0.0), (0.0, 1.0), (0.25, 2.0)):
+        b = b4.copy()
+        b[0:2] = f16_bytes(d)
+        b[2:4] = f16_bytes(dmin)
+        j = np.arange(256) // 32
+        assert np.array_equal(kq.decode_q4k(b), q4 * (sc4[j] * d) - m4[j] * dmin)
     for d, dmin in ((1.0, 0.0), (0.0, 1.0), (0.25, 2.0)):
         b = b5.copy()
         b[0:2] = f16_bytes(d)
@@ -270,6 +360,12 @@ def test_encode_decode_round_trip():
         j = np.arange(256) // 32
         assert np.array_equal(kq.decode_q5k(b), d * sc[j] * q - dmin * m[j])
 
+        q4 = g.integers(0, 16, 256)
+        b4 = kq.encode_q4k(d, dmin, sc, m, q4)
+        sc4, m4 = kq.q4k_scale_min(b4)
+        assert (sc4 == sc).all() and (m4 == m).all() and (kq.q4k_codes(b4) == q4).all()
+        assert np.array_equal(kq.decode_q4k(b4), q4 * (sc[j] * d) - m[j] * dmin)
+
         sc6 = g.integers(-32, 32, 16)
         q6 = g.integers(0, 64, 256)
         b6 = kq.encode_q6k(d, sc6, q6)
@@ -281,6 +377,9 @@ def test_encode_decode_round_trip():
 
 def test_random_blocks_decode_codes_in_range():
     from gguf_quant_block_amd import synth
+    b4 = kq.as_blocks(synth.q4k_blocks(4, 1024, synth.rng(99, 5, 0)), "q4_k")
+    q4 = kq.q4k_codes(b4)
+    assert q4.min() == 0 and q4.max() == 15
     b5 = kq.as_blocks(synth.q5k_blocks(4, 1024, synth.rng(99, 3, 0)), "q5_k")
     q5 = kq.q5k_codes(b5)
     assert q5.min() >= 0 and q5.max() <= 31
