@@ -15,9 +15,9 @@ import threading
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfcgguf.so")
 
-Q5_K, Q6_K = 5, 6
-QTYPES = {"q5_k": Q5_K, "q6_k": Q6_K}
-BLOCK_BYTES = {Q5_K: 176, Q6_K: 210}
+Q4_K, Q5_K, Q6_K = 4, 5, 6
+QTYPES = {"q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
+BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
 PATHS = {"auto": 0, "decode": 1, "prefill": 2}
 
 _lib = None
@@ -101,7 +101,7 @@ def _blocks_arg(blocks):
 
 
 class FcGguf:
-    """One weight matrix W[N, K] in GGUF Q5_K or Q6_K blocks, resident on the GPU.
+    """One weight matrix W[N, K] in GGUF Q4_K, Q5_K or Q6_K blocks, resident on the GPU.
 
     y = fc(A, R=None, out=None): A f16 [..., K] on cuda; R f16 [..., N] or None.
     """
@@ -179,7 +179,7 @@ class FcGguf:
     def debug_int_dots(self, qa):
         torch = _torch()
         M = qa.shape[0]
-        ns = self.K // (32 if self.qtype == "q5_k" else 16)
+        ns = self.K // (16 if self.qtype == "q6_k" else 32)
         S = torch.empty((M, self.N, ns), dtype=torch.int32, device=qa.device)
         _check(lib().fc_gguf_debug_int_dots(self._h, _ptr(qa.contiguous()), M, _ptr(S), _stream()),
                "fc_gguf_debug_int_dots")

@@ -13,8 +13,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte register chunk
 
 constexpr int QK = 256;          // values per super-block
+constexpr int Q4K_BYTES = 144;   // d, dmin, scales[12], qs[128]
 constexpr int Q5K_BYTES = 176;   // d, dmin, scales[12], qh[32], qs[128]
 constexpr int Q6K_BYTES = 210;   // ql[128], qh[64], sc[16], d
+constexpr int QT_Q4K = 4;
 constexpr int QT_Q5K = 5;
 constexpr int QT_Q6K = 6;
 
@@ -32,5 +34,10 @@ __device__ __forceinline__ int dot4(int a, int b, int c) {
 }
 
 __device__ __forceinline__ int sext8(uint32_t x) { return (int)(int8_t)(x & 0xFF); }
+
+// bytes per super-block and 16-byte pieces per block (Q6_K: the sum over its planes)
+__host__ __device__ constexpr int block_bytes_of(int qt) {
+  return qt == QT_Q4K ? Q4K_BYTES : (qt == QT_Q5K ? Q5K_BYTES : Q6K_BYTES);
+}
 
 }  // namespace fcg

@@ -16,7 +16,7 @@
 struct fc_gguf {
   int64_t E = 1, N = 0, K = 0;
   int qtype = 0;
-  uint8_t* w = nullptr;         // device weights (Q5_K AoS; Q6_K planes, per expert)
+  uint8_t* w = nullptr;         // device weights (Q4_K / Q5_K blocks; Q6_K planes; per expert)
   size_t expert_bytes = 0;      // bytes of one [N, K] matrix
   int path = FC_GGUF_PATH_AUTO;
   int device = 0;
@@ -31,7 +31,12 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
 int block_bytes(int qtype) {
-  return qtype == FC_GGUF_Q5_K ? 176 : (qtype == FC_GGUF_Q6_K ? 210 : 0);
+  switch (qtype) {
+    case FC_GGUF_Q4_K: return 144;
+    case FC_GGUF_Q5_K: return 176;
+    case FC_GGUF_Q6_K: return 210;
+    default: return 0;
+  }
 }
 
 int hip_fail(fc_gguf* h, hipError_t e) {
@@ -246,7 +251,7 @@ int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S,
   if (!h || M < 0 || h->E != 1) return FC_GGUF_EINVAL;
   if (M == 0) return FC_GGUF_OK;
   if (!qa || !S || !aligned(qa, 16)) return FC_GGUF_EINVAL;
-  const int ns = (int)(h->K / (h->qtype == FC_GGUF_Q5_K ? 32 : 16));
+  const int ns = (int)(h->K / (h->qtype == FC_GGUF_Q6_K ? 16 : 32));
   if (M * h->N * ns > ((int64_t)1 << 31)) return FC_GGUF_ERANGE;
   hipError_t e = fcg::launch_debug_int_dots(h->qtype, h->w, qa, (int)M, (int)h->N, (int)h->K, S,
                                             (hipStream_t)stream);

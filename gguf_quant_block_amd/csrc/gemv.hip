@@ -1,5 +1,5 @@
 // Decode path (M < 8): per-32 int8 activation quantisation fused into an
-// int8 GEMV that streams the raw Q5_K / Q6_K blocks once.
+// int8 GEMV that streams the raw Q4_K / Q5_K / Q6_K blocks once.
 //
 // OpenVINO PR #39119, section Implementation: the GEMV quantises the
 // activations per 32 values and takes int8 dot products directly against the
@@ -15,8 +15,9 @@
 //     for the activation loads, which complete first) into LDS: int8 codes
 //     (16-byte chunks XOR-swizzled by the block index so lanes on different
 //     blocks hit different banks) and a per-(row, block) record of the f32
-//     group scales s and the code sums the scale algebra needs (Q5_K: s*T per
-//     32-group for the min term; Q6_K: 16-value sums for the -32 offset).
+//     group scales s and the code sums the scale algebra needs (Q4_K, Q5_K:
+//     s*T per 32-group for the min term; Q6_K: 16-value sums for the -32
+//     offset).
 //     The weights arrive meanwhile.
 //   * After the barrier each lane decodes its block with compile-time field
 //     offsets, takes v_dot4_i32_i8 integer sums per sub-block and applies the
@@ -39,6 +40,7 @@ template <int QT> struct GemvFmt;
 template <> struct GemvFmt<QT_Q5K> {
   static constexpr int REC = 20;           // words per (m, kb) record: s[8], s*T[8], pad[4]
 };
+template <> struct GemvFmt<QT_Q4K> : GemvFmt<QT_Q5K> {};
 template <> struct GemvFmt<QT_Q6K> {
   static constexpr int REC = 28;           // s[8], T16[16], pad[4]
 };
@@ -177,7 +179,7 @@ __device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4 raw
     *(uint4*)(smem + qa_chunk(m, K, kb, t16 + 1)) = make_uint4(q[4], q[5], q[6], q[7]);
     uint32_t* r = rec + ((size_t)m * KB + kb) * REC;
     r[g] = __builtin_bit_cast(uint32_t, s);
-    if constexpr (QT == QT_Q5K) {
+    if constexpr (QT != QT_Q6K) {
       r[8 + g] = __builtin_bit_cast(uint32_t, s * (float)tsum);
     } else {
       r[8 + 2 * g] = (uint32_t)thalf[0];
@@ -223,17 +225,23 @@ __device__ __forceinline__ void quant_finish(const f16* A, int K, uint8_t* smem,
 // Q5_K: 176 B = d|dmin, scales[12], qh[32], qs[128] (11 x 16 B).  For the
 // sub-block pair (2c, 2c+1): qs[32c + l] low nibble -> value 64c + l, high
 // nibble -> 64c + 32 + l; bits 2c / 2c+1 of qh[l] are the fifth bits.
-// lo[w] / hi[w]: packed codes (0..31) of values 64c + 4w.. / 64c + 32 + 4w..
-template <int C>
-__device__ __forceinline__ void q5k_codes(const uint32_t* qh, const uint32_t* qs, uint32_t* lo,
-                                          uint32_t* hi) {
+// Q4_K: 144 B = d|dmin, scales[12], qs[128] (9 x 16 B); the same nibbles,
+// no fifth bit (mobius GGUF proposal, section 7.3).
+// lo[w] / hi[w]: packed codes (0..31 / 0..15) of values 64c + 4w.. /
+// 64c + 32 + 4w..
+template <int QT, int C>
+__device__ __forceinline__ void q45k_codes(const uint32_t* qh, const uint32_t* qs, uint32_t* lo,
+                                           uint32_t* hi) {
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
-    const uint32_t d = qs[8 * C + w], h = qh[w];
-    const uint32_t hl = (4 - 2 * C >= 0 ? h << (4 - 2 * C) : h >> (2 * C - 4)) & 0x10101010u;
-    const uint32_t hh = (3 - 2 * C >= 0 ? h << (3 - 2 * C) : h >> (2 * C - 3)) & 0x10101010u;
-    lo[w] = (d & 0x0F0F0F0Fu) | hl;
-    hi[w] = ((d >> 4) & 0x0F0F0F0Fu) | hh;
+    const uint32_t d = qs[8 * C + w];
+    lo[w] = d & 0x0F0F0F0Fu;
+    hi[w] = (d >> 4) & 0x0F0F0F0Fu;
+    if constexpr (QT == QT_Q5K) {
+      const uint32_t h = qh[w];
+      lo[w] |= (4 - 2 * C >= 0 ? h << (4 - 2 * C) : h >> (2 * C - 4)) & 0x10101010u;
+      hi[w] |= (3 - 2 * C >= 0 ? h << (3 - 2 * C) : h >> (2 * C - 3)) & 0x10101010u;
+    }
   }
 }
 
@@ -260,10 +268,11 @@ __device__ __forceinline__ int dot16u(const uint32_t* c, uint4 a) {
 
 // ------------------------------------------------------- block kernels ----
 
-// Q5_K block -> part[m] (lane's contribution to row m): blk = the 44 words.
-template <int MR>
-__device__ __forceinline__ void q5k_block(const uint32_t* blk, int kb, int K, const uint8_t* smem,
-                                          const uint32_t* rec, int KB, float* part) {
+// Q4_K / Q5_K block -> part[m] (lane's contribution to row m): blk = the
+// block's 36 / 44 words.
+template <int QT, int MR>
+__device__ __forceinline__ void q45k_block(const uint32_t* blk, int kb, int K, const uint8_t* smem,
+                                           const uint32_t* rec, int KB, float* part) {
   const float d = h2f(blk[0]), dmin = h2f(blk[0] >> 16);
   const uint32_t w0 = blk[1], w1 = blk[2], w2 = blk[3];
   // 6-bit scales / mins as bytes: j = 0..3 and j = 4..7
@@ -271,14 +280,14 @@ __device__ __forceinline__ void q5k_block(const uint32_t* blk, int kb, int K, co
   const uint32_t sc_hi = (w2 & 0x0F0F0F0Fu) | ((w0 >> 2) & 0x30303030u);
   const uint32_t m_hi = ((w2 >> 4) & 0x0F0F0F0Fu) | ((w1 >> 2) & 0x30303030u);
   const uint32_t* qh = blk + 4;
-  const uint32_t* qs = blk + 12;
+  const uint32_t* qs = blk + (QT == QT_Q5K ? 12 : 4);
   float X[MR], Z[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) X[m] = Z[m] = 0.f;
   auto pair = [&](auto cc) {
     constexpr int C = decltype(cc)::value;
     uint32_t lo[8], hi[8];
-    q5k_codes<C>(qh, qs, lo, hi);
+    q45k_codes<QT, C>(qh, qs, lo, hi);
     const uint32_t scw = C < 2 ? sc_lo : sc_hi, mw = C < 2 ? m_lo : m_hi;
     const float sc0 = (float)((scw >> (16 * (C & 1))) & 0xFF), sc1 = (float)((scw >> (16 * (C & 1) + 8)) & 0xFF);
     const float mn0 = (float)((mw >> (16 * (C & 1))) & 0xFF), mn1 = (float)((mw >> (16 * (C & 1) + 8)) & 0xFF);
@@ -290,7 +299,7 @@ __device__ __forceinline__ void q5k_block(const uint32_t* blk, int kb, int K, co
       const uint4 a3 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C + 3));
       const int S0 = dot16u(lo, a0) + dot16u(lo + 4, a1);
       const int S1 = dot16u(hi, a2) + dot16u(hi + 4, a3);
-      const uint32_t* r = rec + ((size_t)m * KB + kb) * GemvFmt<QT_Q5K>::REC;
+      const uint32_t* r = rec + ((size_t)m * KB + kb) * GemvFmt<QT>::REC;
       const float2 s2 = *(const float2*)(r + 2 * C);
       const float2 t2 = *(const float2*)(r + 8 + 2 * C);
       X[m] = fmaf(sc0, s2.x * (float)S0, X[m]);
@@ -377,11 +386,12 @@ __device__ __forceinline__ void wait_all_and_sync_wave() {
 // waves issue no weight loads, so their activation loads return from L2 and
 // the quantisation completes while the weights are still in flight.
 // The lane's whole super-block, straight from global memory into registers
-// (Q5_K: its 11 pieces; Q6_K: its QL, QH, SC and D bytes).  In the device
+// (Q4_K / Q5_K: its 9 / 11 pieces; Q6_K: its QL, QH, SC and D bytes).  In the device
 // layout the lanes of a wave own consecutive blocks, so every piece load of
 // the wave is one or two contiguous runs.
 struct GemvBlock {
-  uint32_t w[48];     // Q5_K: the 176 bytes in w[0..43]; Q6_K: ql in w[0..31], qh in w[32..47]
+  uint32_t w[48];     // Q4_K / Q5_K: the 144 / 176 bytes in w[0..35] / w[0..43];
+                      // Q6_K: ql in w[0..31], qh in w[32..47]
   uint4 scv;          // Q6_K scales
   uint32_t dbits;     // Q6_K d
 };
@@ -395,10 +405,11 @@ struct GemvBlock {
 
 template <int QT>
 __device__ __forceinline__ void load_block(const uint8_t* W, size_t nbp, size_t gb, GemvBlock& b) {
-  if constexpr (QT == QT_Q5K) {
+  if constexpr (QT != QT_Q6K) {
+    constexpr int P = block_bytes_of(QT) / 16;
 #pragma unroll
-    for (int c = 0; c < 11; ++c) {
-      const uint4 v = *(const uint4*)(W + piece_off(gb, 11, c));
+    for (int c = 0; c < P; ++c) {
+      const uint4 v = *(const uint4*)(W + piece_off(gb, P, c));
       b.w[4 * c] = v.x; b.w[4 * c + 1] = v.y; b.w[4 * c + 2] = v.z; b.w[4 * c + 3] = v.w;
       FCG_KEEP_ORDER();
     }
@@ -479,10 +490,10 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
     if (r > 0) load_block<QT>(W, nbp, j < nb_w ? gb_w + j : 0, blk);
     if (j < nb_w) {
       const int kb = j % KB;
-      if constexpr (QT == QT_Q5K)
-        q5k_block<MR>(blk.w, kb, K, smem, rec, KB, part);
-      else
+      if constexpr (QT == QT_Q6K)
         q6k_block<MR>(blk.w, blk.w + 32, blk.scv, blk.dbits, kb, K, smem, rec, KB, part);
+      else
+        q45k_block<QT, MR>(blk.w, kb, K, smem, rec, KB, part);
     }
   }
   // row sums in lane order, + R, store
@@ -561,11 +572,16 @@ static hipError_t launch_gemv_q(const uint8_t* W, const f16* A, const f16* R, f1
 }
 
 size_t gemv_lds_bytes(int qtype, int M, int K) {
-  return qtype == QT_Q5K ? gemv_layout<QT_Q5K>(M, K).total : gemv_layout<QT_Q6K>(M, K).total;
+  switch (qtype) {
+    case QT_Q4K: return gemv_layout<QT_Q4K>(M, K).total;
+    case QT_Q5K: return gemv_layout<QT_Q5K>(M, K).total;
+    default: return gemv_layout<QT_Q6K>(M, K).total;
+  }
 }
 
 hipError_t launch_gemv(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, int M,
                        int N, int K, hipStream_t st) {
+  if (qtype == QT_Q4K) return launch_gemv_q<QT_Q4K>(W, A, R, Y, M, N, K, st);
   if (qtype == QT_Q5K) return launch_gemv_q<QT_Q5K>(W, A, R, Y, M, N, K, st);
   return launch_gemv_q<QT_Q6K>(W, A, R, Y, M, N, K, st);
 }
@@ -609,7 +625,7 @@ hipError_t launch_debug_quantize(const f16* A, int M, int K, int8_t* qa, float* 
 }
 
 // Integer sub-block sums with the GEMV's code routines: one thread per block
-// (n, kb), blocks read straight from global memory (Q5_K AoS / Q6_K planes).
+// (n, kb), blocks read straight from the device layout.
 template <int QT>
 __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ qa,
                                       int M, int N, int K, int* __restrict__ S) {
@@ -619,11 +635,12 @@ __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_
   const int n = (int)(gb / KB), kb = (int)(gb % KB);
   const size_t nbp = padded_blocks((size_t)N * KB);
   const uint4 ones = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
-  if constexpr (QT == QT_Q5K) {
+  if constexpr (QT != QT_Q6K) {
+    constexpr int P = block_bytes_of(QT) / 16;
     uint32_t blk[44];
 #pragma unroll
-    for (int c = 0; c < 11; ++c) {
-      const uint4 v = *(const uint4*)(W + piece_off((size_t)gb, 11, c));
+    for (int c = 0; c < P; ++c) {
+      const uint4 v = *(const uint4*)(W + piece_off((size_t)gb, P, c));
       blk[4 * c] = v.x; blk[4 * c + 1] = v.y; blk[4 * c + 2] = v.z; blk[4 * c + 3] = v.w;
     }
     const int ns = K / 32;
@@ -633,7 +650,7 @@ __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_
       auto pair = [&](auto cc) {
         constexpr int C = decltype(cc)::value;
         uint32_t lo[8], hi[8];
-        q5k_codes<C>(blk + 4, blk + 12, lo, hi);
+        q45k_codes<QT, C>(blk + 4, blk + (QT == QT_Q5K ? 12 : 4), lo, hi);
         out[2 * C] = dot16u(lo, a[4 * C]) + dot16u(lo + 4, a[4 * C + 1]);
         out[2 * C + 1] = dot16u(hi, a[4 * C + 2]) + dot16u(hi + 4, a[4 * C + 3]);
       };
@@ -682,7 +699,9 @@ hipError_t launch_debug_int_dots(int qtype, const uint8_t* W, const int8_t* qa, 
                                  int* S, hipStream_t st) {
   const long long total = (long long)N * (K / QK);
   const int grid = (int)((total + 255) / 256);
-  if (qtype == QT_Q5K)
+  if (qtype == QT_Q4K)
+    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q4K>, dim3(grid), dim3(256), 0, st, W, qa, M, N, K, S);
+  else if (qtype == QT_Q5K)
     hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q5K>, dim3(grid), dim3(256), 0, st, W, qa, M, N, K, S);
   else
     hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q6K>, dim3(grid), dim3(256), 0, st, W, qa, M, N, K, S);

@@ -8,6 +8,7 @@
 // owns block 64g + l therefore reads every piece with one fully coalesced
 // 1 KB access (wave64 x 16 B), instead of 64 accesses 176 or 210 bytes apart.
 // The block count is padded to a multiple of 64 with zero bytes.
+//   Q4_K: one plane, P = 9 (the 144 bytes of the block, in order).
 //   Q5_K: one plane, P = 11 (the 176 bytes of the block, in order).
 //   Q6_K: the QL | QH | SC | D planes of OpenVINO PR #39119 (section
 //         Transformation), each over the padded block count: QL P = 8,

@@ -16,10 +16,11 @@
 //   A: BM rows x 16 chunks of 16 B; chunk c of row r sits at position
 //      c ^ (r & 15) of the row, so that the 16 rows of an MFMA operand read
 //      hit 16 distinct bank groups;
-//   W: 7 pieces x 128 rows x 16 B (the 16-byte pieces of the half-block
+//   W: WP pieces x 128 rows x 16 B (the 16-byte pieces of the half-block
 //      that the decode reads: Q5_K header, the two fifth-bit pieces, four
-//      code pieces; Q6_K four QL pieces, two QH pieces, the scales), then for
-//      Q6_K the 4-byte word holding each row's d.
+//      code pieces (WP = 7); Q4_K header and four code pieces (WP = 5); Q6_K
+//      four QL pieces, two QH pieces, the scales (WP = 7)), then for Q6_K
+//      the 4-byte word holding each row's d.
 // One barrier per stage: a compute wave reaches it after reading its slot,
 // a loader wave after its loads for the next stage have landed.
 #pragma once
@@ -41,14 +42,14 @@ namespace fcg {
 constexpr int DMA_SLOTS = FCG_DMA_SLOTS;          // LDS ring depth (stages)
 constexpr int DMA_ALOADERS = FCG_DMA_ALOADERS;    // waves loading the activation tile
 constexpr int DMA_THREADS = 64 * (4 + DMA_ALOADERS + 1);
-constexpr int DMA_WP = 7;                 // weight pieces per row per stage
 
 template <int QT, int MT>
 struct DmaCfg {
   static constexpr int BM = 16 * MT;
   static constexpr int BN = 128;
+  static constexpr int WP = QT == QT_Q4K ? 5 : 7;   // weight pieces per row per stage
   static constexpr int A_BYTES = BM * 256;
-  static constexpr int W_BYTES = DMA_WP * BN * 16 + (QT == QT_Q6K ? BN * 4 : 0);
+  static constexpr int W_BYTES = WP * BN * 16 + (QT == QT_Q6K ? BN * 4 : 0);
   static constexpr int SLOT = A_BYTES + W_BYTES;
   static constexpr int LDS = DMA_SLOTS * SLOT;
 };
@@ -128,7 +129,7 @@ template <int QT, int MT, bool IL>
 __device__ __forceinline__ void dma_load_w(const uint8_t* W, size_t nbp, int N, int K, int n0,
                                            uint8_t* smem, int s_begin, int s_end, int rot) {
   using C = DmaCfg<QT, MT>;
-  constexpr int NI = 2 * DMA_WP + (QT == QT_Q6K ? 2 : 0);
+  constexpr int NI = 2 * C::WP + (QT == QT_Q6K ? 2 : 0);
   const int lane = threadIdx.x & 63;
   const int nst = s_end - s_begin;
   const int KB = K >> 8;
@@ -151,10 +152,12 @@ __device__ __forceinline__ void dma_load_w(const uint8_t* W, size_t nbp, int N, 
     for (int h = 0; h < 2; ++h) {
       const size_t b = rb[h] + kb;
 #pragma unroll
-      for (int q = 0; q < DMA_WP; ++q) {
+      for (int q = 0; q < C::WP; ++q) {
         size_t off;
         if constexpr (QT == QT_Q5K) {
           off = piece(b, 11, q < 3 ? q : q + 4 * hb);
+        } else if constexpr (QT == QT_Q4K) {
+          off = piece(b, 9, q < 1 ? q : q + 4 * hb);
         } else {
           if (q < 4) off = piece(b, 8, 4 * hb + q);
           else if (q < 6) off = q6k_qh_base(nbp) + piece(b, 4, 2 * hb + (q - 4));
@@ -163,7 +166,7 @@ __device__ __forceinline__ void dma_load_w(const uint8_t* W, size_t nbp, int N, 
         dma16(W + off, base + (q * 128 + 64 * h) * 16);
       }
       if constexpr (QT == QT_Q6K)
-        dma4(W + q6k_d_base(nbp) + ((2 * b) & ~(size_t)3), base + DMA_WP * 128 * 16 + 64 * h * 4);
+        dma4(W + q6k_d_base(nbp) + ((2 * b) & ~(size_t)3), base + C::WP * 128 * 16 + 64 * h * 4);
     }
   };
   constexpr int AHEAD = DMA_SLOTS - 1;
@@ -231,13 +234,19 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
         r.qsA = *(const uint2*)(pc(3 + pq) + sub);
         r.qsB = *(const uint2*)(pc(5 + pq) + sub);
         decode_q5k_half(r, hb, wf[j]);
+      } else if constexpr (QT == QT_Q4K) {
+        RawQ4 r;
+        r.hdr = *(const uint4*)pc(0);
+        r.qsA = *(const uint2*)(pc(1 + pq) + sub);
+        r.qsB = *(const uint2*)(pc(3 + pq) + sub);
+        decode_q4k_half(r, hb, wf[j]);
       } else {
         RawQ6 r;
         r.qlA = *(const uint2*)(pc(pq) + sub);
         r.qlB = *(const uint2*)(pc(2 + pq) + sub);
         r.qh = *(const uint2*)(pc(4 + pq) + sub);
         r.sc = *(const uint2*)(pc(6) + 8 * hb);
-        const uint32_t dw = *(const uint32_t*)(Ws + DMA_WP * 128 * 16 + 4 * nloc[j]);
+        const uint32_t dw = *(const uint32_t*)(Ws + C::WP * 128 * 16 + 4 * nloc[j]);
         r.d = dw >> (16 * (int)((rb[j] + kb) & 1));
         decode_q6k_half(r, kq, wf[j]);
       }

@@ -18,7 +18,8 @@
 //     registers.  Decoding is exact up to one f16 rounding:
 //       magic f16 (1024 + q) from a byte permute, t = fma(1024+q, sc, -1024*sc
 //       [Q6_K: -1056*sc]) = sc*q [sc*(q-32)] exactly, then w = t*d - dmin*m
-//       [Q6_K: t*d] with a single rounding.
+//       [Q6_K: t*d] with a single rounding (Q4_K as Q5_K, without the fifth
+//       bit).
 //   * Only the first MTA 16-row halves of the tile are staged and run on the
 //     matrix cores: a tile whose rows end early skips its empty halves
 //     (llama.cpp PR #28301, section Overview, skips the empty upper half of
@@ -43,6 +44,11 @@ struct RawQ5 {  // one lane, one row, one half-block
   uint2 qsA;    // qs[64hb + 8kq .. +8]      : sub-blocks 4hb+0 (lo), 4hb+1 (hi)
   uint2 qsB;    // qs[64hb + 32 + 8kq .. +8] : sub-blocks 4hb+2 (lo), 4hb+3 (hi)
   uint2 qh;     // qh[8kq .. +8]
+};
+struct RawQ4 {  // one lane, one row, one half-block
+  uint4 hdr;    // d | dmin, scales[0..3], scales[4..7], scales[8..11]
+  uint2 qsA;    // qs[64hb + 8kq .. +8]      : sub-blocks 4hb+0 (lo), 4hb+1 (hi)
+  uint2 qsB;    // qs[64hb + 32 + 8kq .. +8] : sub-blocks 4hb+2 (lo), 4hb+3 (hi)
 };
 struct RawQ6 {
   uint2 qlA;    // ql[64hb + 8kq .. +8]      : groups g=0 (lo), g=2 (hi)
@@ -83,8 +89,10 @@ __device__ __forceinline__ half8v decode8(uint32_t c0, uint32_t c1, half2v sc2, 
 __device__ __forceinline__ half2v splat(f16 x) { half2v r; r[0] = x; r[1] = x; return r; }
 
 // Decode the lane's 4 x 8 weights of one half-block (k-step g = 0..3 covers
-// values 128hb + 32g + 8kq .. +7 of its row).
-__device__ __forceinline__ void decode_q5k_half(const RawQ5& r, int hb, half8v out[4]) {
+// values 128hb + 32g + 8kq .. +7 of its row).  Q4_K: HAS_QH = false and the
+// fifth-bit words are ignored.
+template <bool HAS_QH, class Raw>
+__device__ __forceinline__ void decode_q45k_half(const Raw& r, uint2 qh, int hb, half8v out[4]) {
   const uint32_t w0 = r.hdr.y, w1 = r.hdr.z, w2 = r.hdr.w;
   uint32_t scb, mb;   // bytes g = 0..3: scale / min of sub-block 4hb + g
   if (hb == 0) {
@@ -103,8 +111,12 @@ __device__ __forceinline__ void decode_q5k_half(const RawQ5& r, int hb, half8v o
   for (int g = 0; g < 4; ++g) {
     const int sh = 4 * (g & 1);
     const int j = 4 * hb + g;
-    const uint32_t c0 = ((src[g] >> sh) & 0x0F0F0F0Fu) | (((r.qh.x >> j) & 0x01010101u) << 4);
-    const uint32_t c1 = ((src1[g] >> sh) & 0x0F0F0F0Fu) | (((r.qh.y >> j) & 0x01010101u) << 4);
+    uint32_t c0 = (src[g] >> sh) & 0x0F0F0F0Fu;
+    uint32_t c1 = (src1[g] >> sh) & 0x0F0F0F0Fu;
+    if constexpr (HAS_QH) {
+      c0 |= ((qh.x >> j) & 0x01010101u) << 4;
+      c1 |= ((qh.y >> j) & 0x01010101u) << 4;
+    }
     const int sc = (scb >> (8 * g)) & 0xFF;
     const int mn = (mb >> (8 * g)) & 0xFF;
     const f16 scf = (f16)(float)sc;
@@ -113,6 +125,13 @@ __device__ __forceinline__ void decode_q5k_half(const RawQ5& r, int hb, half8v o
     const half2v negdmm2 = splat((f16)(-(dmin * (float)mn)));
     out[g] = decode8(c0, c1, sc2, bias2, d2, negdmm2);
   }
+}
+
+__device__ __forceinline__ void decode_q5k_half(const RawQ5& r, int hb, half8v out[4]) {
+  decode_q45k_half<true>(r, r.qh, hb, out);
+}
+__device__ __forceinline__ void decode_q4k_half(const RawQ4& r, int hb, half8v out[4]) {
+  decode_q45k_half<false>(r, uint2{0u, 0u}, hb, out);
 }
 
 __device__ __forceinline__ void decode_q6k_half(const RawQ6& r, int kq, half8v out[4]) {
@@ -151,7 +170,7 @@ struct TileRows {
 // stage s_begin + rot (wrapping), for the first MTA (<= MT) 16-row halves of
 // the tile.  W is one weight matrix [N, K] over nbp (padded) blocks, in the
 // piece-interleaved device layout of layout.h (IL) or in the canonical one
-// (Q5_K blocks in order; Q6_K row-major QL | QH | SC | D planes).  n0 is its
+// (Q4_K / Q5_K blocks in order; Q6_K row-major QL | QH | SC | D planes).  n0 is its
 // first weight row (rows past N are clamped to N - 1: loaded, never stored).
 // acc[i][j] receives C[n][m] of the 16x16 sub-tile (half i < MTA, weight
 // sub-tile j).  A stage is SH half super-blocks (128*SH values of K; stages
@@ -200,6 +219,17 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
       raw[j].qh = *(const uint2*)(W + piece(b, 11, 1 + pq) + sub);
     }
   };
+  auto load_raw_q4 = [&](int s, RawQ4* raw) {
+    const int kb = s >> 1, hb = s & 1;
+    const int sub = 8 * (kq & 1), pq = kq >> 1;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const size_t b = (size_t)nrow[j] * KB + kb;
+      raw[j].hdr = *(const uint4*)(W + piece(b, 9, 0));
+      raw[j].qsA = *(const uint2*)(W + piece(b, 9, 1 + 4 * hb + pq) + sub);
+      raw[j].qsB = *(const uint2*)(W + piece(b, 9, 3 + 4 * hb + pq) + sub);
+    }
+  };
   auto load_raw_q6 = [&](int s, RawQ6* raw) {
     const int kb = s >> 1, hb = s & 1;
     const int sub = 8 * (kq & 1), pq = kq >> 1;
@@ -213,12 +243,15 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
       raw[j].d = *(const uint16_t*)(W + q6k_d_base(nbp) + 2 * b);
     }
   };
-  using Raw = typename std::conditional<QT == QT_Q5K, RawQ5, RawQ6>::type;
+  using Raw = typename std::conditional<
+      QT == QT_Q5K, RawQ5, typename std::conditional<QT == QT_Q4K, RawQ4, RawQ6>::type>::type;
   // the raw bytes of stage s: its SH half-blocks (half index SH*s + x)
   auto load_raw = [&](int s, Raw (*raw)[NT]) {
 #pragma unroll
     for (int x = 0; x < SH; ++x) {
-      if constexpr (QT == QT_Q5K) load_raw_q5(SH * s + x, raw[x]); else load_raw_q6(SH * s + x, raw[x]);
+      if constexpr (QT == QT_Q5K) load_raw_q5(SH * s + x, raw[x]);
+      else if constexpr (QT == QT_Q4K) load_raw_q4(SH * s + x, raw[x]);
+      else load_raw_q6(SH * s + x, raw[x]);
     }
   };
 
@@ -248,6 +281,7 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         if constexpr (QT == QT_Q5K) decode_q5k_half(raw[x][j], (SH * s + x) & 1, wf[j]);
+        else if constexpr (QT == QT_Q4K) decode_q4k_half(raw[x][j], (SH * s + x) & 1, wf[j]);
         else decode_q6k_half(raw[x][j], kq, wf[j]);
       }
 #pragma unroll

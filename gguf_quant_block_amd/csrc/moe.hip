@@ -1,4 +1,4 @@
-// Grouped (MoE expert) FC on Q5_K / Q6_K blocks: every expert's routed rows
+// Grouped (MoE expert) FC on Q4_K / Q5_K / Q6_K blocks: every expert's routed rows
 // times that expert's weights, all experts in one launch.
 //
 // llama.cpp PR #28301 (Metal mul_mm_id), section Overview: the routed rows are
@@ -254,7 +254,9 @@ hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, i
   if (e != hipSuccess) return e;
 #define FCG_MOE(QT_, MT_) \
   if (mt == MT_) return launch_grouped_t<QT_, MT_>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
-  if (qtype == QT_Q5K) {
+  if (qtype == QT_Q4K) {
+    FCG_MOE(QT_Q4K, 2) FCG_MOE(QT_Q4K, 4) FCG_MOE(QT_Q4K, 8)
+  } else if (qtype == QT_Q5K) {
     FCG_MOE(QT_Q5K, 2) FCG_MOE(QT_Q5K, 4) FCG_MOE(QT_Q5K, 8)
   } else {
     FCG_MOE(QT_Q6K, 2) FCG_MOE(QT_Q6K, 4) FCG_MOE(QT_Q6K, 8)

@@ -1,4 +1,4 @@
-// Prefill path (M >= 8): f16 matrix-core FC on raw Q5_K / Q6_K blocks.
+// Prefill path (M >= 8): f16 matrix-core FC on raw Q4_K / Q5_K / Q6_K blocks.
 //
 // OpenVINO PR #39119, section Implementation: each 256-value weight block is
 // decoded once into on-chip memory and reused across many activation rows,
@@ -218,7 +218,9 @@ hipError_t launch_prefill(int qtype, const uint8_t* W, const f16* A, const f16* 
                           int M, int N, int K, int mt, int nt, int splits, hipStream_t st) {
 #define FCG_PF(QT_, MT_, NT_)                                                   \
   if (mt == MT_ && nt == NT_) return launch_prefill_t<QT_, MT_, NT_>(W, A, R, Y, P, M, N, K, splits, st);
-  if (qtype == QT_Q5K) {
+  if (qtype == QT_Q4K) {
+    FCG_PF(QT_Q4K, 1, 2) FCG_PF(QT_Q4K, 2, 2) FCG_PF(QT_Q4K, 4, 2) FCG_PF(QT_Q4K, 8, 2)
+  } else if (qtype == QT_Q5K) {
     FCG_PF(QT_Q5K, 1, 2) FCG_PF(QT_Q5K, 2, 2) FCG_PF(QT_Q5K, 4, 2) FCG_PF(QT_Q5K, 8, 2)
   } else {
     FCG_PF(QT_Q6K, 1, 2) FCG_PF(QT_Q6K, 2, 2) FCG_PF(QT_Q6K, 4, 2) FCG_PF(QT_Q6K, 8, 2)

@@ -1,6 +1,6 @@
 /*
  * fc_gguf.h -- fully-connected layer computed directly on GGUF K-quant
- * weight blocks (Q5_K, Q6_K) on an AMD Instinct MI355X (gfx950).
+ * weight blocks (Q4_K, Q5_K, Q6_K) on an AMD Instinct MI355X (gfx950).
  *
  *   Y[M,N] = A[M,K] . W[N,K]^T (+ R[M,N])
  *
@@ -11,7 +11,7 @@
  *     K/256 * block_bytes, so K must be a multiple of 256;
  *   - section "Transformation": the weights are converted once; Q6_K blocks
  *     are regrouped into the planes QL|QH|SC|D (done on the device at create
- *     time here, where every plane, and the Q5_K blocks, are also
+ *     time here, where every plane, and the Q4_K / Q5_K blocks, are also
  *     piece-interleaved over groups of 64 blocks for coalesced wave64 loads);
  *   - section "Implementation": the path is chosen from the number of
  *     activation rows M: M < 8 -> per-32 int8 activation quantisation and an
@@ -19,6 +19,9 @@
  *     memory and reused across rows on f16 matrix cores, with a tile that
  *     grows with M; a same-shape residual Add is fused into the store;
  *     GPU_GGUF_PREFILL_PATH-style forcing of a path for testing.
+ * Q4_K, which that PR leaves on its converted path, is taken on the same
+ * paths here; its 144-byte block is the struct printed in the
+ * onnxruntime-mobius "GGUF Support Proposal", section 7.3.
  * The grouped (MoE) entry points follow llama.cpp PR #28301 (Metal
  * mul_mm_id), section Overview: each expert's routed rows are multiplied by
  * that expert's weights in one launch, and under-filled row tiles skip their
@@ -47,6 +50,7 @@ extern "C" {
 typedef struct fc_gguf* fc_gguf_t;
 
 /* Quantisation types (this library's own numbering). */
+#define FC_GGUF_Q4_K 4   /* 144 B per 256 values: d, dmin, 12 B scales/mins, qs[128] */
 #define FC_GGUF_Q5_K 5   /* 176 B per 256 values: d, dmin, 12 B scales/mins, qh[32], qs[128] */
 #define FC_GGUF_Q6_K 6   /* 210 B per 256 values: ql[128], qh[64], sc[16] (int8), d */
 
@@ -128,17 +132,18 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
  *
  * fc_gguf_debug_int_dots: the integer sub-block dot sums of the decode path,
  *   from given int8 activations qa device i8[M,K].  S device i32:
- *   Q5_K [M, N, K/32] (sum of qa*q over each 32-value sub-block, q in [0,31]);
+ *   Q4_K, Q5_K [M, N, K/32] (sum of qa*q over each 32-value sub-block,
+ *   q in [0,15] / [0,31]);
  *   Q6_K [M, N, K/16] (sum of qa*(q-32) over each 16-value sub-block).
  *
  * fc_gguf_debug_weights: copies the handle's device weight bytes to device
  *   memory `dst` (fc_gguf_info's weight_bytes long).  Device layout, per
  *   matrix (experts one after another): blocks b = n*(K/256) + kb, padded
- *   with zero bytes to a multiple of 64.  Q5_K: one plane of P = 11 pieces
- *   (16 bytes) per block.  Q6_K: planes QL (P = 8) | QH (P = 4) | SC (16 B
+ *   with zero bytes to a multiple of 64.  Q4_K / Q5_K: one plane of P = 9 /
+ *   P = 11 pieces (16 bytes) per block.  Q6_K: planes QL (P = 8) | QH (P = 4) | SC (16 B
  *   per block, in block order) | D (2 B per block, in block order), each over
- *   the padded block count.  Single-matrix handles store the QL, QH and Q5_K
- *   planes piece-interleaved: groups of 64 consecutive blocks piece-major,
+ *   the padded block count.  Single-matrix handles store the QL, QH, Q4_K and
+ *   Q5_K planes piece-interleaved: groups of 64 consecutive blocks piece-major,
  *   piece p of block b at ((b/64)*P + p)*1024 + (b%64)*16 within its plane.
  *   Grouped handles store every plane in block order (piece p of block b at
  *   b*16*P + 16*p).

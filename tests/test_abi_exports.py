@@ -43,7 +43,8 @@ def test_host_validation_without_gpu(L):
     # K not a multiple of 256, N <= 0, unknown qtype, NULL blocks, NULL out
     assert L.fc_gguf_create(1, 255, 5, buf, 0, ctypes.byref(h)) == -1
     assert L.fc_gguf_create(0, 256, 5, buf, 0, ctypes.byref(h)) == -1
-    assert L.fc_gguf_create(1, 256, 4, buf, 0, ctypes.byref(h)) == -2
+    for qt in (0, 3, 7, 8, -1):
+        assert L.fc_gguf_create(1, 256, qt, buf, 0, ctypes.byref(h)) == -2
     assert L.fc_gguf_create(1, 256, 5, None, 0, ctypes.byref(h)) == -1
     assert L.fc_gguf_create(1, 256, 5, buf, 0, None) == -1
     # NULL handle

@@ -17,7 +17,7 @@ from helpers import DECODE_TOL, case, maxrel
 
 pytestmark = pytest.mark.gpu
 
-QTYPES = ["q5_k", "q6_k"]
+QTYPES = ["q4_k", "q5_k", "q6_k"]
 
 
 def _dev(x):
@@ -80,9 +80,12 @@ def _interleave(plane, P):
 
 
 def expected_device_bytes(w, qtype):
-    """The library's device copy of canonical blocks w: Q5_K pieces interleaved
-    over groups of 64 blocks; Q6_K planes QL | QH | SC | D (the oracle's
-    regroup) with QL and QH interleaved the same way, zero-padded to 64 blocks."""
+    """The library's device copy of canonical blocks w: Q4_K / Q5_K pieces
+    interleaved over groups of 64 blocks; Q6_K planes QL | QH | SC | D (the
+    oracle's regroup) with QL and QH interleaved the same way, zero-padded to
+    64 blocks."""
+    if qtype == "q4_k":
+        return _interleave(w.reshape(-1, 144), 9)
     if qtype == "q5_k":
         return _interleave(w.reshape(-1, 176), 11)
     planes = okq.q6k_regroup(w)
@@ -103,6 +106,9 @@ def test_device_layout_bytes(gpu_lib, N, K):
     w5 = synth.q5k_blocks(N, K, synth.rng(51, N + 1, 0))
     got5 = _host(_fc(w5, "q5_k", N, K).debug_weights())
     assert np.array_equal(got5, expected_device_bytes(w5, "q5_k"))
+    w4 = synth.q4k_blocks(N, K, synth.rng(51, N + 2, 0))
+    got4 = _host(_fc(w4, "q4_k", N, K).debug_weights())
+    assert np.array_equal(got4, expected_device_bytes(w4, "q4_k"))
 
 
 def test_layout_helper_is_a_permutation():
@@ -182,13 +188,14 @@ def test_m_zero_is_noop(gpu_lib):
 FULL = [("q5_k", name, M) for name in synth.PHI35_LAYERS for M in (1, 2, 4, 7)]
 FULL += [("q6_k", name, M) for name in synth.PHI35_LAYERS for M in (1, 4)]
 FULL += [("q6_k", "output", M) for M in (1, 4)]
+FULL += [("q4_k", name, M) for name in synth.PHI35_LAYERS for M in (1, 3)]
 
 
 @pytest.mark.parametrize("qtype,name,M", FULL)
 def test_gemv_full_size_sampled(gpu_lib, qtype, name, M):
     N, K = synth.PHI35_OUTPUT if name == "output" else synth.PHI35_LAYERS[name]
     with_r = name != "output"
-    cfg = 1 if qtype == "q5_k" else 2
+    cfg = {"q5_k": 1, "q6_k": 2, "q4_k": 5}[qtype]
     w, A, R = case(qtype, M, N, K, cfg, list(synth.PHI35_LAYERS).index(name) if with_r else 9, with_r)
     y = _host(_fc(w, qtype, N, K)(_dev(A), None if R is None else _dev(R)))
     cols = np.sort(np.random.default_rng(N + M).choice(N, size=min(N, 192), replace=False))

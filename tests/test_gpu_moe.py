@@ -19,7 +19,7 @@ from helpers import PREFILL_TOL, relfro
 
 pytestmark = pytest.mark.gpu
 
-QTYPES = ["q5_k", "q6_k"]
+QTYPES = ["q4_k", "q5_k", "q6_k"]
 
 
 def _dev(x):
@@ -117,7 +117,7 @@ def test_grouped_device_layout_bytes(gpu_lib, qtype):
     # a multiple of 64 blocks
     from gguf_quant_block_amd.binding import FcGguf
     E, N, K = 3, 5, 512
-    bb = 176 if qtype == "q5_k" else 210
+    bb = {"q4_k": 144, "q5_k": 176, "q6_k": 210}[qtype]
     w = synth.blocks(qtype, E * N, K, synth.rng(44, 0, 0)).reshape(E, N, -1)
     got = _host(FcGguf(N, K, qtype, w, experts=E).debug_weights())
     nblk = N * K // 256
@@ -127,7 +127,7 @@ def test_grouped_device_layout_bytes(gpu_lib, qtype):
         blocks = w[e].reshape(nblk, bb)
         pad = np.zeros((64, bb), dtype=np.uint8)
         pad[:nblk] = blocks
-        if qtype == "q5_k":
+        if qtype != "q6_k":
             exp = pad.reshape(-1)
         else:
             exp = np.concatenate([pad[:, :128].reshape(-1), pad[:, 128:192].reshape(-1),

@@ -16,7 +16,7 @@ from helpers import PREFILL_TOL, case, relfro
 
 pytestmark = pytest.mark.gpu
 
-QTYPES = ["q5_k", "q6_k"]
+QTYPES = ["q4_k", "q5_k", "q6_k"]
 
 
 def _dev(x):
