@@ -23,7 +23,8 @@ Value distributions (all uniform unless stated):
   Q4_K: as Q5_K, with d in [2e-3, 2e-2] (4-bit codes need twice the step
         for a similar weight range).
   Q6_K: ql, qh uniform bytes; sc uniform integers in [-32, 31]; d as Q5_K.
-  Activations and residuals: f32 N(0,1) draws rounded to f16.
+  Activations and residuals: f32 N(0,1) draws rounded to f16 (or kept in
+  f32 for f32 activations).
   MoE routing: Zipf(s) popularity over a seeded permutation of the experts,
   top-k distinct experts per token by Gumbel-top-k (sampling without
   replacement).
@@ -104,6 +105,10 @@ def block_bytes(qtype: str) -> int:
 
 def normal_f16(shape, g: np.random.Generator) -> np.ndarray:
     return g.standard_normal(size=shape, dtype=np.float32).astype(np.float16)
+
+
+def normal_f32(shape, g: np.random.Generator) -> np.ndarray:
+    return g.standard_normal(size=shape, dtype=np.float32)
 
 
 def moe_routing(T: int, E: int, top_k: int, g: np.random.Generator, s: float = 1.1) -> np.ndarray:

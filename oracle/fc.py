@@ -25,7 +25,10 @@ by the pages):
   * activation quantisation is symmetric per aligned group of 32 values of
     one row: amax = max|a| (f32), s = fl32(amax/127), inv = fl32(127/amax),
     qa = clamp(round_half_even(fl32(a*inv)), -127, 127); an all-zero group
-    has s = 0 and qa = 0;
+    has s = 0 and qa = 0, and so has a group whose inverse scale 127/amax
+    overflows f32 (amax < 127/FLT_MAX, reachable with f32 activations only);
+  * f32 activations are quantised from their f32 values (the same steps; f16
+    activations are widened to f32 exactly first);
   * the Q5_K min term uses the sum of the quantised activations,
     s_g * T_g with T_g = sum(qa over group g), so that the decode path
     computes exactly (s*qa) . W^T;
@@ -74,7 +77,7 @@ def fc_gguf_ref(A, w_bytes, qtype, R=None):
 # ------------------------------------------- int8 activation quantisation --
 
 def quantize_act(A: np.ndarray):
-    """Per-32 symmetric int8 quantisation of f16 activations A[M, K].
+    """Per-32 symmetric int8 quantisation of f16 or f32 activations A[M, K].
 
     Returns qa int8[M, K], s float32[M, K/32], T int32[M, K/32].
     All float steps are IEEE float32 (numpy float32 division and product are
@@ -84,10 +87,12 @@ def quantize_act(A: np.ndarray):
     assert K % GROUP == 0
     a = A.astype(np.float32).reshape(M, K // GROUP, GROUP)
     amax = np.abs(a).max(axis=2)
-    nz = amax > 0
-    safe = np.where(nz, amax, np.float32(1))
+    safe = np.where(amax > 0, amax, np.float32(1))
+    with np.errstate(over="ignore"):
+        inv_all = (np.float32(127) / safe).astype(np.float32)
+    nz = (amax > 0) & np.isfinite(inv_all)
     s = np.where(nz, safe / np.float32(127), np.float32(0)).astype(np.float32)
-    inv = np.where(nz, np.float32(127) / safe, np.float32(0)).astype(np.float32)
+    inv = np.where(nz, inv_all, np.float32(0)).astype(np.float32)
     prod = (a * inv[..., None]).astype(np.float32)
     qa = np.clip(np.rint(prod), -127, 127).astype(np.int8)
     T = qa.astype(np.int32).sum(axis=2).astype(np.int32)

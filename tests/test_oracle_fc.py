@@ -114,6 +114,54 @@ def test_quantize_zero_group_and_invariants():
     assert np.array_equal(T, qa.reshape(4, 8, 32).astype(np.int32).sum(axis=2))
 
 
+def test_quantize_f32_unit_amax_matches_golden():
+    # the same closed-form group as f32 values: identical codes and scale
+    path = os.path.join(os.path.dirname(__file__), "golden", "actquant_unit_amax.txt")
+    gold = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = line.split(":", 1)
+            gold[k.strip()] = [int(x) for x in v.split()]
+    a = np.array([(k - 16) / 16 for k in range(32)], dtype=np.float32)[None]
+    qa, s, T = fc.quantize_act(a)
+    assert list(qa[0]) == gold["qa"] and T[0, 0] == gold["T"][0]
+    assert s[0, 0] == np.float32(1) / np.float32(127)
+
+
+def test_quantize_f32_groups_beyond_f16():
+    g = np.random.default_rng(8)
+    A = g.standard_normal((3, 128)).astype(np.float32)
+    A[0, :32] *= np.float32(1e-37)          # 127/amax overflows f32: a zero group
+    A[0, 32:64] = np.float32(5e-37) * np.array([(k - 16) / 16 for k in range(32)], dtype=np.float32)
+    #                                         tiny but 127/amax finite: s is subnormal
+    A[1, :32] *= np.float32(1e30)           # far beyond the f16 range
+    A[2, 5] = np.float32(1e-40)             # an f32 subnormal inside a normal group
+    qa, s, T = fc.quantize_act(A)
+    assert s[0, 0] == 0 and (qa[0, :32] == 0).all() and T[0, 0] == 0
+    amax = np.abs(A[0, 32:64]).max()
+    assert np.isfinite(np.float32(127) / amax)
+    assert s[0, 1] == amax / np.float32(127) and s[0, 1] < np.finfo(np.float32).tiny
+    assert np.abs(qa[0, 32:64].astype(int)).max() == 127
+    assert np.abs(qa[1, :32].astype(int)).max() == 127 and s[1, 0] == np.abs(A[1, :32]).max() / np.float32(127)
+    assert qa[2, 5] == 0
+    # every nonzero group: |s*q - a| <= s/2 (up to the f32 rounding of a*inv)
+    a3 = A.astype(np.float64).reshape(3, 4, 32)
+    q3 = qa.reshape(3, 4, 32).astype(np.float64)
+    for m in range(3):
+        for gi in range(4):
+            if s[m, gi] == 0:
+                continue
+            sc = float(s[m, gi])
+            assert (np.abs(sc * q3[m, gi] - a3[m, gi]) <= sc * 0.5 * (1 + 1e-5) + 1e-6 * np.abs(a3[m, gi])).all()
+
+
+def test_quantize_f16_equals_f32_of_same_values():
+    A = synth.normal_f16((2, 256), synth.rng(97, 40, 1))
+    for x, y in zip(fc.quantize_act(A), fc.quantize_act(A.astype(np.float32))):
+        assert np.array_equal(x, y)
+
+
 # ------------------------------------------------------------ int dots ----
 
 @pytest.mark.parametrize("qtype", ["q4_k", "q5_k", "q6_k"])
