@@ -30,12 +30,14 @@ _SIGS = {
     "fc_gguf_create_grouped": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_int, _vp, ctypes.c_int,
                                               ctypes.POINTER(_vp)]),
     "fc_gguf_run": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp, _vp]),
+    "fc_gguf_run_f32": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp, _vp]),
     "fc_gguf_run_grouped": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp]),
     "fc_gguf_set_path": (ctypes.c_int, [_vp, ctypes.c_int]),
     "fc_gguf_destroy": (ctypes.c_int, [_vp]),
     "fc_gguf_info": (ctypes.c_int, [_vp, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64),
                                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_c_i64)]),
     "fc_gguf_debug_quantize": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "fc_gguf_debug_quantize_f32": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
     "fc_gguf_debug_int_dots": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp]),
     "fc_gguf_debug_weights": (ctypes.c_int, [_vp, _vp, _vp]),
     "fc_gguf_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -103,7 +105,10 @@ def _blocks_arg(blocks):
 class FcGguf:
     """One weight matrix W[N, K] in GGUF Q4_K, Q5_K or Q6_K blocks, resident on the GPU.
 
-    y = fc(A, R=None, out=None): A f16 [..., K] on cuda; R f16 [..., N] or None.
+    y = fc(A, R=None, out=None): A [..., K] on cuda, f16 or f32 (any number
+    of leading dims, flattened to M rows; M may change from call to call);
+    R [..., N] of A's dtype or None; the output has A's dtype.  f32
+    activations always take the int8 GEMV path.
     """
 
     def __init__(self, N: int, K: int, qtype: str, blocks, *, experts: int | None = None):
@@ -146,17 +151,19 @@ class FcGguf:
 
     def __call__(self, A, R=None, out=None):
         torch = _torch()
-        assert A.dtype == torch.float16 and A.is_cuda and A.shape[-1] == self.K
+        dt = A.dtype
+        assert dt in (torch.float16, torch.float32) and A.is_cuda and A.shape[-1] == self.K
         lead = A.shape[:-1]
         A2 = A.reshape(-1, self.K).contiguous()
         M = A2.shape[0]
         if R is not None:
-            assert R.dtype == torch.float16 and R.shape == (*lead, self.N)
+            assert R.dtype == dt and R.shape == (*lead, self.N)
             R = R.reshape(M, self.N).contiguous()
         if out is None:
-            out = torch.empty((*lead, self.N), dtype=torch.float16, device=A.device)
-        assert out.is_contiguous() and out.dtype == torch.float16
-        _check(lib().fc_gguf_run(self._h, _ptr(A2), M, _ptr(R), _ptr(out), _stream()), "fc_gguf_run")
+            out = torch.empty((*lead, self.N), dtype=dt, device=A.device)
+        assert out.is_contiguous() and out.dtype == dt and out.shape == (*lead, self.N)
+        run = lib().fc_gguf_run if dt == torch.float16 else lib().fc_gguf_run_f32
+        _check(run(self._h, _ptr(A2), M, _ptr(R), _ptr(out), _stream()), "fc_gguf_run")
         return out
 
     def grouped(self, A, ids, a_per_slot: bool, out=None):
@@ -193,12 +200,14 @@ class FcGguf:
 
 
 def debug_quantize(A):
-    """The decode path's per-32 int8 quantisation: (qa i8[M,K], s f32[M,K/32], T i32[M,K/32])."""
+    """The decode path's per-32 int8 quantisation of f16 or f32 A[M, K]:
+    (qa i8[M,K], s f32[M,K/32], T i32[M,K/32])."""
     torch = _torch()
     M, K = A.shape
+    assert A.dtype in (torch.float16, torch.float32)
     qa = torch.empty((M, K), dtype=torch.int8, device=A.device)
     s = torch.empty((M, K // 32), dtype=torch.float32, device=A.device)
     T = torch.empty((M, K // 32), dtype=torch.int32, device=A.device)
-    _check(lib().fc_gguf_debug_quantize(_ptr(A.contiguous()), M, K, _ptr(qa), _ptr(s), _ptr(T), _stream()),
-           "fc_gguf_debug_quantize")
+    f = lib().fc_gguf_debug_quantize if A.dtype == torch.float16 else lib().fc_gguf_debug_quantize_f32
+    _check(f(_ptr(A.contiguous()), M, K, _ptr(qa), _ptr(s), _ptr(T), _stream()), "fc_gguf_debug_quantize")
     return qa, s, T

@@ -132,6 +132,46 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
   return FC_GGUF_OK;
 }
 
+// Validation shared by fc_gguf_run and fc_gguf_run_f32 (element size es).
+int check_run(fc_gguf_t h, const void* A, int64_t M, const void* R, const void* Y, size_t es) {
+  if (!h || M < 0) return FC_GGUF_EINVAL;
+  if (h->E != 1) return FC_GGUF_EINVAL;            // grouped handles use run_grouped
+  if (M == 0) return FC_GGUF_OK;
+  if (!A || !Y) return FC_GGUF_EINVAL;
+  if (M > kMaxDim || M * h->N > ((int64_t)1 << 31) || M * h->K > ((int64_t)1 << 31))
+    return FC_GGUF_ERANGE;
+  const size_t ya = es == 2 ? 8 : 4;
+  if (!aligned(A, 16) || !aligned(Y, ya) || (R && !aligned(R, ya))) return FC_GGUF_EINVAL;
+  return FC_GGUF_OK;
+}
+
+// The decode path over M rows: chunks of at most 7 rows (one launch each),
+// smaller when the quantised activations of a chunk would not fit in one CU's
+// LDS.
+template <class AT>
+hipError_t run_decode(fc_gguf_t h, const AT* a, const AT* r, AT* y, int64_t M, hipStream_t st,
+                      int* rc) {
+  const int N = (int)h->N, K = (int)h->K;
+  int cap = 7;
+  while (cap > 1 && fcg::gemv_lds_bytes(h->qtype, cap, K) > 160 * 1024) --cap;
+  if (fcg::gemv_lds_bytes(h->qtype, cap, K) > 160 * 1024) {
+    *rc = FC_GGUF_ERANGE;
+    return hipSuccess;
+  }
+  hipError_t e = hipSuccess;
+  for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += cap) {
+    const int mc = (int)(M - m0 < cap ? M - m0 : cap);
+    if constexpr (sizeof(AT) == 2)
+      e = fcg::launch_gemv(h->qtype, h->w, a + m0 * K, r ? r + m0 * N : nullptr, y + m0 * N, mc, N,
+                           K, st);
+    else
+      e = fcg::launch_gemv_f32(h->qtype, h->w, a + m0 * K, r ? r + m0 * N : nullptr, y + m0 * N, mc,
+                               N, K, st);
+  }
+  *rc = FC_GGUF_OK;
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,13 +214,8 @@ int fc_gguf_info(fc_gguf_t h, int64_t* N, int64_t* K, int* qtype, int64_t* weigh
 }
 
 int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, void* stream) {
-  if (!h || M < 0) return FC_GGUF_EINVAL;
-  if (h->E != 1) return FC_GGUF_EINVAL;            // grouped handles use run_grouped
-  if (M == 0) return FC_GGUF_OK;
-  if (!A || !Y) return FC_GGUF_EINVAL;
-  if (M > kMaxDim || M * h->N > ((int64_t)1 << 31) || M * h->K > ((int64_t)1 << 31))
-    return FC_GGUF_ERANGE;
-  if (!aligned(A, 16) || !aligned(Y, 8) || (R && !aligned(R, 8))) return FC_GGUF_EINVAL;
+  int rc = check_run(h, A, M, R, Y, 2);
+  if (rc != FC_GGUF_OK || M == 0) return rc;
   const int N = (int)h->N, K = (int)h->K;
   hipStream_t st = (hipStream_t)stream;
   int path = h->path;
@@ -190,27 +225,29 @@ int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, v
   fcg::f16* y = (fcg::f16*)Y;
   hipError_t e = hipSuccess;
   if (path == FC_GGUF_PATH_DECODE) {
-    // rows in chunks of at most 7 (one launch each), smaller when the
-    // quantised activations of a chunk would not fit in one CU's LDS
-    int cap = 7;
-    while (cap > 1 && fcg::gemv_lds_bytes(h->qtype, cap, K) > 160 * 1024) --cap;
-    if (fcg::gemv_lds_bytes(h->qtype, cap, K) > 160 * 1024) return FC_GGUF_ERANGE;
-    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += cap) {
-      const int mc = (int)(M - m0 < cap ? M - m0 : cap);
-      e = fcg::launch_gemv(h->qtype, h->w, a + m0 * K, r ? r + m0 * N : nullptr, y + m0 * N, mc,
-                           N, K, st);
-    }
+    e = run_decode(h, a, r, y, M, st, &rc);
+    if (rc != FC_GGUF_OK) return rc;
   } else {
     int mt, nt, splits;
     fcg::prefill_choose(h->qtype, (int)M, N, K, h->num_cu, &mt, &nt, &splits);
     const size_t need = fcg::prefill_workspace_bytes((int)M, N, splits);
     if (need) {
-      const int rc = ensure_ws(h, need);
+      rc = ensure_ws(h, need);
       if (rc != FC_GGUF_OK) return rc;
     }
     e = fcg::launch_prefill(h->qtype, h->w, a, r, y, (float*)h->ws, (int)M, N, K, mt, nt, splits,
                             st);
   }
+  if (e != hipSuccess) return hip_fail(h, e);
+  return FC_GGUF_OK;
+}
+
+int fc_gguf_run_f32(fc_gguf_t h, const float* A, int64_t M, const float* R, float* Y,
+                    void* stream) {
+  int rc = check_run(h, A, M, R, Y, 4);
+  if (rc != FC_GGUF_OK || M == 0) return rc;
+  const hipError_t e = run_decode(h, A, R, Y, M, (hipStream_t)stream, &rc);
+  if (rc != FC_GGUF_OK) return rc;
   if (e != hipSuccess) return hip_fail(h, e);
   return FC_GGUF_OK;
 }
@@ -242,8 +279,17 @@ int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, floa
   if (M == 0) return FC_GGUF_OK;
   if (!A || !qa || !s || !T || !aligned(A, 16) || !aligned(qa, 16)) return FC_GGUF_EINVAL;
   if (M * K > ((int64_t)1 << 31)) return FC_GGUF_ERANGE;
-  hipError_t e = fcg::launch_debug_quantize((const fcg::f16*)A, (int)M, (int)K, qa, s, T,
-                                            (hipStream_t)stream);
+  hipError_t e = fcg::launch_debug_quantize(A, false, (int)M, (int)K, qa, s, T, (hipStream_t)stream);
+  return e == hipSuccess ? FC_GGUF_OK : FC_GGUF_EHIP;
+}
+
+int fc_gguf_debug_quantize_f32(const float* A, int64_t M, int64_t K, int8_t* qa, float* s,
+                               int32_t* T, void* stream) {
+  if (M < 0 || K <= 0 || (K % 32) != 0) return FC_GGUF_EINVAL;
+  if (M == 0) return FC_GGUF_OK;
+  if (!A || !qa || !s || !T || !aligned(A, 16) || !aligned(qa, 16)) return FC_GGUF_EINVAL;
+  if (M * K > ((int64_t)1 << 31)) return FC_GGUF_ERANGE;
+  hipError_t e = fcg::launch_debug_quantize(A, true, (int)M, (int)K, qa, s, T, (hipStream_t)stream);
   return e == hipSuccess ? FC_GGUF_OK : FC_GGUF_EHIP;
 }
 

@@ -66,18 +66,17 @@ __device__ __forceinline__ int qa_chunk(int m, int K, int kb, int t) {
 
 // ------------------------------------------------ activation quantisation --
 // Per-32 int8 quantisation (OpenVINO PR #39119, sections Transformation and
-// Implementation: dynamic quantisation in groups of 32 for the int8 GEMV).
+// Implementation: dynamic quantisation in groups of 32 for the int8 GEMV;
+// f16 activations, and f32 activations at any row count, take this path).
 // Symmetric: s = amax/127, inv = 127/amax (IEEE-correct f32 divisions),
 // code = round-half-even(fl32(a * inv)); |fl32(a * inv)| <= 127.5 so no clamp
-// is needed; an all-zero group gives s = 0 and codes 0.
+// is needed.  An all-zero group, or an f32 group so small that 127/amax
+// overflows (amax < 127/FLT_MAX), gives s = 0 and codes 0.
 //
-// One lane quantises 8*V consecutive values (V = 1, 2 or 4); 4/V adjacent
-// lanes share a 32-value group and exchange its maximum, so every lane of the
-// group derives bit-identical s and inv.
-//   q[0 .. 2V):  packed int8 codes of the lane's values
+// One lane quantises one 32-value group (64 bytes of f16 or 128 of f32):
+//   q[0 .. 8):   packed int8 codes of the group's values
 //   tsum:        sum of the group's 32 codes
 //   thalf[0,1]:  sums of the group's first and second 16 codes
-// All lanes of a group must call it together (it shuffles for V < 4).
 // round-half-even(fl32(a * inv)) in the low byte of the result.  The product
 // is rounded to f32 first and only then rounded to an integer (adding 1.5*2^23
 // rounds to the nearest integer, ties to even, for |x| < 2^22); the empty asm
@@ -89,88 +88,84 @@ __device__ __forceinline__ uint32_t rne_code(float a, float inv) {
   return __builtin_bit_cast(uint32_t, p + RNE_MAGIC);
 }
 
-template <int V>
-__device__ __forceinline__ void quant_lane(const uint4* raw, uint32_t* q, float& s, int& tsum,
-                                           int* thalf) {
-  half2v m2 = {(f16)0.f, (f16)0.f};
+// 16-byte loads per 32-value group of activations of type AT
+template <class AT>
+constexpr int act_u4() { return (int)sizeof(AT) * 2; }
+
+template <class AT>
+__device__ __forceinline__ void quant_group(const uint4* raw, uint32_t* q, float& s, int& tsum,
+                                            int* thalf) {
+  constexpr int U4 = act_u4<AT>();
+  uint32_t w[4 * U4];
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(half2v, w[j] & 0x7FFF7FFFu));
+  for (int i = 0; i < U4; ++i) {
+    w[4 * i] = raw[i].x; w[4 * i + 1] = raw[i].y; w[4 * i + 2] = raw[i].z; w[4 * i + 3] = raw[i].w;
   }
-  float amax = fmaxf((float)m2[0], (float)m2[1]);
-  if constexpr (V < 4) amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  if constexpr (V < 2) amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  auto value = [&](int i) -> float {
+    if constexpr (std::is_same<AT, f16>::value) return h2f(w[i >> 1] >> (16 * (i & 1)));
+    else return __builtin_bit_cast(float, w[i]);
+  };
+  float amax;
+  if constexpr (std::is_same<AT, f16>::value) {
+    half2v m2 = {(f16)0.f, (f16)0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(half2v, w[j] & 0x7FFF7FFFu));
+    amax = fmaxf((float)m2[0], (float)m2[1]);
+  } else {
+    amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, __builtin_bit_cast(float, w[j] & 0x7FFFFFFFu));
+  }
   float inv = 0.f;
   s = 0.f;
   if (amax > 0.f) {
-    s = __fdiv_rn(amax, 127.0f);
     inv = __fdiv_rn(127.0f, amax);
+    if (inv <= 3.402823466e38f) s = __fdiv_rn(amax, 127.0f);   // inv finite
+    else inv = 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; j += 2) {
-      // four values -> four rounded floats -> the low byte of each is the code
-      const uint32_t r0 = rne_code(h2f(w[j]), inv);
-      const uint32_t r1 = rne_code(h2f(w[j] >> 16), inv);
-      const uint32_t r2 = rne_code(h2f(w[j + 1]), inv);
-      const uint32_t r3 = rne_code(h2f(w[j + 1] >> 16), inv);
-      const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x0c0c0400u);
-      const uint32_t hi = __builtin_amdgcn_perm(r3, r2, 0x0c0c0400u);
-      q[2 * i + (j >> 1)] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
+  for (int c = 0; c < 8; ++c) {
+    // four values -> four rounded floats -> the low byte of each is the code
+    const uint32_t r0 = rne_code(value(4 * c), inv);
+    const uint32_t r1 = rne_code(value(4 * c + 1), inv);
+    const uint32_t r2 = rne_code(value(4 * c + 2), inv);
+    const uint32_t r3 = rne_code(value(4 * c + 3), inv);
+    const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(r3, r2, 0x0c0c0400u);
+    q[c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
   }
   // code sums: 16-value halves and the group total
-  if constexpr (V == 4) {
-    int a = 0, b = 0;
+  int a = 0, b = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a = dot4((int)q[i], 0x01010101, a);
+  for (int i = 0; i < 4; ++i) a = dot4((int)q[i], 0x01010101, a);
 #pragma unroll
-    for (int i = 4; i < 8; ++i) b = dot4((int)q[i], 0x01010101, b);
-    thalf[0] = a;
-    thalf[1] = b;
-  } else if constexpr (V == 2) {
-    int own = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) own = dot4((int)q[i], 0x01010101, own);
-    const int other = __shfl_xor(own, 1, 64);
-    const bool first = (threadIdx.x & 1) == 0;
-    thalf[0] = first ? own : other;
-    thalf[1] = first ? other : own;
-  } else {
-    const int own = dot4((int)q[0], 0x01010101, dot4((int)q[1], 0x01010101, 0));
-    const int pair = own + __shfl_xor(own, 1, 64);
-    const int other = __shfl_xor(pair, 2, 64);
-    const bool first = (threadIdx.x & 2) == 0;
-    thalf[0] = first ? pair : other;
-    thalf[1] = first ? other : pair;
-  }
-  tsum = thalf[0] + thalf[1];
+  for (int i = 4; i < 8; ++i) b = dot4((int)q[i], 0x01010101, b);
+  thalf[0] = a;
+  thalf[1] = b;
+  tsum = a + b;
 }
 
 // Quantisation of MR rows of A into the LDS layout by the whole workgroup:
 // thread tid takes the 32-value groups (tasks) tid, tid + 256, ...  The
-// activation loads of the first QPRE rounds are issued before the weight
-// loads, so the quantisation waits only for them (loads complete in order)
-// while the weights are still in flight.
-constexpr int QPRE = 2;
+// activation loads of the first qpre<AT>() rounds are issued before the
+// weight loads, so the quantisation waits only for them (loads complete in
+// order) while the weights are still in flight.
 constexpr int GEMV_THREADS = 64 * GEMV_WAVES;
+template <class AT>
+constexpr int qpre() { return std::is_same<AT, f16>::value ? 2 : 1; }
 
-template <int QT, int MR>
-__device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4 raw[4], uint8_t* smem,
+template <int QT, int MR, class AT>
+__device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4* raw, uint8_t* smem,
                                               uint32_t* rec) {
   constexpr int REC = GemvFmt<QT>::REC;
   const int KB = K / QK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = t < tasks ? raw[i] : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < act_u4<AT>(); ++i) raw[i] = t < tasks ? raw[i] : make_uint4(0, 0, 0, 0);
   uint32_t q[8];
   float s;
   int tsum, thalf[2];
-  quant_lane<4>(raw, q, s, tsum, thalf);
+  quant_group<AT>(raw, q, s, tsum, thalf);
   if (t < tasks) {
     const int e = t * 32;                           // first value (flat over MR x K)
     const int m = e / K, pos = e - m * K;
@@ -188,36 +183,38 @@ __device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4 raw
   }
 }
 
-template <int MR>
-__device__ __forceinline__ void quant_issue(const f16* A, int K, int tid, uint4 (&raw)[QPRE][4]) {
+template <int MR, class AT>
+__device__ __forceinline__ void quant_issue(const AT* A, int K, int tid,
+                                            uint4 (&raw)[qpre<AT>()][act_u4<AT>()]) {
   const int tasks = MR * K / 32;
 #pragma unroll
-  for (int r = 0; r < QPRE; ++r) {
+  for (int r = 0; r < qpre<AT>(); ++r) {
     const int t = r * GEMV_THREADS + tid;
     const int tc = t < tasks ? t : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[r][i] = *(const uint4*)(A + (size_t)tc * 32 + 8 * i);
+    for (int i = 0; i < act_u4<AT>(); ++i) raw[r][i] = ((const uint4*)(A + (size_t)tc * 32))[i];
   }
 }
 
-template <int QT, int MR>
-__device__ __forceinline__ void quant_finish(const f16* A, int K, uint8_t* smem, int tid,
-                                             uint4 (&raw)[QPRE][4]) {
+template <int QT, int MR, class AT>
+__device__ __forceinline__ void quant_finish(const AT* A, int K, uint8_t* smem, int tid,
+                                             uint4 (&raw)[qpre<AT>()][act_u4<AT>()]) {
+  constexpr int QP = qpre<AT>(), U4 = act_u4<AT>();
   const int tasks = MR * K / 32;
   const int wbase = tid & ~63;                        // wave-uniform skip of idle waves
   uint32_t* rec = (uint32_t*)(smem + gemv_layout<QT>(MR, K).rec);
 #pragma unroll
-  for (int r = 0; r < QPRE; ++r)
+  for (int r = 0; r < QP; ++r)
     if (r * GEMV_THREADS + wbase < tasks)
-      quantise_task<QT, MR>(r * GEMV_THREADS + tid, tasks, K, raw[r], smem, rec);
-  for (int t0 = QPRE * GEMV_THREADS; t0 < tasks; t0 += GEMV_THREADS) {
+      quantise_task<QT, MR, AT>(r * GEMV_THREADS + tid, tasks, K, raw[r], smem, rec);
+  for (int t0 = QP * GEMV_THREADS; t0 < tasks; t0 += GEMV_THREADS) {
     if (t0 + wbase >= tasks) break;
     const int t = t0 + tid;
     const int tc = t < tasks ? t : 0;
-    uint4 v[4];
+    uint4 v[U4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *(const uint4*)(A + (size_t)tc * 32 + 8 * i);
-    quantise_task<QT, MR>(t, tasks, K, v, smem, rec);
+    for (int i = 0; i < U4; ++i) v[i] = ((const uint4*)(A + (size_t)tc * 32))[i];
+    quantise_task<QT, MR, AT>(t, tasks, K, v, smem, rec);
   }
 }
 
@@ -440,10 +437,11 @@ __device__ __forceinline__ void load_block(const uint8_t* W, size_t nbp, size_t 
 // loads of its lane's super-block, quantises its activation groups into LDS
 // (waiting only for the activation loads) and meets the others at the
 // barrier; the weights arrive while this happens.
-template <int QT, int MR, int V>
+// AT: the type of A, R and Y (f16, or f32 for f32 activations).
+template <int QT, int MR, class AT>
 __global__ void __launch_bounds__(GEMV_THREADS)
-gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__ R,
-            f16* __restrict__ Y, int N, int K, int rows_per_wave) {
+gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R,
+            AT* __restrict__ Y, int N, int K, int rows_per_wave) {
   extern __shared__ __align__(16) uint8_t smem[];
   const GemvLayout L = gemv_layout<QT>(MR, K);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -457,13 +455,13 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
   const size_t gb_w = (size_t)n_w * KB;               // its first block
   float* part_lds = (float*)(smem + L.part) + (size_t)wave * MR * 64;
 
-  uint4 araw[QPRE][4];
-  quant_issue<MR>(A, K, tid, araw);
+  uint4 araw[qpre<AT>()][act_u4<AT>()];
+  quant_issue<MR, AT>(A, K, tid, araw);
   // the residual of the row this lane stores (lanes < rows_w), fetched now so
   // that its latency hides under the weight stream
   // (unconditional loads from a valid address, so that nothing waits on them
   // before the weight loads are issued; without R they read A and are unused)
-  f16 rres[MR];
+  AT rres[MR];
   {
     int nr = n_w + lane;
     nr = nr < N ? nr : N - 1;
@@ -477,7 +475,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
   load_block<QT>(W, nbp, lane < nb_w ? gb_w + lane : 0, blk);
   asm volatile("" ::: "memory");                    // ... then the weight loads
 
-  quant_finish<QT, MR>(A, K, smem, tid, araw);
+  quant_finish<QT, MR, AT>(A, K, smem, tid, araw);
   barrier_after_lds_writes();                         // quantised activations ready
 
   const uint32_t* rec = (const uint32_t*)(smem + L.rec);
@@ -509,7 +507,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* __restrict__
       for (int i = 0; i < per; ++i) y += part_lds[m * 64 + first + i];
       const int n = n_w + lane;
       if (R) y += (float)rres[m];
-      Y[(size_t)m * N + n] = (f16)y;
+      Y[(size_t)m * N + n] = (AT)y;
     }
   }
 }
@@ -521,17 +519,12 @@ static int gemv_rows_per_wave(int K) {
   return KB <= 64 ? 64 / KB : 1;
 }
 
-static int gemv_quant_v(int M, int K) {
-  (void)M; (void)K;
-  return 4;      // 32 values (one group) per quantising lane
-}
-
-template <int QT, int MR, int V>
-static hipError_t launch_gemv_t(const uint8_t* W, const f16* A, const f16* R, f16* Y, int N, int K,
+template <int QT, int MR, class AT>
+static hipError_t launch_gemv_t(const uint8_t* W, const AT* A, const AT* R, AT* Y, int N, int K,
                                 hipStream_t st) {
   const size_t lds = gemv_layout<QT>(MR, K).total;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  auto kern = gemv_kernel<QT, MR, V>;
+  auto kern = gemv_kernel<QT, MR, AT>;
   // raise the dynamic-LDS limit once per instantiation (to the CU's 160 KB)
   static bool attr_set = false;
   if (lds > 65536 && !attr_set) {
@@ -547,27 +540,17 @@ static hipError_t launch_gemv_t(const uint8_t* W, const f16* A, const f16* R, f1
   return hipGetLastError();
 }
 
-template <int QT, int MR>
-static hipError_t launch_gemv_m(const uint8_t* W, const f16* A, const f16* R, f16* Y, int N, int K,
-                                hipStream_t st) {
-  switch (gemv_quant_v(MR, K)) {
-    case 1: return launch_gemv_t<QT, MR, 1>(W, A, R, Y, N, K, st);
-    case 2: return launch_gemv_t<QT, MR, 2>(W, A, R, Y, N, K, st);
-    default: return launch_gemv_t<QT, MR, 4>(W, A, R, Y, N, K, st);
-  }
-}
-
-template <int QT>
-static hipError_t launch_gemv_q(const uint8_t* W, const f16* A, const f16* R, f16* Y, int M, int N,
+template <int QT, class AT>
+static hipError_t launch_gemv_q(const uint8_t* W, const AT* A, const AT* R, AT* Y, int M, int N,
                                 int K, hipStream_t st) {
   switch (M) {
-    case 1: return launch_gemv_m<QT, 1>(W, A, R, Y, N, K, st);
-    case 2: return launch_gemv_m<QT, 2>(W, A, R, Y, N, K, st);
-    case 3: return launch_gemv_m<QT, 3>(W, A, R, Y, N, K, st);
-    case 4: return launch_gemv_m<QT, 4>(W, A, R, Y, N, K, st);
-    case 5: return launch_gemv_m<QT, 5>(W, A, R, Y, N, K, st);
-    case 6: return launch_gemv_m<QT, 6>(W, A, R, Y, N, K, st);
-    default: return launch_gemv_m<QT, 7>(W, A, R, Y, N, K, st);
+    case 1: return launch_gemv_t<QT, 1, AT>(W, A, R, Y, N, K, st);
+    case 2: return launch_gemv_t<QT, 2, AT>(W, A, R, Y, N, K, st);
+    case 3: return launch_gemv_t<QT, 3, AT>(W, A, R, Y, N, K, st);
+    case 4: return launch_gemv_t<QT, 4, AT>(W, A, R, Y, N, K, st);
+    case 5: return launch_gemv_t<QT, 5, AT>(W, A, R, Y, N, K, st);
+    case 6: return launch_gemv_t<QT, 6, AT>(W, A, R, Y, N, K, st);
+    default: return launch_gemv_t<QT, 7, AT>(W, A, R, Y, N, K, st);
   }
 }
 
@@ -579,48 +562,60 @@ size_t gemv_lds_bytes(int qtype, int M, int K) {
   }
 }
 
+template <class AT>
+static hipError_t launch_gemv_at(int qtype, const uint8_t* W, const AT* A, const AT* R, AT* Y, int M,
+                                 int N, int K, hipStream_t st) {
+  if (qtype == QT_Q4K) return launch_gemv_q<QT_Q4K, AT>(W, A, R, Y, M, N, K, st);
+  if (qtype == QT_Q5K) return launch_gemv_q<QT_Q5K, AT>(W, A, R, Y, M, N, K, st);
+  return launch_gemv_q<QT_Q6K, AT>(W, A, R, Y, M, N, K, st);
+}
+
 hipError_t launch_gemv(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, int M,
                        int N, int K, hipStream_t st) {
-  if (qtype == QT_Q4K) return launch_gemv_q<QT_Q4K>(W, A, R, Y, M, N, K, st);
-  if (qtype == QT_Q5K) return launch_gemv_q<QT_Q5K>(W, A, R, Y, M, N, K, st);
-  return launch_gemv_q<QT_Q6K>(W, A, R, Y, M, N, K, st);
+  return launch_gemv_at<f16>(qtype, W, A, R, Y, M, N, K, st);
+}
+
+hipError_t launch_gemv_f32(int qtype, const uint8_t* W, const float* A, const float* R, float* Y,
+                           int M, int N, int K, hipStream_t st) {
+  return launch_gemv_at<float>(qtype, W, A, R, Y, M, N, K, st);
 }
 
 // --------------------------------------------------------------- debug ----
 
-// The decode path's quantisation routine (the same quant_lane<V> that the
-// GEMV uses for this M, K), written out unswizzled to global memory.
-template <int V>
-__global__ void debug_quantize_kernel(const f16* __restrict__ A, int M, int K, int8_t* qa, float* s,
+// The decode path's quantisation routine (the same quant_group<AT> that
+// the GEMV runs), one thread per 32-value group, written out unswizzled to
+// global memory.
+template <class AT>
+__global__ void debug_quantize_kernel(const AT* __restrict__ A, int M, int K, int8_t* qa, float* s,
                                       int* T) {
-  constexpr int LPG = 4 / V;
-  const int tasks = M * K / (8 * V);
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;   // whole groups per block
-  uint4 raw[V];
+  constexpr int U4 = act_u4<AT>();
+  const int tasks = M * K / 32;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  uint4 raw[U4];
 #pragma unroll
-  for (int i = 0; i < V; ++i)
-    raw[i] = t < tasks ? *(const uint4*)(A + (size_t)t * 8 * V + 8 * i) : make_uint4(0, 0, 0, 0);
-  uint32_t q[2 * V];
+  for (int i = 0; i < U4; ++i)
+    raw[i] = t < tasks ? ((const uint4*)(A + (size_t)t * 32))[i] : make_uint4(0, 0, 0, 0);
+  uint32_t q[8];
   float sc;
   int tsum, thalf[2];
-  quant_lane<V>(raw, q, sc, tsum, thalf);
+  quant_group<AT>(raw, q, sc, tsum, thalf);
   if (t >= tasks) return;
 #pragma unroll
-  for (int i = 0; i < 2 * V; ++i) ((uint32_t*)qa)[(size_t)t * 2 * V + i] = q[i];
-  if ((t % LPG) == 0) {
-    s[t / LPG] = sc;
-    T[t / LPG] = tsum;
-  }
+  for (int i = 0; i < 8; ++i) ((uint32_t*)qa)[(size_t)t * 8 + i] = q[i];
+  s[t] = sc;
+  T[t] = tsum;
 }
 
-hipError_t launch_debug_quantize(const f16* A, int M, int K, int8_t* qa, float* s, int* T,
+hipError_t launch_debug_quantize(const void* A, bool f32, int M, int K, int8_t* qa, float* s, int* T,
                                  hipStream_t st) {
-  const int V = gemv_quant_v(M, K);
-  const long long tasks = (long long)M * K / (8 * V);
+  const long long tasks = (long long)M * K / 32;
   const unsigned grid = (unsigned)((tasks + 255) / 256);
-  if (V == 1) hipLaunchKernelGGL(debug_quantize_kernel<1>, dim3(grid), dim3(256), 0, st, A, M, K, qa, s, T);
-  else if (V == 2) hipLaunchKernelGGL(debug_quantize_kernel<2>, dim3(grid), dim3(256), 0, st, A, M, K, qa, s, T);
-  else hipLaunchKernelGGL(debug_quantize_kernel<4>, dim3(grid), dim3(256), 0, st, A, M, K, qa, s, T);
+  if (f32)
+    hipLaunchKernelGGL(debug_quantize_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)A, M,
+                       K, qa, s, T);
+  else
+    hipLaunchKernelGGL(debug_quantize_kernel<f16>, dim3(grid), dim3(256), 0, st, (const f16*)A, M, K,
+                       qa, s, T);
   return hipGetLastError();
 }
 

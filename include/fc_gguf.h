@@ -88,6 +88,20 @@ int fc_gguf_create(int64_t N, int64_t K, int qtype, const void* blocks,
  */
 int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, void* stream);
 
+/*
+ * Y = A . W^T (+ R) with f32 activations, residual and output.
+ *   A  device f32[M,K] (16-byte aligned); R device f32[M,N] or NULL;
+ *   Y device f32[M,N].  Y may be the same pointer as R; Y must not overlap A.
+ * OpenVINO PR #39119, section Implementation: f32 activations take the int8
+ * quantisation + GEMV path at every row count, so this call ignores
+ * fc_gguf_set_path and runs the decode path (rows in chunks of at most 7,
+ * one launch each).  The per-32 quantisation reads the f32 values directly
+ * (no f16 rounding); the result is stored in f32 without rounding to f16.
+ * Single-matrix handles only.  M == 0 is a no-op.
+ */
+int fc_gguf_run_f32(fc_gguf_t h, const float* A, int64_t M, const float* R, float* Y,
+                    void* stream);
+
 /* Force a path (FC_GGUF_PATH_*); the testing switch of the FC primitive. */
 int fc_gguf_set_path(fc_gguf_t h, int path);
 
@@ -129,6 +143,8 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
  * fc_gguf_debug_quantize: the per-32 int8 activation quantisation of the
  *   decode path.  A device f16[M,K] (K % 32 == 0); qa device i8[M,K];
  *   s device f32[M,K/32]; T device i32[M,K/32] (sum of qa per group).
+ * fc_gguf_debug_quantize_f32: the same for f32 activations, A device
+ *   f32[M,K] (the quantisation fc_gguf_run_f32 runs).
  *
  * fc_gguf_debug_int_dots: the integer sub-block dot sums of the decode path,
  *   from given int8 activations qa device i8[M,K].  S device i32:
@@ -150,6 +166,8 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
  */
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s,
                            int32_t* T, void* stream);
+int fc_gguf_debug_quantize_f32(const float* A, int64_t M, int64_t K, int8_t* qa, float* s,
+                               int32_t* T, void* stream);
 int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S, void* stream);
 int fc_gguf_debug_weights(fc_gguf_t h, void* dst, void* stream);
 

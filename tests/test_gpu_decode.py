@@ -1,4 +1,5 @@
-"""GPU parity of the decode path (M < 8) against the CPU oracle.
+"""GPU parity of the decode path (M < 8, and f32 activations at any M) against
+the CPU oracle; input ranks and row counts that change between calls.
 
 Bit-exact: the int8 activation quantisation (codes, scales, group sums), the
 integer sub-block dot sums, and the device weight layout (Q6_K plane regroup
@@ -13,7 +14,7 @@ import pytest
 from gguf_quant_block_amd import synth
 from oracle import fc as ofc
 from oracle import kquant as okq
-from helpers import DECODE_TOL, case, maxrel
+from helpers import DECODE_TOL, PREFILL_TOL, case, maxrel, relfro
 
 pytestmark = pytest.mark.gpu
 
@@ -202,3 +203,104 @@ def test_gemv_full_size_sampled(gpu_lib, qtype, name, M):
     cols = np.unique(np.concatenate([cols, [0, N - 1]]))
     ref = ofc.fc_ref_int8(A, w[cols], qtype, None if R is None else R[:, cols])
     assert maxrel(y[:, cols], ref) <= DECODE_TOL
+
+
+# ------------------------------------------------------ f32 activations ----
+# OpenVINO PR #39119, section Implementation: f32 activations take the int8
+# quantisation + GEMV path at every row count.
+
+def _special_rows_f32(K):
+    g = np.random.default_rng(6)
+    A = g.standard_normal((6, K)).astype(np.float32)
+    A[0, :32] = 0                                                     # zero group
+    A[1, :32] = np.array([(k - 16) / 16 for k in range(32)])           # exact ties
+    A[2, :32] *= np.float32(1e-37)                                    # 127/amax overflows: zero group
+    A[2, 32:64] = np.float32(5e-37) * np.array([(k - 16) / 16 for k in range(32)])  # subnormal s
+    A[3, 64:96] *= np.float32(1e30)                                   # beyond the f16 range
+    A[4, 7] = np.float32(1e-40)                                       # subnormal value
+    A[5, 96:128] = np.float32(-3.0)                                   # constant group
+    return A
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 3072), (7, 8192), (6, 512)])
+def test_quantize_f32_bit_exact(gpu_lib, M, K):
+    from gguf_quant_block_amd.binding import debug_quantize
+    A = synth.normal_f32((M, K), synth.rng(57, K, 1))
+    if M == 6:
+        A = _special_rows_f32(K)
+    qa, s, T = (_host(x) for x in debug_quantize(_dev(A)))
+    qa0, s0, T0 = ofc.quantize_act(A)
+    assert np.array_equal(qa, qa0)
+    assert np.array_equal(s.view(np.uint32), s0.view(np.uint32))
+    assert np.array_equal(T, T0)
+
+
+def _case_f32(qtype, M, N, K, idx, with_r):
+    w = synth.blocks(qtype, N, K, synth.rng(58, idx, synth.TAG_BLOCKS))
+    A = synth.normal_f32((M, K), synth.rng(58, idx, synth.TAG_A))
+    R = synth.normal_f32((M, N), synth.rng(58, idx, synth.TAG_R)) if with_r else None
+    return w, A, R
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M", [1, 4, 7, 8, 20])
+@pytest.mark.parametrize("N,K", [(37, 768), (512, 2048), (24, 8192)])
+def test_gemv_f32_parity(gpu_lib, qtype, M, N, K):
+    import torch
+    with_r = (M + N) % 2 == 1
+    w, A, R = _case_f32(qtype, M, N, K, 100 * M + N, with_r)
+    y = _fc(w, qtype, N, K)(_dev(A), None if R is None else _dev(R))
+    assert y.dtype == torch.float32
+    assert maxrel(_host(y), ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
+
+
+def test_f32_ignores_forced_prefill_path(gpu_lib):
+    M, N, K = 12, 64, 512
+    w, A, R = _case_f32("q5_k", M, N, K, 1, True)
+    fcg = _fc(w, "q5_k", N, K)
+    y0 = _host(fcg(_dev(A), _dev(R)))
+    fcg.set_path("prefill")
+    y1 = _host(fcg(_dev(A), _dev(R)))
+    assert np.array_equal(y0, y1)
+    assert maxrel(y1, ofc.fc_ref_int8(A, w, "q5_k", R)) <= DECODE_TOL
+
+
+def test_f32_in_place_residual(gpu_lib):
+    M, N, K = 3, 96, 1024
+    w, A, R = _case_f32("q6_k", M, N, K, 2, True)
+    Rd = _dev(R)
+    _fc(w, "q6_k", N, K)(_dev(A), Rd, out=Rd)
+    assert maxrel(_host(Rd), ofc.fc_ref_int8(A, w, "q6_k", R)) <= DECODE_TOL
+
+
+# ---------------------------------------- input ranks and changing row count --
+
+@pytest.mark.parametrize("lead", [(2, 3), (4, 5), (1, 1, 2), (2, 2, 16)])
+def test_nd_inputs(gpu_lib, lead):
+    qtype, N, K = "q4_k", 80, 512
+    M = int(np.prod(lead))
+    w, A, R = case(qtype, M, N, K, 59, M)
+    A_nd, R_nd = A.reshape(*lead, K), R.reshape(*lead, N)
+    y = _host(_fc(w, qtype, N, K)(_dev(A_nd), _dev(R_nd)))
+    assert y.shape == (*lead, N)
+    ref = ofc.fc_ref_int8(A, w, qtype, R) if M < 8 else ofc.fc_gguf_ref(A, w, qtype, R)
+    err = maxrel(y.reshape(M, N), ref) if M < 8 else relfro(y.reshape(M, N), ref)
+    assert err <= (DECODE_TOL if M < 8 else PREFILL_TOL)
+
+
+def test_row_count_changes_between_calls(gpu_lib):
+    # one handle, M changing from call to call across both paths and the
+    # split-K workspace growth
+    qtype, N, K = "q6_k", 256, 4096
+    fcg = None
+    for i, M in enumerate([1, 9, 3, 64, 2, 200, 7, 8, 1]):
+        w, A, R = case(qtype, M, N, K, 59, 1000, with_r=True)
+        A = synth.normal_f16((M, K), synth.rng(59, 2000 + i, 1))
+        R = synth.normal_f16((M, N), synth.rng(59, 2000 + i, 2))
+        if fcg is None:
+            fcg = _fc(w, qtype, N, K)
+        y = _host(fcg(_dev(A), _dev(R)))
+        if M < 8:
+            assert maxrel(y, ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL, M
+        else:
+            assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL, M
