@@ -17,6 +17,9 @@ One step = one pass of the hot path over one batch of synthetic input:
     routing): expert bucketing + one grouped launch for gate/up [768, 2048]
     and for down [2048, 768], over 7 weight copies with 7 routings so that
     the touched expert weights stream from HBM.
+  * the widened paths, reported beside the headline: Q4_K decode (the same
+    layer set, 8 layers of weights) and Q4_K prefill at M = 512, and the f32
+    activation path (Q5_K decode GEMV on f32 A, R and Y, 8 layers).
 Each phase is captured once as a HIP graph and replayed; HIP events on the
 replay stream time the phases.  `value` is the decode phase's weight bytes /
 decode time.  Weights and activations are resident in HBM before timing.
@@ -292,15 +295,51 @@ def main():
         for fc, A, ids, per_slot, Y in moe:
             fc.grouped(A, ids, per_slot, out=Y)
 
+    # ---- widened paths: Q4_K decode and prefill; f32 activations ----
+    WIDE_LAYERS = 8
+    q4_dec, q4_dec_bytes = [], 0
+    q4_base = {}
+    for i, (name, (N, K)) in enumerate(shapes):
+        q4_base[name] = torch.from_numpy(synth.q4k_blocks(N, K, synth.rng(6, i, synth.TAG_BLOCKS))).to(dev)
+    for layer in range(WIDE_LAYERS):
+        for name, (N, K) in shapes:
+            A, R, Y = acts[name]
+            q4_dec.append((FcGguf(N, K, "q4_k", q4_base[name]), A, R, Y))
+            q4_dec_bytes += N * (K // 256) * 144
+    q4_pre, q4_pre_flops = [], 0
+    for si, (N, K) in enumerate(synth.PREFILL_SHAPES):
+        w = torch.from_numpy(synth.q4k_blocks(N, K, synth.rng(6, 10 + si, synth.TAG_BLOCKS))).to(dev)
+        A = torch.from_numpy(synth.normal_f16((Mp, K), synth.rng(6, 10 + si, synth.TAG_A))).to(dev)
+        R = torch.from_numpy(synth.normal_f16((Mp, N), synth.rng(6, 10 + si, synth.TAG_R))).to(dev)
+        q4_pre.append((FcGguf(N, K, "q4_k", w), A, R, torch.empty((Mp, N), dtype=torch.float16, device=dev)))
+        q4_pre_flops += 2 * Mp * N * K
+    f32_dec, f32_bytes = [], 0
+    acts32 = {}
+    for i, (name, (N, K)) in enumerate(shapes):
+        acts32[name] = (torch.from_numpy(synth.normal_f32((1, K), synth.rng(7, i, synth.TAG_A))).to(dev),
+                        torch.from_numpy(synth.normal_f32((1, N), synth.rng(7, i, synth.TAG_R))).to(dev),
+                        torch.empty((1, N), dtype=torch.float32, device=dev))
+    for fcs in layer_sets[:WIDE_LAYERS]:
+        for name, (N, K) in shapes:
+            f32_dec.append((fcs[name], *acts32[name]))
+            f32_bytes += N * (K // 256) * 176
+
+    def run_list(lst):
+        def f():
+            for fc, A, R, Y in lst:
+                fc(A, R, out=Y)
+        return f
+
     # eager warm-up (sets kernel attributes, allocates split-K workspaces)
-    decode_pass()
-    prefill_pass()
-    moe_pass()
+    phases = (("decode", decode_pass), ("prefill", prefill_pass), ("moe", moe_pass),
+              ("q4k_decode", run_list(q4_dec)), ("q4k_prefill", run_list(q4_pre)),
+              ("f32_decode", run_list(f32_dec)))
+    for _, fn in phases:
+        fn()
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
     graphs = {}
-    phases = (("decode", decode_pass), ("prefill", prefill_pass), ("moe", moe_pass))
     for key, fn in phases:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
@@ -328,10 +367,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
+    def phase_s(k):
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev[k]) / 1e3 / args.steps
+
     dec_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev["decode"])
     pre_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev["prefill"])
     moe_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev["moe"])
-    step_ms = (dec_ms + pre_ms + moe_ms) / args.steps
+    step_ms = sum(phase_s(k) for k, _ in phases) * 1e3
+    q4d_s, q4p_s, f32_s = phase_s("q4k_decode"), phase_s("q4k_prefill"), phase_s("f32_decode")
     moe_s = moe_ms / 1e3 / args.steps
     dec_s = dec_ms / 1e3 / args.steps
     pre_s = pre_ms / 1e3 / args.steps
@@ -391,12 +434,26 @@ def main():
         },
         "roofline_prefill": {
             "bound": "mfma",
-            "kernel": "prefill_kernel (M=512)",
+            "kernel": "prefill_dma_kernel (M=512)",
             "achieved": round(prefill_tflops, 1),
             "peak": F16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(prefill_tflops / F16_MFMA_PEAK_TFLOPS, 4),
             "traffic": None,
+        },
+        "q4k": {
+            "workload": f"Q4_K decode GEMV over the same layer set ({WIDE_LAYERS} layers of weights, M=1, fused "
+                        "residual) and Q4_K prefill at M=512 on [8192,2048] and [2048,8192]",
+            "decode_weight_gbps": round(q4_dec_bytes / q4d_s / 1e9, 1),
+            "decode_us_per_launch": round(q4d_s * 1e6 / len(q4_dec), 3),
+            "decode_frac_of_hbm_peak": round(q4_dec_bytes / q4d_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "prefill_tflops_m512": round(q4_pre_flops / q4p_s / 1e12, 1),
+            "prefill_frac_of_f16_peak": round(q4_pre_flops / q4p_s / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+        },
+        "f32_decode": {
+            "workload": f"Q5_K decode GEMV on f32 activations, residual and output, M=1, {WIDE_LAYERS} layers",
+            "weight_gbps": round(f32_bytes / f32_s / 1e9, 1),
+            "us_per_launch": round(f32_s * 1e6 / len(f32_dec), 3),
         },
         "wall_s": round(wall, 3),
     }

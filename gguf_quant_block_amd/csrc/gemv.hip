@@ -1,28 +1,31 @@
-// Decode path (M < 8): per-32 int8 activation quantisation fused into an
-// int8 GEMV that streams the raw Q4_K / Q5_K / Q6_K blocks once.
+// Decode path (M < 8, and f32 activations): per-32 int8 activation
+// quantisation fused into an int8 GEMV that streams the raw Q4_K / Q5_K /
+// Q6_K blocks once.
 //
 // OpenVINO PR #39119, section Implementation: the GEMV quantises the
 // activations per 32 values and takes int8 dot products directly against the
 // blocks; the residual Add is fused into the output store.
 //
-// Work layout (one launch; workgroup = 4 waves):
-//   * A wave owns R = 64 / (K/256) whole rows of W (one row per wave when a
-//     row has more than 64 blocks).  Each lane owns ONE whole super-block; in
-//     the device layout (layout.h) the wave's blocks are piece-interleaved,
-//     so each of its 16-byte piece loads is one coalesced access.
+// Work layout (one launch):
+//   * A workgroup owns one row tile of the device layout (layout.h): 16
+//     weight rows over all of K.  It has nw = min(KBp/4, 8) waves; wave w
+//     takes the 16 x 4-block tiles w, w + nw, ... of the row tile, one block
+//     per lane (lane = (kb % 4) * 16 + row % 16), so every 16-byte piece load
+//     of the wave is one contiguous kilobyte.
 //   * Every thread first issues the activation loads of its quantisation
 //     groups, then its block's weight loads, then quantises (waiting only
 //     for the activation loads, which complete first) into LDS: int8 codes
-//     (16-byte chunks XOR-swizzled by the block index so lanes on different
-//     blocks hit different banks) and a per-(row, block) record of the f32
-//     group scales s and the code sums the scale algebra needs (Q4_K, Q5_K:
-//     s*T per 32-group for the min term; Q6_K: 16-value sums for the -32
-//     offset).
-//     The weights arrive meanwhile.
+//     and a per-(row, block) record of the f32 group scales s and the code
+//     sums the scale algebra needs (Q4_K, Q5_K: s*T per 32-group for the min
+//     term; Q6_K: 16-value sums for the -32 offset).  The weights arrive
+//     meanwhile.
 //   * After the barrier each lane decodes its block with compile-time field
 //     offsets, takes v_dot4_i32_i8 integer sums per sub-block and applies the
-//     scales in f32; the per-lane partials of a row are summed in lane order
-//     (deterministic), R is added, and the result is rounded once to f16.
+//     scales in f32.  The lanes of a wave read the activations of only four
+//     blocks at a time (one per kb % 4), so the LDS reads are broadcasts.
+//   * Row sums in a fixed order: over a lane's tiles, then across the four
+//     lanes of a row (butterfly), then across the waves in wave order; R is
+//     added and the result is rounded once to the output type.
 #include <type_traits>
 
 #include "common.h"
@@ -31,7 +34,8 @@
 
 namespace fcg {
 
-constexpr int GEMV_WAVES = 4;
+constexpr int GEMV_MAX_WAVES = 8;
+constexpr int GEMV_MAX_THREADS = 64 * GEMV_MAX_WAVES;
 constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23: x + magic rounds x to an integer, ties to even
 
 // ------------------------------------------------------ LDS layout ----
@@ -46,22 +50,40 @@ template <> struct GemvFmt<QT_Q6K> {
 };
 
 struct GemvLayout {
-  size_t rec, part, dyn, total;   // dyn == total: all LDS is dynamic
+  size_t rec, part, total;
 };
 
-// LDS: qa int8 [MR][K] | rec u32 [MR][KB][REC] | part f32 [WAVES][MR][64].
+#ifndef FCG_GEMV_RT
+#define FCG_GEMV_RT 1
+#endif
+// Row tiles per workgroup and waves per row tile for K: one wave per 4-block
+// tile of a row tile, at most 8 waves in all.
+__host__ __device__ inline int gemv_rt(int K) {
+  (void)K;
+  return FCG_GEMV_RT;
+}
+__host__ __device__ inline int gemv_waves(int K) {
+  const int g = tiled_kb(K / QK) / TILE_KB, rt = gemv_rt(K);
+  const int per = g < GEMV_MAX_WAVES / rt ? g : GEMV_MAX_WAVES / rt;
+  return per * rt;
+}
+
+// LDS: qa int8 [MR][KBp] records of QA_REC bytes (256 codes + 16 bytes of
+// padding, so that the four blocks a wave reads at once start on different
+// banks) | rec u32 [MR][KBp][REC] | part f32 [waves][MR][16] (a wave's sums
+// for the 16 rows of its row tile).
+constexpr int QA_REC = QK + 16;
 template <int QT>
-__host__ __device__ constexpr GemvLayout gemv_layout(int MR, int K) {
-  const size_t qa = (size_t)MR * K;
-  const size_t rec = qa;
-  const size_t part = rec + (size_t)MR * (K / QK) * GemvFmt<QT>::REC * 4;
-  const size_t total = part + (size_t)GEMV_WAVES * MR * 64 * 4;
-  return GemvLayout{rec, part, total, total};
+__host__ __device__ constexpr GemvLayout gemv_layout(int MR, int KBp, int waves) {
+  const size_t rec = (size_t)MR * KBp * QA_REC;
+  const size_t part = rec + (size_t)MR * KBp * GemvFmt<QT>::REC * 4;
+  const size_t total = part + (size_t)waves * MR * TILE_ROWS * 4;
+  return GemvLayout{rec, part, total};
 }
 
 // byte offset of the 16-byte code chunk t (0..15) of block kb in row m
-__device__ __forceinline__ int qa_chunk(int m, int K, int kb, int t) {
-  return m * K + kb * QK + 16 * (t ^ (kb & 15));
+__device__ __forceinline__ int qa_chunk(int m, int KBp, int kb, int t) {
+  return (m * KBp + kb) * QA_REC + 16 * t;
 }
 
 // ------------------------------------------------ activation quantisation --
@@ -146,20 +168,18 @@ __device__ __forceinline__ void quant_group(const uint4* raw, uint32_t* q, float
   tsum = a + b;
 }
 
-// Quantisation of MR rows of A into the LDS layout by the whole workgroup:
-// thread tid takes the 32-value groups (tasks) tid, tid + 256, ...  The
-// activation loads of the first qpre<AT>() rounds are issued before the
+// Quantisation of MR rows of A into the LDS layout by the whole workgroup of
+// nt threads: thread tid takes the 32-value groups (tasks) tid, tid + nt, ...
+// The activation loads of the first qpre<AT>() rounds are issued before the
 // weight loads, so the quantisation waits only for them (loads complete in
 // order) while the weights are still in flight.
-constexpr int GEMV_THREADS = 64 * GEMV_WAVES;
 template <class AT>
 constexpr int qpre() { return std::is_same<AT, f16>::value ? 2 : 1; }
 
 template <int QT, int MR, class AT>
-__device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4* raw, uint8_t* smem,
-                                              uint32_t* rec) {
+__device__ __forceinline__ void quantise_task(int t, int tasks, int K, int KBp, uint4* raw,
+                                              uint8_t* smem, uint32_t* rec) {
   constexpr int REC = GemvFmt<QT>::REC;
-  const int KB = K / QK;
 #pragma unroll
   for (int i = 0; i < act_u4<AT>(); ++i) raw[i] = t < tasks ? raw[i] : make_uint4(0, 0, 0, 0);
   uint32_t q[8];
@@ -170,9 +190,9 @@ __device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4* ra
     const int e = t * 32;                           // first value (flat over MR x K)
     const int m = e / K, pos = e - m * K;
     const int kb = pos / QK, t16 = (pos % QK) / 16, g = (pos % QK) / 32;
-    *(uint4*)(smem + qa_chunk(m, K, kb, t16)) = make_uint4(q[0], q[1], q[2], q[3]);
-    *(uint4*)(smem + qa_chunk(m, K, kb, t16 + 1)) = make_uint4(q[4], q[5], q[6], q[7]);
-    uint32_t* r = rec + ((size_t)m * KB + kb) * REC;
+    *(uint4*)(smem + qa_chunk(m, KBp, kb, t16)) = make_uint4(q[0], q[1], q[2], q[3]);
+    *(uint4*)(smem + qa_chunk(m, KBp, kb, t16 + 1)) = make_uint4(q[4], q[5], q[6], q[7]);
+    uint32_t* r = rec + ((size_t)m * KBp + kb) * REC;
     r[g] = __builtin_bit_cast(uint32_t, s);
     if constexpr (QT != QT_Q6K) {
       r[8 + g] = __builtin_bit_cast(uint32_t, s * (float)tsum);
@@ -184,12 +204,12 @@ __device__ __forceinline__ void quantise_task(int t, int tasks, int K, uint4* ra
 }
 
 template <int MR, class AT>
-__device__ __forceinline__ void quant_issue(const AT* A, int K, int tid,
+__device__ __forceinline__ void quant_issue(const AT* A, int K, int tid, int nt,
                                             uint4 (&raw)[qpre<AT>()][act_u4<AT>()]) {
   const int tasks = MR * K / 32;
 #pragma unroll
   for (int r = 0; r < qpre<AT>(); ++r) {
-    const int t = r * GEMV_THREADS + tid;
+    const int t = r * nt + tid;
     const int tc = t < tasks ? t : 0;
 #pragma unroll
     for (int i = 0; i < act_u4<AT>(); ++i) raw[r][i] = ((const uint4*)(A + (size_t)tc * 32))[i];
@@ -197,24 +217,24 @@ __device__ __forceinline__ void quant_issue(const AT* A, int K, int tid,
 }
 
 template <int QT, int MR, class AT>
-__device__ __forceinline__ void quant_finish(const AT* A, int K, uint8_t* smem, int tid,
+__device__ __forceinline__ void quant_finish(const AT* A, int K, int KBp, uint8_t* smem,
+                                             uint32_t* rec, int tid, int nt,
                                              uint4 (&raw)[qpre<AT>()][act_u4<AT>()]) {
   constexpr int QP = qpre<AT>(), U4 = act_u4<AT>();
   const int tasks = MR * K / 32;
   const int wbase = tid & ~63;                        // wave-uniform skip of idle waves
-  uint32_t* rec = (uint32_t*)(smem + gemv_layout<QT>(MR, K).rec);
 #pragma unroll
   for (int r = 0; r < QP; ++r)
-    if (r * GEMV_THREADS + wbase < tasks)
-      quantise_task<QT, MR, AT>(r * GEMV_THREADS + tid, tasks, K, raw[r], smem, rec);
-  for (int t0 = QP * GEMV_THREADS; t0 < tasks; t0 += GEMV_THREADS) {
+    if (r * nt + wbase < tasks)
+      quantise_task<QT, MR, AT>(r * nt + tid, tasks, K, KBp, raw[r], smem, rec);
+  for (int t0 = QP * nt; t0 < tasks; t0 += nt) {
     if (t0 + wbase >= tasks) break;
     const int t = t0 + tid;
     const int tc = t < tasks ? t : 0;
     uint4 v[U4];
 #pragma unroll
     for (int i = 0; i < U4; ++i) v[i] = ((const uint4*)(A + (size_t)tc * 32))[i];
-    quantise_task<QT, MR, AT>(t, tasks, K, v, smem, rec);
+    quantise_task<QT, MR, AT>(t, tasks, K, KBp, v, smem, rec);
   }
 }
 
@@ -268,8 +288,8 @@ __device__ __forceinline__ int dot16u(const uint32_t* c, uint4 a) {
 // Q4_K / Q5_K block -> part[m] (lane's contribution to row m): blk = the
 // block's 36 / 44 words.
 template <int QT, int MR>
-__device__ __forceinline__ void q45k_block(const uint32_t* blk, int kb, int K, const uint8_t* smem,
-                                           const uint32_t* rec, int KB, float* part) {
+__device__ __forceinline__ void q45k_block(const uint32_t* blk, int kb, int KBp, const uint8_t* smem,
+                                           const uint32_t* rec, float* part) {
   const float d = h2f(blk[0]), dmin = h2f(blk[0] >> 16);
   const uint32_t w0 = blk[1], w1 = blk[2], w2 = blk[3];
   // 6-bit scales / mins as bytes: j = 0..3 and j = 4..7
@@ -290,13 +310,13 @@ __device__ __forceinline__ void q45k_block(const uint32_t* blk, int kb, int K, c
     const float mn0 = (float)((mw >> (16 * (C & 1))) & 0xFF), mn1 = (float)((mw >> (16 * (C & 1) + 8)) & 0xFF);
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      const uint4 a0 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C));
-      const uint4 a1 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C + 1));
-      const uint4 a2 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C + 2));
-      const uint4 a3 = *(const uint4*)(smem + qa_chunk(m, K, kb, 4 * C + 3));
+      const uint4 a0 = *(const uint4*)(smem + qa_chunk(m, KBp, kb, 4 * C));
+      const uint4 a1 = *(const uint4*)(smem + qa_chunk(m, KBp, kb, 4 * C + 1));
+      const uint4 a2 = *(const uint4*)(smem + qa_chunk(m, KBp, kb, 4 * C + 2));
+      const uint4 a3 = *(const uint4*)(smem + qa_chunk(m, KBp, kb, 4 * C + 3));
       const int S0 = dot16u(lo, a0) + dot16u(lo + 4, a1);
       const int S1 = dot16u(hi, a2) + dot16u(hi + 4, a3);
-      const uint32_t* r = rec + ((size_t)m * KB + kb) * GemvFmt<QT>::REC;
+      const uint32_t* r = rec + ((size_t)m * KBp + kb) * GemvFmt<QT>::REC;
       const float2 s2 = *(const float2*)(r + 2 * C);
       const float2 t2 = *(const float2*)(r + 8 + 2 * C);
       X[m] = fmaf(sc0, s2.x * (float)S0, X[m]);
@@ -316,8 +336,8 @@ __device__ __forceinline__ void q45k_block(const uint32_t* blk, int kb, int K, c
 // Q6_K block -> part[m]: ql (32 words), qh (16 words), sc (4 words), d bits.
 template <int MR>
 __device__ __forceinline__ void q6k_block(const uint32_t* ql, const uint32_t* qh, uint4 scv,
-                                          uint32_t dbits, int kb, int K, const uint8_t* smem,
-                                          const uint32_t* rec, int KB, float* part) {
+                                          uint32_t dbits, int kb, int KBp, const uint8_t* smem,
+                                          const uint32_t* rec, float* part) {
   const float d = h2f(dbits);
   const uint32_t scw[4] = {scv.x, scv.y, scv.z, scv.w};
   float X[MR];
@@ -334,11 +354,11 @@ __device__ __forceinline__ void q6k_block(const uint32_t* ql, const uint32_t* qh
     const int c5 = sext8(scw[(s0 + 5) >> 2] >> (8 * ((s0 + 5) & 3)));
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      const uint4 a0 = *(const uint4*)(smem + qa_chunk(m, K, kb, s0));
-      const uint4 a1 = *(const uint4*)(smem + qa_chunk(m, K, kb, s0 + 1));
-      const uint4 a4 = *(const uint4*)(smem + qa_chunk(m, K, kb, s0 + 4));
-      const uint4 a5 = *(const uint4*)(smem + qa_chunk(m, K, kb, s0 + 5));
-      const uint32_t* r = rec + ((size_t)m * KB + kb) * GemvFmt<QT_Q6K>::REC;
+      const uint4 a0 = *(const uint4*)(smem + qa_chunk(m, KBp, kb, s0));
+      const uint4 a1 = *(const uint4*)(smem + qa_chunk(m, KBp, kb, s0 + 1));
+      const uint4 a4 = *(const uint4*)(smem + qa_chunk(m, KBp, kb, s0 + 4));
+      const uint4 a5 = *(const uint4*)(smem + qa_chunk(m, KBp, kb, s0 + 5));
+      const uint32_t* r = rec + ((size_t)m * KBp + kb) * GemvFmt<QT_Q6K>::REC;
       const int2 tl = *(const int2*)(r + 8 + s0);
       const int2 th = *(const int2*)(r + 8 + s0 + 4);
       const int S0 = dot16u(lo, a0) - 32 * tl.x;
@@ -361,31 +381,12 @@ __device__ __forceinline__ void q6k_block(const uint32_t* ql, const uint32_t* qh
   for (int m = 0; m < MR; ++m) part[m] += d * X[m];
 }
 
-// Workgroup barrier after the quantisation: every wave's LDS writes complete
-// (lgkmcnt(0)) before it arrives, while its weight loads stay in flight.
-// (s_waitcnt immediate, gfx9 encoding: vmcnt 63, expcnt 7, lgkmcnt 0.)
-__device__ __forceinline__ void barrier_after_lds_writes() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void wait_all_and_sync_wave() {
-  __builtin_amdgcn_s_waitcnt(0);        // vmcnt = expcnt = lgkmcnt = 0
-  __builtin_amdgcn_wave_barrier();
-}
-
 // ---------------------------------------------------------------- kernel --
 
-// Workgroup = GEMV_WAVES worker waves + NQ quantiser waves.  The workers
-// issue their weight loads and go straight to the barrier; the quantiser
-// waves issue no weight loads, so their activation loads return from L2 and
-// the quantisation completes while the weights are still in flight.
 // The lane's whole super-block, straight from global memory into registers
-// (Q4_K / Q5_K: its 9 / 11 pieces; Q6_K: its QL, QH, SC and D bytes).  In the device
-// layout the lanes of a wave own consecutive blocks, so every piece load of
-// the wave is one or two contiguous runs.
+// (Q4_K / Q5_K: its 9 / 11 pieces; Q6_K: its QL, QH, SC and D bytes).  The
+// lanes of a wave own the 64 blocks of one tile, so every piece load of the
+// wave is one contiguous kilobyte.
 struct GemvBlock {
   uint32_t w[48];     // Q4_K / Q5_K: the 144 / 176 bytes in w[0..35] / w[0..43];
                       // Q6_K: ql in w[0..31], qh in w[32..47]
@@ -401,27 +402,28 @@ struct GemvBlock {
 #define FCG_KEEP_ORDER() asm volatile("" ::: "memory")
 
 template <int QT>
-__device__ __forceinline__ void load_block(const uint8_t* W, size_t nbp, size_t gb, GemvBlock& b) {
+__device__ __forceinline__ void load_block(const uint8_t* W, const WMap<true>& L, int n, int kb,
+                                           GemvBlock& b) {
   if constexpr (QT != QT_Q6K) {
     constexpr int P = block_bytes_of(QT) / 16;
 #pragma unroll
     for (int c = 0; c < P; ++c) {
-      const uint4 v = *(const uint4*)(W + piece_off(gb, P, c));
+      const uint4 v = *(const uint4*)(W + L.piece(n, kb, P, c));
       b.w[4 * c] = v.x; b.w[4 * c + 1] = v.y; b.w[4 * c + 2] = v.z; b.w[4 * c + 3] = v.w;
       FCG_KEEP_ORDER();
     }
   } else {
-    b.scv = *(const uint4*)(W + q6k_sc_base(nbp) + 16 * gb);
-    b.dbits = *(const uint16_t*)(W + q6k_d_base(nbp) + 2 * gb);
+    b.scv = *(const uint4*)(W + L.sc(n, kb));
+    b.dbits = *(const uint16_t*)(W + L.d(n, kb));
     FCG_KEEP_ORDER();
-    const uint8_t* qh = W + q6k_qh_base(nbp);
+    const uint8_t* qh = W + L.qh_base();
     auto ql_piece = [&](int f) {
-      const uint4 v = *(const uint4*)(W + piece_off(gb, 8, f));
+      const uint4 v = *(const uint4*)(W + L.piece(n, kb, 8, f));
       b.w[4 * f] = v.x; b.w[4 * f + 1] = v.y; b.w[4 * f + 2] = v.z; b.w[4 * f + 3] = v.w;
       FCG_KEEP_ORDER();
     };
     auto qh_piece = [&](int f) {
-      const uint4 v = *(const uint4*)(qh + piece_off(gb, 4, f));
+      const uint4 v = *(const uint4*)(qh + L.piece(n, kb, 4, f));
       b.w[32 + 4 * f] = v.x; b.w[33 + 4 * f] = v.y; b.w[34 + 4 * f] = v.z; b.w[35 + 4 * f] = v.w;
       FCG_KEEP_ORDER();
     };
@@ -433,79 +435,96 @@ __device__ __forceinline__ void load_block(const uint8_t* W, size_t nbp, size_t 
   }
 }
 
-// Workgroup = 4 waves.  Each thread issues its activation loads, then the
-// loads of its lane's super-block, quantises its activation groups into LDS
-// (waiting only for the activation loads) and meets the others at the
-// barrier; the weights arrive while this happens.
-// AT: the type of A, R and Y (f16, or f32 for f32 activations).
-template <int QT, int MR, class AT>
-__global__ void __launch_bounds__(GEMV_THREADS)
-gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R,
-            AT* __restrict__ Y, int N, int K, int rows_per_wave) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const GemvLayout L = gemv_layout<QT>(MR, K);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int KB = K / QK;
-  const size_t nbp = padded_blocks((size_t)N * KB);
+// Workgroup barrier after the quantisation: every wave's LDS writes complete
+// (lgkmcnt(0)) before it arrives, while its weight loads stay in flight.
+// (s_waitcnt immediate, gfx9 encoding: vmcnt 63, expcnt 7, lgkmcnt 0.)
+__device__ __forceinline__ void barrier_after_lds_writes() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-  const int n_w = (blockIdx.x * GEMV_WAVES + wave) * rows_per_wave;
-  int rows_w = N - n_w;
-  rows_w = rows_w < 0 ? 0 : (rows_w > rows_per_wave ? rows_per_wave : rows_w);
-  const int nb_w = rows_w * KB;                       // blocks of this wave
-  const size_t gb_w = (size_t)n_w * KB;               // its first block
-  float* part_lds = (float*)(smem + L.part) + (size_t)wave * MR * 64;
+// Workgroup = RT row tiles (16 weight rows each), nw = RT * per waves: wave
+// w works on row tile w % RT, on its tiles w / RT, w / RT + per, ...  Each
+// thread issues its activation loads, then the loads of its lane's first
+// block, quantises its activation groups into LDS (waiting only for the
+// activation loads) and meets the others at the barrier; the weights arrive
+// while this happens.  AT: the type of A, R and Y (f16, or f32 for f32
+// activations).
+template <int QT, int MR, class AT>
+__global__ void __launch_bounds__(GEMV_MAX_THREADS)
+gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R,
+            AT* __restrict__ Y, int N, int K, int RT) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const WMap<true> L(N, K);
+  const int KB = L.KB, KBp = L.KBp;
+  const int G = KBp / TILE_KB;                        // tiles of a row tile
+  const int nt = blockDim.x, nw = nt >> 6, per = nw / RT;
+  const GemvLayout Ly = gemv_layout<QT>(MR, KBp, nw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rt = wave % RT, g0 = wave / RT;
+  const int r = lane % TILE_ROWS, kbq = lane / TILE_ROWS;
+  const int n = (blockIdx.x * RT + rt) * TILE_ROWS + r;   // < tiled_rows(N) when the
+                                                         // row tile exists
+  uint32_t* rec = (uint32_t*)(smem + Ly.rec);
+  float* part_lds = (float*)(smem + Ly.part);
 
   uint4 araw[qpre<AT>()][act_u4<AT>()];
-  quant_issue<MR, AT>(A, K, tid, araw);
-  // the residual of the row this lane stores (lanes < rows_w), fetched now so
-  // that its latency hides under the weight stream
-  // (unconditional loads from a valid address, so that nothing waits on them
-  // before the weight loads are issued; without R they read A and are unused)
+  quant_issue<MR, AT>(A, K, tid, nt, araw);
+  // the residual of the row this lane stores, fetched now so that its latency
+  // hides under the weight stream (unconditional loads from a valid address,
+  // so that nothing waits on them before the weight loads are issued;
+  // without R they read A and are unused)
   AT rres[MR];
   {
-    int nr = n_w + lane;
-    nr = nr < N ? nr : N - 1;
+    const int nr = n < N ? n : N - 1;
 #pragma unroll
     for (int m = 0; m < MR; ++m) rres[m] = *(R ? R + (size_t)m * N + nr : A);
   }
   asm volatile("" ::: "memory");                    // activation and residual loads first
 
-  // the lane's first block (lanes without one re-read block 0; never used)
+  // the row tile exists unless it is past the last one (a partial workgroup)
+  const bool live = n < tiled_rows(N);
+  const int nl = live ? n : r;                        // row 0's tile stands in
+  // the lane's first block (waves without a tile re-read tile 0; never used)
   GemvBlock blk;
-  load_block<QT>(W, nbp, lane < nb_w ? gb_w + lane : 0, blk);
+  load_block<QT>(W, L, nl, (g0 < G ? g0 : 0) * TILE_KB + kbq, blk);
   asm volatile("" ::: "memory");                    // ... then the weight loads
 
-  quant_finish<QT, MR, AT>(A, K, smem, tid, araw);
+  quant_finish<QT, MR, AT>(A, K, KBp, smem, rec, tid, nt, araw);
   barrier_after_lds_writes();                         // quantised activations ready
 
-  const uint32_t* rec = (const uint32_t*)(smem + L.rec);
   float part[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) part[m] = 0.f;
-  const int rounds = (nb_w + 63) / 64;
-  for (int r = 0; r < rounds; ++r) {
-    const int j = 64 * r + lane;                      // local block index
-    if (r > 0) load_block<QT>(W, nbp, j < nb_w ? gb_w + j : 0, blk);
-    if (j < nb_w) {
-      const int kb = j % KB;
+  for (int g = g0; g < G; g += per) {
+    const int kb = g * TILE_KB + kbq;
+    if (g != g0) load_block<QT>(W, L, nl, kb, blk);
+    if (kb < KB) {
       if constexpr (QT == QT_Q6K)
-        q6k_block<MR>(blk.w, blk.w + 32, blk.scv, blk.dbits, kb, K, smem, rec, KB, part);
+        q6k_block<MR>(blk.w, blk.w + 32, blk.scv, blk.dbits, kb, KBp, smem, rec, part);
       else
-        q45k_block<QT, MR>(blk.w, kb, K, smem, rec, KB, part);
+        q45k_block<QT, MR>(blk.w, kb, KBp, smem, rec, part);
     }
   }
-  // row sums in lane order, + R, store
+  // row sums: the four lanes of a row (kbq = 0..3), then the waves of the
+  // row tile in order
 #pragma unroll
-  for (int m = 0; m < MR; ++m) part_lds[m * 64 + lane] = part[m];
-  wait_all_and_sync_wave();
-  if (lane < rows_w) {
-    const int per = KB < 64 ? KB : 64;                // lanes holding this row's partials
-    const int first = KB < 64 ? lane * KB : 0;
+  for (int m = 0; m < MR; ++m) {
+    part[m] += __shfl_xor(part[m], 16, 64);
+    part[m] += __shfl_xor(part[m], 32, 64);
+  }
+  if (lane < TILE_ROWS) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) part_lds[(wave * MR + m) * TILE_ROWS + lane] = part[m];
+  }
+  __syncthreads();
+  if (wave < RT && lane < TILE_ROWS && n < N) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       float y = 0.f;
-      for (int i = 0; i < per; ++i) y += part_lds[m * 64 + first + i];
-      const int n = n_w + lane;
+      for (int w = wave; w < nw; w += RT) y += part_lds[(w * MR + m) * TILE_ROWS + lane];
       if (R) y += (float)rres[m];
       Y[(size_t)m * N + n] = (AT)y;
     }
@@ -514,15 +533,11 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R
 
 // ------------------------------------------------------------------ launch --
 
-static int gemv_rows_per_wave(int K) {
-  const int KB = K / QK;
-  return KB <= 64 ? 64 / KB : 1;
-}
-
 template <int QT, int MR, class AT>
 static hipError_t launch_gemv_t(const uint8_t* W, const AT* A, const AT* R, AT* Y, int N, int K,
                                 hipStream_t st) {
-  const size_t lds = gemv_layout<QT>(MR, K).total;
+  const int nw = gemv_waves(K);
+  const size_t lds = gemv_layout<QT>(MR, tiled_kb(K / QK), nw).total;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = gemv_kernel<QT, MR, AT>;
   // raise the dynamic-LDS limit once per instantiation (to the CU's 160 KB)
@@ -533,10 +548,9 @@ static hipError_t launch_gemv_t(const uint8_t* W, const AT* A, const AT* R, AT* 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int rpw = gemv_rows_per_wave(K);
-  const int rows_wg = GEMV_WAVES * rpw;
-  const int grid = (N + rows_wg - 1) / rows_wg;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(GEMV_THREADS), lds, st, W, A, R, Y, N, K, rpw);
+  const int rt = gemv_rt(K);
+  const int grid = (tiled_rows(N) / TILE_ROWS + rt - 1) / rt;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), lds, st, W, A, R, Y, N, K, rt);
   return hipGetLastError();
 }
 
@@ -555,10 +569,11 @@ static hipError_t launch_gemv_q(const uint8_t* W, const AT* A, const AT* R, AT* 
 }
 
 size_t gemv_lds_bytes(int qtype, int M, int K) {
+  const int KBp = tiled_kb(K / QK), nw = gemv_waves(K);
   switch (qtype) {
-    case QT_Q4K: return gemv_layout<QT_Q4K>(M, K).total;
-    case QT_Q5K: return gemv_layout<QT_Q5K>(M, K).total;
-    default: return gemv_layout<QT_Q6K>(M, K).total;
+    case QT_Q4K: return gemv_layout<QT_Q4K>(M, KBp, nw).total;
+    case QT_Q5K: return gemv_layout<QT_Q5K>(M, KBp, nw).total;
+    default: return gemv_layout<QT_Q6K>(M, KBp, nw).total;
   }
 }
 
@@ -628,14 +643,14 @@ __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_
   const long long gb = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gb >= (long long)N * KB) return;
   const int n = (int)(gb / KB), kb = (int)(gb % KB);
-  const size_t nbp = padded_blocks((size_t)N * KB);
+  const WMap<true> L(N, K);
   const uint4 ones = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
   if constexpr (QT != QT_Q6K) {
     constexpr int P = block_bytes_of(QT) / 16;
     uint32_t blk[44];
 #pragma unroll
     for (int c = 0; c < P; ++c) {
-      const uint4 v = *(const uint4*)(W + piece_off((size_t)gb, P, c));
+      const uint4 v = *(const uint4*)(W + L.piece(n, kb, P, c));
       blk[4 * c] = v.x; blk[4 * c + 1] = v.y; blk[4 * c + 2] = v.z; blk[4 * c + 3] = v.w;
     }
     const int ns = K / 32;
@@ -658,12 +673,12 @@ __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_
     uint32_t ql[32], qh[16];
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      const uint4 v = *(const uint4*)(W + piece_off((size_t)gb, 8, f));
+      const uint4 v = *(const uint4*)(W + L.piece(n, kb, 8, f));
       ql[4 * f] = v.x; ql[4 * f + 1] = v.y; ql[4 * f + 2] = v.z; ql[4 * f + 3] = v.w;
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const uint4 v = *(const uint4*)(W + q6k_qh_base(nbp) + piece_off((size_t)gb, 4, f));
+      const uint4 v = *(const uint4*)(W + L.qh_base() + L.piece(n, kb, 4, f));
       qh[4 * f] = v.x; qh[4 * f + 1] = v.y; qh[4 * f + 2] = v.z; qh[4 * f + 3] = v.w;
     }
     const int ns = K / 16;

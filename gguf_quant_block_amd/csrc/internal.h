@@ -8,11 +8,11 @@
 namespace fcg {
 typedef _Float16 f16;
 
-// canonical AoS blocks -> a device layout of layout.h, piece-interleaved or
-// canonical (nblk blocks; the destination holds layout_bytes(qtype, nblk) bytes)
-size_t layout_bytes(int qtype, size_t nblk);
-hipError_t launch_weight_layout(int qtype, bool interleaved, const uint8_t* src, uint8_t* dst,
-                                size_t nblk, hipStream_t st);
+// canonical AoS blocks of an [N, K] matrix -> a device layout of layout.h,
+// tiled or canonical (the destination holds layout_bytes(...) bytes)
+size_t layout_bytes(int qtype, bool tiled, int N, int K);
+hipError_t launch_weight_layout(int qtype, bool tiled, const uint8_t* src, uint8_t* dst, int N, int K,
+                                hipStream_t st);
 
 // decode path (M in 1..7); A, R, Y all f16, or all f32
 size_t gemv_lds_bytes(int qtype, int M, int K);

@@ -1,19 +1,29 @@
 // Device layout of the weight blocks (shared by every kernel that reads them).
 //
-// The blocks of one [N, K] matrix are numbered b = n * (K/256) + kb (row-major,
-// the order of the GGUF tensor) and split into 16-byte pieces.  Groups of 64
-// consecutive blocks are stored piece-major: piece p of block b sits at
-//     ((b / 64) * P + p) * 1024 + (b % 64) * 16
-// inside its plane (P = pieces per block in that plane).  A wave whose lane l
-// owns block 64g + l therefore reads every piece with one fully coalesced
-// 1 KB access (wave64 x 16 B), instead of 64 accesses 176 or 210 bytes apart.
-// The block count is padded to a multiple of 64 with zero bytes.
-//   Q4_K: one plane, P = 9 (the 144 bytes of the block, in order).
-//   Q5_K: one plane, P = 11 (the 176 bytes of the block, in order).
+// Block (n, kb) is the kb-th super-block of weight row n (the GGUF tensor
+// holds row n's K/256 blocks in order).  Every block is cut into 16-byte
+// pieces.
+//
+// Tiled layout (single-matrix handles, read by the decode and prefill paths):
+// the block grid is cut into tiles of 16 rows x 4 blocks (64 blocks; the row
+// count is padded to a multiple of 16 and the blocks per row to a multiple
+// of 4 with zero bytes).  Tiles are numbered row-tile major,
+//     t = (n / 16) * (KBp / 4) + kb / 4,
+// and each tile is stored piece-major, the 64 blocks of a piece in the order
+// l = (kb % 4) * 16 + n % 16, so that piece p of block (n, kb) sits at
+//     (t * P + p) * 1024 + l * 16
+// inside its plane (P = pieces per block in that plane).  One 16-byte load
+// per lane then reads a contiguous kilobyte for a GEMV wave whose lane l
+// owns block l of a tile, and contiguous 256-byte runs (16 consecutive rows
+// at one kb) for a matrix-core tile whose lanes own consecutive rows.
+//   Q4_K / Q5_K: one plane, P = 9 / 11 (the 144 / 176 bytes of the block).
 //   Q6_K: the QL | QH | SC | D planes of OpenVINO PR #39119 (section
 //         Transformation), each over the padded block count: QL P = 8,
-//         QH P = 4; SC (16 B per block) and D (2 B per block) are already
-//         lane-contiguous, so their pieces are simply in block order.
+//         QH P = 4, SC P = 1; D holds 2 bytes per block at t * 128 + l * 2.
+//
+// Canonical layout (grouped handles, whose expert tiles read whole rows):
+// blocks b = n * (K/256) + kb in order, padded to a multiple of 64 blocks;
+// Q4_K / Q5_K blocks as in the file, Q6_K as the four planes in block order.
 #pragma once
 
 #include <stddef.h>
@@ -22,19 +32,53 @@
 namespace fcg {
 
 constexpr int LAYOUT_GROUP = 64;
+constexpr int TILE_ROWS = 16;      // rows per tile
+constexpr int TILE_KB = 4;         // blocks per row per tile
 
 __host__ __device__ inline size_t padded_blocks(size_t nblk) {
   return (nblk + LAYOUT_GROUP - 1) / LAYOUT_GROUP * LAYOUT_GROUP;
 }
+__host__ __device__ inline int tiled_rows(int N) { return (N + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS; }
+__host__ __device__ inline int tiled_kb(int KB) { return (KB + TILE_KB - 1) / TILE_KB * TILE_KB; }
 
-// byte offset of 16-byte piece p of block b in a plane of P pieces per block
-__host__ __device__ inline size_t piece_off(size_t b, int P, int p) {
-  return (((b >> 6) * (size_t)P + (size_t)p) << 10) + ((b & 63) << 4);
-}
+// Addressing of one [N, K] matrix in the tiled (TILED) or canonical layout.
+template <bool TILED>
+struct WMap {
+  int KB;        // blocks per row
+  int KBp;       // blocks per row as stored (padded to TILE_KB when tiled)
+  size_t nbt;    // blocks per plane, padding included
 
-// Q6_K plane bases for nbp (padded) blocks
-__host__ __device__ inline size_t q6k_qh_base(size_t nbp) { return 128 * nbp; }
-__host__ __device__ inline size_t q6k_sc_base(size_t nbp) { return 192 * nbp; }
-__host__ __device__ inline size_t q6k_d_base(size_t nbp) { return 208 * nbp; }
+  __host__ __device__ WMap(int N, int K) {
+    KB = K >> 8;
+    if constexpr (TILED) {
+      KBp = tiled_kb(KB);
+      nbt = (size_t)tiled_rows(N) * KBp;
+    } else {
+      KBp = KB;
+      nbt = padded_blocks((size_t)N * KB);
+    }
+  }
+  // tile index and position inside the tile of block (n, kb) (tiled layout)
+  __host__ __device__ size_t tile(int n, int kb) const {
+    return (size_t)(n / TILE_ROWS) * (KBp / TILE_KB) + kb / TILE_KB;
+  }
+  __host__ __device__ static int slot(int n, int kb) {
+    return (kb % TILE_KB) * TILE_ROWS + n % TILE_ROWS;
+  }
+  // byte offset of 16-byte piece p of block (n, kb) in a plane of P pieces per block
+  __host__ __device__ size_t piece(int n, int kb, int P, int p) const {
+    if constexpr (TILED) return ((tile(n, kb) * P + p) << 10) + ((size_t)slot(n, kb) << 4);
+    else return ((size_t)n * KB + kb) * (size_t)(16 * P) + (size_t)(16 * p);
+  }
+  // Q6_K planes
+  __host__ __device__ size_t qh_base() const { return 128 * nbt; }
+  __host__ __device__ size_t sc_base() const { return 192 * nbt; }
+  __host__ __device__ size_t d_base() const { return 208 * nbt; }
+  __host__ __device__ size_t sc(int n, int kb) const { return sc_base() + piece(n, kb, 1, 0); }
+  __host__ __device__ size_t d(int n, int kb) const {
+    if constexpr (TILED) return d_base() + tile(n, kb) * 128 + (size_t)slot(n, kb) * 2;
+    else return d_base() + ((size_t)n * KB + kb) * 2;
+  }
+};
 
 }  // namespace fcg

@@ -1,100 +1,106 @@
 // Weight layout transform, run once when a handle is created: canonical GGUF
-// blocks (array of structures, row-major) -> the device layout of layout.h
-// (piece-interleaved, for single-matrix handles) or the canonical device
-// layout (Q4_K / Q5_K blocks in order, Q6_K row-major planes; for grouped handles,
-// whose expert tiles read rows rather than runs of consecutive blocks).
+// blocks (array of structures, row-major) -> the tiled device layout of
+// layout.h (single-matrix handles) or the canonical device layout (Q4_K /
+// Q5_K blocks in order, Q6_K row-major planes; grouped handles, whose expert
+// tiles read rows).
 //
 // OpenVINO PR #39119, section Transformation: Q6_K blocks are regrouped into
 // the planes QL | QH | SC | D with unchanged size and contents; here every
-// plane (and the single Q4_K / Q5_K plane) is additionally piece-interleaved over
-// groups of 64 blocks so that a wave reads 64 whole blocks with coalesced
-// accesses.  One thread per destination byte (a one-time byte permutation).
+// plane (and the single Q4_K / Q5_K plane) is additionally cut into tiles of
+// 16 rows x 4 blocks stored piece-major, so that both the GEMV waves and the
+// matrix-core tiles read their blocks with coalesced accesses.  One thread
+// per destination byte (a one-time byte permutation).
 #include "common.h"
 #include "internal.h"
 #include "layout.h"
 
 namespace fcg {
 
-// source (block b, byte f of the block) of destination byte o of a
-// single-plane format (Q4_K, Q5_K) of BB = 16*P bytes per block
-template <int BB, bool IL>
-__device__ __forceinline__ void aos_src(size_t o, size_t& b, int& f) {
-  constexpr int P = BB / 16;
-  if constexpr (IL) {
-    const size_t g = o / (P * 1024);
-    const int r = (int)(o % (P * 1024));
-    b = g * 64 + ((r >> 4) & 63);
-    f = 16 * (r >> 10) + (r & 15);
-  } else {
-    b = o / BB;
-    f = (int)(o % BB);
-  }
-}
-
-// piece-interleaved plane of P pieces: (block, byte within the plane's part)
-__device__ __forceinline__ void il_src(size_t q, int P, size_t& b, int& f) {
-  const size_t g = q / ((size_t)P * 1024);
-  const int r = (int)(q % ((size_t)P * 1024));
-  b = g * 64 + ((r >> 4) & 63);
-  f = 16 * (r >> 10) + (r & 15);
-}
-
-template <bool IL>
-__device__ __forceinline__ void q6k_src(size_t o, size_t nbp, size_t& b, int& f) {
-  if (o < q6k_qh_base(nbp)) {                       // QL, 8 pieces
-    if constexpr (IL) il_src(o, 8, b, f);
-    else { b = o / 128; f = (int)(o % 128); }
-  } else if (o < q6k_sc_base(nbp)) {                // QH, 4 pieces
-    const size_t q = o - q6k_qh_base(nbp);
-    if constexpr (IL) il_src(q, 4, b, f);
-    else { b = q / 64; f = (int)(q % 64); }
+// source (row n, block kb, byte f of the block) of destination byte o;
+// false for padding
+template <int QT, bool TILED>
+__device__ __forceinline__ bool layout_src(size_t o, const WMap<TILED>& L, int& n, int& kb, int& f) {
+  constexpr int BB = block_bytes_of(QT);
+  // position inside a plane of P pieces per block -> (block, byte of the plane's part)
+  auto from_plane = [&](size_t q, int P) {
+    if constexpr (TILED) {
+      const size_t t = q / ((size_t)P * 1024);
+      const int r = (int)(q % ((size_t)P * 1024));
+      const int l = (r >> 4) & 63;
+      const int tiles_k = L.KBp / TILE_KB;
+      n = (int)(t / tiles_k) * TILE_ROWS + (l % TILE_ROWS);
+      kb = (int)(t % tiles_k) * TILE_KB + l / TILE_ROWS;
+      f = 16 * (r >> 10) + (r & 15);
+    } else {
+      const size_t b = q / (16 * P);
+      n = (int)(b / L.KB);
+      kb = (int)(b % L.KB);
+      f = (int)(q % (16 * P));
+    }
+  };
+  if constexpr (QT != QT_Q6K) {
+    from_plane(o, BB / 16);
+  } else if (o < L.qh_base()) {                       // QL, 8 pieces
+    from_plane(o, 8);
+  } else if (o < L.sc_base()) {                       // QH, 4 pieces
+    from_plane(o - L.qh_base(), 4);
     f += 128;
-  } else if (o < q6k_d_base(nbp)) {                 // SC, block order
-    const size_t q = o - q6k_sc_base(nbp);
-    b = q / 16;
-    f = 192 + (int)(q % 16);
-  } else {                                          // D, block order
-    const size_t q = o - q6k_d_base(nbp);
-    b = q / 2;
+  } else if (o < L.d_base()) {                        // SC, 1 piece
+    from_plane(o - L.sc_base(), 1);
+    f += 192;
+  } else {                                            // D, 2 bytes per block
+    const size_t q = o - L.d_base();
+    if constexpr (TILED) {
+      const size_t t = q / 128;
+      const int l = (int)(q % 128) / 2;
+      const int tiles_k = L.KBp / TILE_KB;
+      n = (int)(t / tiles_k) * TILE_ROWS + (l % TILE_ROWS);
+      kb = (int)(t % tiles_k) * TILE_KB + l / TILE_ROWS;
+    } else {
+      const size_t b = q / 2;
+      n = (int)(b / L.KB);
+      kb = (int)(b % L.KB);
+    }
     f = 208 + (int)(q % 2);
   }
+  return kb < L.KB;                                   // (rows past N are checked by the caller)
 }
 
-template <int QT, bool IL>
+template <int QT, bool TILED>
 __global__ void weight_layout_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                     size_t nblk) {
-  const size_t nbp = padded_blocks(nblk);
+                                     int N, int K) {
   constexpr int BB = block_bytes_of(QT);
-  const size_t total = (size_t)BB * nbp;
+  const WMap<TILED> L(N, K);
+  const size_t total = (size_t)BB * L.nbt;
   for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (size_t)gridDim.x * blockDim.x) {
-    size_t b;
-    int f;
-    if constexpr (QT == QT_Q6K) q6k_src<IL>(o, nbp, b, f); else aos_src<BB, IL>(o, b, f);
-    dst[o] = b < nblk ? src[b * BB + f] : (uint8_t)0;
+    int n, kb, f;
+    const bool in = layout_src<QT, TILED>(o, L, n, kb, f) && n < N;
+    dst[o] = in ? src[((size_t)n * L.KB + kb) * BB + f] : (uint8_t)0;
   }
 }
 
-size_t layout_bytes(int qtype, size_t nblk) {
-  return (size_t)block_bytes_of(qtype) * padded_blocks(nblk);
+size_t layout_bytes(int qtype, bool tiled, int N, int K) {
+  const size_t nbt = tiled ? WMap<true>(N, K).nbt : WMap<false>(N, K).nbt;
+  return (size_t)block_bytes_of(qtype) * nbt;
 }
 
-hipError_t launch_weight_layout(int qtype, bool interleaved, const uint8_t* src, uint8_t* dst,
-                                size_t nblk, hipStream_t st) {
-  const size_t total = layout_bytes(qtype, nblk);
+template <int QT>
+static void launch_layout_q(bool tiled, const uint8_t* src, uint8_t* dst, int N, int K, dim3 g,
+                            hipStream_t st) {
+  if (tiled) hipLaunchKernelGGL((weight_layout_kernel<QT, true>), g, dim3(256), 0, st, src, dst, N, K);
+  else hipLaunchKernelGGL((weight_layout_kernel<QT, false>), g, dim3(256), 0, st, src, dst, N, K);
+}
+
+hipError_t launch_weight_layout(int qtype, bool tiled, const uint8_t* src, uint8_t* dst, int N, int K,
+                                hipStream_t st) {
+  const size_t total = layout_bytes(qtype, tiled, N, K);
   size_t grid = (total + 255) / 256;
   if (grid > 65536) grid = 65536;
-  const dim3 g((unsigned)grid), b(256);
-  if (qtype == QT_Q4K) {
-    if (interleaved) hipLaunchKernelGGL((weight_layout_kernel<QT_Q4K, true>), g, b, 0, st, src, dst, nblk);
-    else hipLaunchKernelGGL((weight_layout_kernel<QT_Q4K, false>), g, b, 0, st, src, dst, nblk);
-  } else if (qtype == QT_Q5K) {
-    if (interleaved) hipLaunchKernelGGL((weight_layout_kernel<QT_Q5K, true>), g, b, 0, st, src, dst, nblk);
-    else hipLaunchKernelGGL((weight_layout_kernel<QT_Q5K, false>), g, b, 0, st, src, dst, nblk);
-  } else {
-    if (interleaved) hipLaunchKernelGGL((weight_layout_kernel<QT_Q6K, true>), g, b, 0, st, src, dst, nblk);
-    else hipLaunchKernelGGL((weight_layout_kernel<QT_Q6K, false>), g, b, 0, st, src, dst, nblk);
-  }
+  const dim3 g((unsigned)grid);
+  if (qtype == QT_Q4K) launch_layout_q<QT_Q4K>(tiled, src, dst, N, K, g, st);
+  else if (qtype == QT_Q5K) launch_layout_q<QT_Q5K>(tiled, src, dst, N, K, g, st);
+  else launch_layout_q<QT_Q6K>(tiled, src, dst, N, K, g, st);
   return hipGetLastError();
 }
 

@@ -124,49 +124,46 @@ __device__ __forceinline__ void dma_load_a(ARow arow, uint8_t* smem, int s_begin
 }
 
 // Loader wave 5: the weight pieces of the tile's 128 rows (rows past N are
-// clamped to N - 1: loaded, never stored).
+// clamped to N - 1: loaded, never stored).  In the tiled layout (IL) each
+// piece load of the wave is four contiguous 256-byte runs (16 rows each).
 template <int QT, int MT, bool IL>
-__device__ __forceinline__ void dma_load_w(const uint8_t* W, size_t nbp, int N, int K, int n0,
-                                           uint8_t* smem, int s_begin, int s_end, int rot) {
+__device__ __forceinline__ void dma_load_w(const uint8_t* W, int N, int K, int n0, uint8_t* smem,
+                                           int s_begin, int s_end, int rot) {
   using C = DmaCfg<QT, MT>;
   constexpr int NI = 2 * C::WP + (QT == QT_Q6K ? 2 : 0);
   const int lane = threadIdx.x & 63;
   const int nst = s_end - s_begin;
-  const int KB = K >> 8;
-  size_t rb[2];                                     // first block of each of the lane's two rows
+  const WMap<IL> L(N, K);
+  int rn[2];                                        // the lane's two rows
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    int n = n0 + 64 * h + lane;
-    n = n < N ? n : N - 1;
-    rb[h] = (size_t)n * KB;
+    const int n = n0 + 64 * h + lane;
+    rn[h] = n < N ? n : N - 1;
   }
-  auto piece = [&](size_t b, int P, int p) -> size_t {
-    if constexpr (IL) return piece_off(b, P, p);
-    else return b * (size_t)(16 * P) + (size_t)(16 * p);
-  };
   auto issue = [&](int t) {
     const int s = dma_stage(t, s_begin, nst, rot);
     const int kb = s >> 1, hb = s & 1;
     uint8_t* base = smem + (t % DMA_SLOTS) * C::SLOT + C::A_BYTES;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const size_t b = rb[h] + kb;
+      const int n = rn[h];
 #pragma unroll
       for (int q = 0; q < C::WP; ++q) {
         size_t off;
         if constexpr (QT == QT_Q5K) {
-          off = piece(b, 11, q < 3 ? q : q + 4 * hb);
+          off = L.piece(n, kb, 11, q < 3 ? q : q + 4 * hb);
         } else if constexpr (QT == QT_Q4K) {
-          off = piece(b, 9, q < 1 ? q : q + 4 * hb);
+          off = L.piece(n, kb, 9, q < 1 ? q : q + 4 * hb);
         } else {
-          if (q < 4) off = piece(b, 8, 4 * hb + q);
-          else if (q < 6) off = q6k_qh_base(nbp) + piece(b, 4, 2 * hb + (q - 4));
-          else off = q6k_sc_base(nbp) + 16 * b;
+          if (q < 4) off = L.piece(n, kb, 8, 4 * hb + q);
+          else if (q < 6) off = L.qh_base() + L.piece(n, kb, 4, 2 * hb + (q - 4));
+          else off = L.sc(n, kb);
         }
         dma16(W + off, base + (q * 128 + 64 * h) * 16);
       }
+      // the aligned word holding this row's d (and a neighbour's)
       if constexpr (QT == QT_Q6K)
-        dma4(W + q6k_d_base(nbp) + ((2 * b) & ~(size_t)3), base + C::WP * 128 * 16 + 64 * h * 4);
+        dma4(W + (L.d(n, kb) & ~(size_t)3), base + C::WP * 128 * 16 + 64 * h * 4);
     }
   };
   constexpr int AHEAD = DMA_SLOTS - 1;
@@ -182,8 +179,10 @@ __device__ __forceinline__ void dma_load_w(const uint8_t* W, size_t nbp, int N, 
 }
 
 // Compute waves 0-3: acc[i][j] += C[n][m] of the 16x16 sub-tiles (half
-// i < MTA, weight sub-tile j of the wave's 32 rows) over the stages.
-template <int QT, int MT, int MTA>
+// i < MTA, weight sub-tile j of the wave's 32 rows) over the stages.  IL:
+// the weights are in the tiled layout (selects which half of a d word is
+// the row's).
+template <int QT, int MT, int MTA, bool IL>
 __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t* smem, int s_begin,
                                             int s_end, int rot, floatx4 (&acc)[MT][2]) {
   using C = DmaCfg<QT, MT>;
@@ -191,14 +190,12 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
   const int kq = lane >> 4, sub = 8 * (kq & 1), pq = kq >> 1;
   const int nst = s_end - s_begin;
   const int KB = K >> 8;
-  int nloc[2];
-  size_t rb[2];
+  int nloc[2], rn[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     nloc[j] = wave * 32 + 16 * j + (lane & 15);
-    int n = n0 + nloc[j];
-    n = n < N ? n : N - 1;
-    rb[j] = (size_t)n * KB;
+    const int n = n0 + nloc[j];
+    rn[j] = n < N ? n : N - 1;                      // the row the loader fetched
   }
 #pragma unroll
   for (int i = 0; i < MTA; ++i)
@@ -247,7 +244,10 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
         r.qh = *(const uint2*)(pc(4 + pq) + sub);
         r.sc = *(const uint2*)(pc(6) + 8 * hb);
         const uint32_t dw = *(const uint32_t*)(Ws + C::WP * 128 * 16 + 4 * nloc[j]);
-        r.d = dw >> (16 * (int)((rb[j] + kb) & 1));
+        // the row's half of the word: tiled, the blocks of rows n and n ^ 1
+        // share it; canonical, the blocks b and b ^ 1
+        const int half = IL ? (rn[j] & 1) : (int)(((size_t)rn[j] * KB + kb) & 1);
+        r.d = dw >> (16 * half);
         decode_q6k_half(r, kq, wf[j]);
       }
     }

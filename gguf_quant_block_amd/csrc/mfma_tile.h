@@ -168,9 +168,9 @@ struct TileRows {
 
 // Main loop of one tile over the stages [s_begin, s_end) of K, walked from
 // stage s_begin + rot (wrapping), for the first MTA (<= MT) 16-row halves of
-// the tile.  W is one weight matrix [N, K] over nbp (padded) blocks, in the
-// piece-interleaved device layout of layout.h (IL) or in the canonical one
-// (Q4_K / Q5_K blocks in order; Q6_K row-major QL | QH | SC | D planes).  n0 is its
+// the tile.  W is one weight matrix [N, K] in the tiled device layout of
+// layout.h (IL) or in the canonical one (Q4_K / Q5_K blocks in order; Q6_K
+// row-major QL | QH | SC | D planes).  n0 is its
 // first weight row (rows past N are clamped to N - 1: loaded, never stored).
 // acc[i][j] receives C[n][m] of the 16x16 sub-tile (half i < MTA, weight
 // sub-tile j).  A stage is SH half super-blocks (128*SH values of K; stages
@@ -178,7 +178,7 @@ struct TileRows {
 // while a stage computes; PD = 2: the next two stages' (three register sets).
 // The loop body has no data-dependent branches.
 template <int QT, int MT, int NT, int MTA, bool IL, int PD, int SH = 1>
-__device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int N,
+__device__ __forceinline__ void tile_mainloop(const uint8_t* W, int N,
                                               int K, int n0, int s_begin, int s_end, int rot,
                                               const TileRows<MT>& rows,
                                               f16 (*As)[16 * MT * astr(SH)],
@@ -190,7 +190,6 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4;
-  const int KB = K >> 8;
 
   // rows of this lane's weight fragments
   int nrow[NT];
@@ -200,11 +199,7 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
     nrow[j] = n < N ? n : N - 1;
   }
 
-  // byte offset of 16-byte piece p of block b in a plane of P pieces per block
-  auto piece = [&](size_t b, int P, int p) -> size_t {
-    if constexpr (IL) return piece_off(b, P, p);
-    else return b * (size_t)(16 * P) + (size_t)(16 * p);
-  };
+  const WMap<IL> L(N, K);
   // raw bytes of the lane's rows for stage s (half-block hb of block kb):
   // 8-byte slices of the 16-byte pieces
   auto load_raw_q5 = [&](int s, RawQ5* raw) {
@@ -212,11 +207,11 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
     const int sub = 8 * (kq & 1), pq = kq >> 1;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const size_t b = (size_t)nrow[j] * KB + kb;
-      raw[j].hdr = *(const uint4*)(W + piece(b, 11, 0));
-      raw[j].qsA = *(const uint2*)(W + piece(b, 11, 3 + 4 * hb + pq) + sub);
-      raw[j].qsB = *(const uint2*)(W + piece(b, 11, 5 + 4 * hb + pq) + sub);
-      raw[j].qh = *(const uint2*)(W + piece(b, 11, 1 + pq) + sub);
+      const int n = nrow[j];
+      raw[j].hdr = *(const uint4*)(W + L.piece(n, kb, 11, 0));
+      raw[j].qsA = *(const uint2*)(W + L.piece(n, kb, 11, 3 + 4 * hb + pq) + sub);
+      raw[j].qsB = *(const uint2*)(W + L.piece(n, kb, 11, 5 + 4 * hb + pq) + sub);
+      raw[j].qh = *(const uint2*)(W + L.piece(n, kb, 11, 1 + pq) + sub);
     }
   };
   auto load_raw_q4 = [&](int s, RawQ4* raw) {
@@ -224,10 +219,10 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
     const int sub = 8 * (kq & 1), pq = kq >> 1;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const size_t b = (size_t)nrow[j] * KB + kb;
-      raw[j].hdr = *(const uint4*)(W + piece(b, 9, 0));
-      raw[j].qsA = *(const uint2*)(W + piece(b, 9, 1 + 4 * hb + pq) + sub);
-      raw[j].qsB = *(const uint2*)(W + piece(b, 9, 3 + 4 * hb + pq) + sub);
+      const int n = nrow[j];
+      raw[j].hdr = *(const uint4*)(W + L.piece(n, kb, 9, 0));
+      raw[j].qsA = *(const uint2*)(W + L.piece(n, kb, 9, 1 + 4 * hb + pq) + sub);
+      raw[j].qsB = *(const uint2*)(W + L.piece(n, kb, 9, 3 + 4 * hb + pq) + sub);
     }
   };
   auto load_raw_q6 = [&](int s, RawQ6* raw) {
@@ -235,12 +230,12 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, size_t nbp, int 
     const int sub = 8 * (kq & 1), pq = kq >> 1;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const size_t b = (size_t)nrow[j] * KB + kb;
-      raw[j].qlA = *(const uint2*)(W + piece(b, 8, 4 * hb + pq) + sub);
-      raw[j].qlB = *(const uint2*)(W + piece(b, 8, 4 * hb + 2 + pq) + sub);
-      raw[j].qh = *(const uint2*)(W + q6k_qh_base(nbp) + piece(b, 4, 2 * hb + pq) + sub);
-      raw[j].sc = *(const uint2*)(W + q6k_sc_base(nbp) + 16 * b + 8 * hb);
-      raw[j].d = *(const uint16_t*)(W + q6k_d_base(nbp) + 2 * b);
+      const int n = nrow[j];
+      raw[j].qlA = *(const uint2*)(W + L.piece(n, kb, 8, 4 * hb + pq) + sub);
+      raw[j].qlB = *(const uint2*)(W + L.piece(n, kb, 8, 4 * hb + 2 + pq) + sub);
+      raw[j].qh = *(const uint2*)(W + L.qh_base() + L.piece(n, kb, 4, 2 * hb + pq) + sub);
+      raw[j].sc = *(const uint2*)(W + L.sc(n, kb) + 8 * hb);
+      raw[j].d = *(const uint16_t*)(W + L.d(n, kb));
     }
   };
   using Raw = typename std::conditional<

@@ -202,14 +202,13 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
   // only the halves that hold routed rows run (mt_act is uniform per workgroup)
   floatx4 acc[MT][NT];
   const uint8_t* We = W + (size_t)e * expert_bytes;
-  const size_t nbp = padded_blocks((size_t)N * (K >> 8));
   const int S = K / (KSTAGE * MOE_SH);
   const int rot = (ti + nt) % S;           // spread concurrent loads over K
   // (active halves rounded up to 1, 2, 4 or MT)
-  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, false, MOE_PD, MOE_SH>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act == 2 || MT == 2) tile_mainloop<QT, MT, NT, (MT < 2 ? MT : 2), false, MOE_PD, MOE_SH>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act <= 4 || MT == 4) tile_mainloop<QT, MT, NT, (MT < 4 ? MT : 4), false, MOE_PD, MOE_SH>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
-  else tile_mainloop<QT, MT, NT, MT, false, MOE_PD, MOE_SH>(We, nbp, N, K, n0, 0, S, rot, rows, As, acc);
+  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, false, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act == 2 || MT == 2) tile_mainloop<QT, MT, NT, (MT < 2 ? MT : 2), false, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act <= 4 || MT == 4) tile_mainloop<QT, MT, NT, (MT < 4 ? MT : 4), false, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else tile_mainloop<QT, MT, NT, MT, false, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
 
 #pragma unroll
   for (int i = 0; i < MT; ++i) {

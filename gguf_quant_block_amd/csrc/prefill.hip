@@ -104,8 +104,7 @@ prefill_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   // channels instead of hitting the same addresses together
   const int nst = s_end - s_begin;
   const int rot = nst > 0 ? (nt + mt) % nst : 0;
-  tile_mainloop<QT, MT, NT, MT, true, 1>(W, padded_blocks((size_t)N * (K >> 8)), N, K, n0, s_begin, s_end, rot, rows, As,
-                                acc);
+  tile_mainloop<QT, MT, NT, MT, true, 1>(W, N, K, n0, s_begin, s_end, rot, rows, As, acc);
 
   prefill_epilogue<MT, NT>(acc, R, Y, P, M, N, m0, n0, sp, splits);
 }
@@ -140,12 +139,11 @@ prefill_dma_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
     return;
   }
   if (wave == 4 + DMA_ALOADERS) {
-    dma_load_w<QT, MT, true>(W, padded_blocks((size_t)N * (K >> 8)), N, K, n0, smem, s_begin,
-                             s_end, rot);
+    dma_load_w<QT, MT, true>(W, N, K, n0, smem, s_begin, s_end, rot);
     return;
   }
   floatx4 acc[MT][2];
-  dma_compute<QT, MT, MT>(N, K, n0, smem, s_begin, s_end, rot, acc);
+  dma_compute<QT, MT, MT, true>(N, K, n0, smem, s_begin, s_end, rot, acc);
   prefill_epilogue<MT, 2>(acc, R, Y, P, M, N, m0, n0, sp, splits);
 }
 

@@ -12,7 +12,7 @@
  *   - section "Transformation": the weights are converted once; Q6_K blocks
  *     are regrouped into the planes QL|QH|SC|D (done on the device at create
  *     time here, where every plane, and the Q4_K / Q5_K blocks, are also
- *     piece-interleaved over groups of 64 blocks for coalesced wave64 loads);
+ *     cut into tiles of 16 rows x 4 blocks for coalesced wave64 loads);
  *   - section "Implementation": the path is chosen from the number of
  *     activation rows M: M < 8 -> per-32 int8 activation quantisation and an
  *     int8 GEMV; M >= 8 -> each 256-value block decoded once into on-chip
@@ -154,15 +154,17 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
  *
  * fc_gguf_debug_weights: copies the handle's device weight bytes to device
  *   memory `dst` (fc_gguf_info's weight_bytes long).  Device layout, per
- *   matrix (experts one after another): blocks b = n*(K/256) + kb, padded
- *   with zero bytes to a multiple of 64.  Q4_K / Q5_K: one plane of P = 9 /
- *   P = 11 pieces (16 bytes) per block.  Q6_K: planes QL (P = 8) | QH (P = 4) | SC (16 B
- *   per block, in block order) | D (2 B per block, in block order), each over
- *   the padded block count.  Single-matrix handles store the QL, QH, Q4_K and
- *   Q5_K planes piece-interleaved: groups of 64 consecutive blocks piece-major,
- *   piece p of block b at ((b/64)*P + p)*1024 + (b%64)*16 within its plane.
- *   Grouped handles store every plane in block order (piece p of block b at
- *   b*16*P + 16*p).
+ *   matrix (experts one after another), block (n, kb) being the kb-th
+ *   super-block of row n, cut into 16-byte pieces.  Q4_K / Q5_K: one plane
+ *   of P = 9 / 11 pieces per block.  Q6_K: planes QL (P = 8) | QH (P = 4) |
+ *   SC (P = 1) | D (2 bytes per block), each over the same padded block count.
+ *   Single-matrix handles are tiled: rows padded with zero bytes to a multiple
+ *   of 16 and blocks per row to a multiple of 4 (KBp); tile
+ *   t = (n/16)*(KBp/4) + kb/4 holds 16 rows x 4 blocks, piece p of block
+ *   (n, kb) at (t*P + p)*1024 + l*16 within its plane, l = (kb%4)*16 + n%16;
+ *   D at t*128 + l*2.  Grouped handles keep the blocks in order
+ *   b = n*(K/256) + kb, padded with zero bytes to a multiple of 64 blocks:
+ *   piece p of block b at b*16*P + 16*p; D at 2*b.
  */
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s,
                            int32_t* T, void* stream);

@@ -3,7 +3,7 @@ the CPU oracle; input ranks and row counts that change between calls.
 
 Bit-exact: the int8 activation quantisation (codes, scales, group sums), the
 integer sub-block dot sums, and the device weight layout (Q6_K plane regroup
-plus the 64-block piece interleave).  Outputs: max
+plus the 16-row x 4-block tiling).  Outputs: max
 relative error <= 1e-3 against the oracle's exact emulation of the int8 path
 (metric max |y-r| / max(|r|, rms(r))).
 """
@@ -66,66 +66,69 @@ def test_quantize_bit_exact(gpu_lib, M, K):
 
 # ---------------------------------------------------------------- regroup --
 
-def _pad_blocks(plane, fill=0):
-    nblk = plane.shape[0]
-    nbp = -(-nblk // 64) * 64
-    out = np.full((nbp, plane.shape[1]), fill, dtype=plane.dtype)
-    out[:nblk] = plane
-    return out
+def _tile(plane, N, KB, P, fill=0):
+    """Canonical plane bytes [N*KB, 16*P] (block (n, kb) at row n*KB + kb) ->
+    the tiled device order: tiles of 16 rows x 4 blocks (rows padded to 16,
+    blocks per row to 4), tile t = (n/16)*(KBp/4) + kb/4 stored piece-major,
+    the blocks of a piece in the order (kb % 4)*16 + n % 16."""
+    Np, KBp = -(-N // 16) * 16, -(-KB // 4) * 4
+    x = np.full((Np, KBp, P, 16), fill, dtype=plane.dtype)
+    x[:N, :KB] = plane.reshape(N, KB, P, 16)
+    return x.reshape(Np // 16, 16, KBp // 4, 4, P, 16).transpose(0, 2, 4, 3, 1, 5).reshape(-1)
 
 
-def _interleave(plane, P):
-    """[nblk, 16P] bytes -> groups of 64 blocks stored piece-major: [g][p][lane][16]."""
-    x = _pad_blocks(plane).reshape(-1, 64, P, 16)
-    return x.transpose(0, 2, 1, 3).reshape(-1)
+def _tile_d(d, N, KB):
+    """Q6_K d bytes [N*KB, 2] -> tiled: 128 bytes per tile, slot (kb % 4)*16 + n % 16."""
+    Np, KBp = -(-N // 16) * 16, -(-KB // 4) * 4
+    x = np.zeros((Np, KBp, 2), dtype=d.dtype)
+    x[:N, :KB] = d.reshape(N, KB, 2)
+    return x.reshape(Np // 16, 16, KBp // 4, 4, 2).transpose(0, 2, 3, 1, 4).reshape(-1)
 
 
-def expected_device_bytes(w, qtype):
-    """The library's device copy of canonical blocks w: Q4_K / Q5_K pieces
-    interleaved over groups of 64 blocks; Q6_K planes QL | QH | SC | D (the
-    oracle's regroup) with QL and QH interleaved the same way, zero-padded to
-    64 blocks."""
+def expected_device_bytes(w, qtype, N, K):
+    """The library's device copy of canonical blocks w[N, K/256*B] in the tiled
+    layout: Q4_K / Q5_K blocks as one plane of 9 / 11 pieces; Q6_K planes
+    QL | QH | SC | D (the oracle's regroup), each tiled the same way."""
+    KB = K // 256
     if qtype == "q4_k":
-        return _interleave(w.reshape(-1, 144), 9)
+        return _tile(w.reshape(-1, 144), N, KB, 9)
     if qtype == "q5_k":
-        return _interleave(w.reshape(-1, 176), 11)
+        return _tile(w.reshape(-1, 176), N, KB, 11)
     planes = okq.q6k_regroup(w)
-    nblk = w.reshape(-1, 210).shape[0]
+    nblk = N * KB
     ql = planes[:128 * nblk].reshape(nblk, 128)
     qh = planes[128 * nblk:192 * nblk].reshape(nblk, 64)
     sc = planes[192 * nblk:208 * nblk].reshape(nblk, 16)
     d = planes[208 * nblk:].reshape(nblk, 2)
-    return np.concatenate([_interleave(ql, 8), _interleave(qh, 4),
-                           _pad_blocks(sc).reshape(-1), _pad_blocks(d).reshape(-1)])
+    return np.concatenate([_tile(ql, N, KB, 8), _tile(qh, N, KB, 4), _tile(sc, N, KB, 1),
+                           _tile_d(d, N, KB)])
 
 
-@pytest.mark.parametrize("N,K", [(3, 768), (512, 2048), (77, 1280)])
+@pytest.mark.parametrize("N,K", [(3, 768), (512, 2048), (77, 1280), (40, 3072)])
 def test_device_layout_bytes(gpu_lib, N, K):
-    w = synth.q6k_blocks(N, K, synth.rng(51, N, 0))
-    got = _host(_fc(w, "q6_k", N, K).debug_weights())
-    assert np.array_equal(got, expected_device_bytes(w, "q6_k"))
-    w5 = synth.q5k_blocks(N, K, synth.rng(51, N + 1, 0))
-    got5 = _host(_fc(w5, "q5_k", N, K).debug_weights())
-    assert np.array_equal(got5, expected_device_bytes(w5, "q5_k"))
-    w4 = synth.q4k_blocks(N, K, synth.rng(51, N + 2, 0))
-    got4 = _host(_fc(w4, "q4_k", N, K).debug_weights())
-    assert np.array_equal(got4, expected_device_bytes(w4, "q4_k"))
+    for i, qtype in enumerate(QTYPES):
+        w = synth.blocks(qtype, N, K, synth.rng(51, N + i, 0))
+        got = _host(_fc(w, qtype, N, K).debug_weights())
+        assert np.array_equal(got, expected_device_bytes(w, qtype, N, K)), qtype
 
 
 def test_layout_helper_is_a_permutation():
     # the expected-bytes helper itself: every canonical byte appears exactly
-    # once, and block 64g + l's piece p lands at ((g*P + p)*64 + l)*16
-    nblk = 70
-    idx = np.arange(nblk * 176, dtype=np.int64).reshape(nblk, 176)
-    x = _pad_blocks(idx, fill=-1).reshape(-1, 64, 11, 16).transpose(0, 2, 1, 3).reshape(-1)
-    assert x.size == 128 * 176
-    assert np.array_equal(np.sort(x[x >= 0]), np.arange(nblk * 176))
-    for b, p in [(0, 0), (5, 3), (63, 10), (64, 0), (69, 7)]:
-        g, l = divmod(b, 64)
-        o = ((g * 11 + p) * 64 + l) * 16
-        assert np.array_equal(x[o:o + 16], idx[b, 16 * p:16 * p + 16])
-    w = synth.q5k_blocks(nblk, 256, synth.rng(51, 0, 1))
-    assert np.array_equal(expected_device_bytes(w, "q5_k")[x >= 0], w.reshape(-1)[x[x >= 0]])
+    # once, and piece p of block (n, kb) lands at ((t*P + p)*64 + l)*16 with
+    # t = (n//16)*(KBp//4) + kb//4 and l = (kb%4)*16 + n%16
+    N, KB, P = 37, 7, 11
+    idx = np.arange(N * KB * 16 * P, dtype=np.int64).reshape(N * KB, 16 * P)
+    x = _tile(idx, N, KB, P, fill=-1)
+    Np, KBp = 48, 8
+    assert x.size == Np * KBp * 16 * P
+    assert np.array_equal(np.sort(x[x >= 0]), np.arange(N * KB * 16 * P))
+    for n, kb, p in [(0, 0, 0), (5, 3, 3), (15, 6, 10), (16, 0, 0), (36, 4, 7), (20, 5, 1)]:
+        t = (n // 16) * (KBp // 4) + kb // 4
+        l = (kb % 4) * 16 + n % 16
+        o = ((t * P + p) * 64 + l) * 16
+        assert np.array_equal(x[o:o + 16], idx[n * KB + kb, 16 * p:16 * p + 16])
+    w = synth.q5k_blocks(N, KB * 256, synth.rng(51, 0, 1))
+    assert np.array_equal(expected_device_bytes(w, "q5_k", N, KB * 256)[x >= 0], w.reshape(-1)[x[x >= 0]])
 
 
 # --------------------------------------------------------------- int sums --
