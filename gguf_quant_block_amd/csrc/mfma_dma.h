@@ -39,9 +39,14 @@ namespace fcg {
 #ifndef FCG_DMA_ALOADERS
 #define FCG_DMA_ALOADERS 1
 #endif
+#ifndef FCG_DMA_CWAVES
+#define FCG_DMA_CWAVES 4
+#endif
 constexpr int DMA_SLOTS = FCG_DMA_SLOTS;          // LDS ring depth (stages)
 constexpr int DMA_ALOADERS = FCG_DMA_ALOADERS;    // waves loading the activation tile
-constexpr int DMA_THREADS = 64 * (4 + DMA_ALOADERS + 1);
+constexpr int DMA_CWAVES = FCG_DMA_CWAVES;        // compute waves (4 or 8)
+constexpr int DMA_NTW = 8 / DMA_CWAVES;           // 16-row weight sub-tiles per compute wave
+constexpr int DMA_THREADS = 64 * (DMA_CWAVES + DMA_ALOADERS + 1);
 
 template <int QT, int MT>
 struct DmaCfg {
@@ -184,23 +189,24 @@ __device__ __forceinline__ void dma_load_w(const uint8_t* W, int N, int K, int n
 // the row's).
 template <int QT, int MT, int MTA, bool IL>
 __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t* smem, int s_begin,
-                                            int s_end, int rot, floatx4 (&acc)[MT][2]) {
+                                            int s_end, int rot, floatx4 (&acc)[MT][DMA_NTW]) {
+  constexpr int NTW = DMA_NTW;
   using C = DmaCfg<QT, MT>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kq = lane >> 4, sub = 8 * (kq & 1), pq = kq >> 1;
   const int nst = s_end - s_begin;
   const int KB = K >> 8;
-  int nloc[2], rn[2];
+  int nloc[NTW], rn[NTW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    nloc[j] = wave * 32 + 16 * j + (lane & 15);
+  for (int j = 0; j < NTW; ++j) {
+    nloc[j] = wave * 16 * NTW + 16 * j + (lane & 15);
     const int n = n0 + nloc[j];
     rn[j] = n < N ? n : N - 1;                      // the row the loader fetched
   }
 #pragma unroll
   for (int i = 0; i < MTA; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NTW; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   stage_barrier();                                  // stage 0 has landed
   for (int t = 0; t < nst; ++t) {
@@ -220,9 +226,9 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
     half8v afc[MTA], afn[MTA];
     lda(0, afc);
     asm volatile("" ::: "memory");                  // keep the reads ahead of their use
-    half8v wf[2][4];
+    half8v wf[NTW][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NTW; ++j) {
       auto pc = [&](int q) { return Ws + (q * 128 + nloc[j]) * 16; };
       if constexpr (QT == QT_Q5K) {
         RawQ5 r;
@@ -258,7 +264,7 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
 #pragma unroll
       for (int i = 0; i < MTA; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NTW; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j][g], afc[i], acc[i][j], 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < MTA; ++i) afc[i] = afn[i];

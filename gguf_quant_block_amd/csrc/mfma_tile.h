@@ -15,11 +15,9 @@
 //     range, or the gathered rows of one expert).
 //   * Each wave owns 16*NT weight rows.  Its lanes load those rows' raw block
 //     bytes one stage ahead and decode them straight into the MFMA operand
-//     registers.  Decoding is exact up to one f16 rounding:
-//       magic f16 (1024 + q) from a byte permute, t = fma(1024+q, sc, -1024*sc
-//       [Q6_K: -1056*sc]) = sc*q [sc*(q-32)] exactly, then w = t*d - dmin*m
-//       [Q6_K: t*d] with a single rounding (Q4_K as Q5_K, without the fifth
-//       bit).
+//     registers (Q45Half / Q6Half): a byte permute builds the magic f16
+//     (1024 + q); Q4_K / Q5_K: fma(1024+q, sc, -1024*sc) = sc*q exactly, then
+//     w = (sc*q)*d - dmin*m with one rounding; Q6_K: w = (q - 32)*(sc*d).
 //   * Only the first MTA 16-row halves of the tile are staged and run on the
 //     matrix cores: a tile whose rows end early skips its empty halves
 //     (llama.cpp PR #28301, section Overview, skips the empty upper half of
@@ -88,71 +86,119 @@ __device__ __forceinline__ half8v decode8(uint32_t c0, uint32_t c1, half2v sc2, 
 
 __device__ __forceinline__ half2v splat(f16 x) { half2v r; r[0] = x; r[1] = x; return r; }
 
-// Decode the lane's 4 x 8 weights of one half-block (k-step g = 0..3 covers
-// values 128hb + 32g + 8kq .. +7 of its row).  Q4_K: HAS_QH = false and the
-// fifth-bit words are ignored.
-template <bool HAS_QH, class Raw>
-__device__ __forceinline__ void decode_q45k_half(const Raw& r, uint2 qh, int hb, half8v out[4]) {
-  const uint32_t w0 = r.hdr.y, w1 = r.hdr.z, w2 = r.hdr.w;
-  uint32_t scb, mb;   // bytes g = 0..3: scale / min of sub-block 4hb + g
-  if (hb == 0) {
-    scb = w0 & 0x3F3F3F3Fu;
-    mb = w1 & 0x3F3F3F3Fu;
-  } else {
-    scb = (w2 & 0x0F0F0F0Fu) | ((w0 >> 2) & 0x30303030u);
-    mb = ((w2 >> 4) & 0x0F0F0F0Fu) | ((w1 >> 2) & 0x30303030u);
-  }
-  const f16 d = __builtin_bit_cast(f16, (uint16_t)(r.hdr.x & 0xFFFF));
-  const float dmin = h2f(r.hdr.x >> 16);
-  const half2v d2 = splat(d);
-  const uint32_t src[4] = {r.qsA.x, r.qsA.x, r.qsB.x, r.qsB.x};
-  const uint32_t src1[4] = {r.qsA.y, r.qsA.y, r.qsB.y, r.qsB.y};
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int sh = 4 * (g & 1);
-    const int j = 4 * hb + g;
-    uint32_t c0 = (src[g] >> sh) & 0x0F0F0F0Fu;
-    uint32_t c1 = (src1[g] >> sh) & 0x0F0F0F0Fu;
-    if constexpr (HAS_QH) {
-      c0 |= ((qh.x >> j) & 0x01010101u) << 4;
-      c1 |= ((qh.y >> j) & 0x01010101u) << 4;
+// Q4_K / Q5_K half-block decoder: a per-half setup, then the lane's 8
+// weights of k-step g = 0..3 (values 128hb + 32g + 8kq .. +7 of its row).
+// Decoding is exact up to one f16 rounding: (1024 + q) * sc - 1024 * sc =
+// sc * q exactly (sc * q <= 63 * 31 < 2048), then w = (sc * q) * d - dmin * m.
+// The four sub-blocks' scales and mins become exact f16 pairs with packed
+// arithmetic: magic f16 (1024 + byte) - 1024; bias = -1024 * sc is exact (a
+// power-of-two product; |bias| <= 64512), and -dmin * m is one correctly
+// rounded f16 product.  Q4_K: HAS_QH = false (no fifth bit).
+template <bool HAS_QH>
+struct Q45Half {
+  half2v sc01, sc23, b01, b23, m01, m23, d2;
+  uint32_t a0, a1, b0, b1;      // qsA.x, qsA.y, qsB.x, qsB.y
+  uint32_t qhx, qhy;            // fifth bits of this half's sub-blocks at bits 0..3
+
+  __device__ __forceinline__ void init(uint4 hdr, uint2 qsA, uint2 qsB, uint2 qh, int hb) {
+    const uint32_t w0 = hdr.y, w1 = hdr.z, w2 = hdr.w;
+    uint32_t scb, mb;   // bytes g = 0..3: scale / min of sub-block 4hb + g
+    if (hb == 0) {
+      scb = w0 & 0x3F3F3F3Fu;
+      mb = w1 & 0x3F3F3F3Fu;
+    } else {
+      scb = (w2 & 0x0F0F0F0Fu) | ((w0 >> 2) & 0x30303030u);
+      mb = ((w2 >> 4) & 0x0F0F0F0Fu) | ((w1 >> 2) & 0x30303030u);
     }
-    const int sc = (scb >> (8 * g)) & 0xFF;
-    const int mn = (mb >> (8 * g)) & 0xFF;
-    const f16 scf = (f16)(float)sc;
-    const half2v sc2 = splat(scf);
-    const half2v bias2 = splat((f16)(float)(-1024 * sc));
-    const half2v negdmm2 = splat((f16)(-(dmin * (float)mn)));
-    out[g] = decode8(c0, c1, sc2, bias2, d2, negdmm2);
+    const half2v k1024 = splat((f16)1024.f), nk = splat((f16)-1024.f);
+    sc01 = magic_pair(scb, 0x04010400u) - k1024;
+    sc23 = magic_pair(scb, 0x04030402u) - k1024;
+    b01 = sc01 * nk;
+    b23 = sc23 * nk;
+    const half2v ndmin = splat(-__builtin_bit_cast(f16, (uint16_t)(hdr.x >> 16)));
+    m01 = (magic_pair(mb, 0x04010400u) - k1024) * ndmin;
+    m23 = (magic_pair(mb, 0x04030402u) - k1024) * ndmin;
+    d2 = splat(__builtin_bit_cast(f16, (uint16_t)(hdr.x & 0xFFFF)));
+    a0 = qsA.x; a1 = qsA.y; b0 = qsB.x; b1 = qsB.y;
+    if constexpr (HAS_QH) {
+      qhx = qh.x >> (4 * hb);
+      qhy = qh.y >> (4 * hb);
+    } else {
+      qhx = qhy = 0;
+    }
   }
-}
+  __device__ __forceinline__ half8v frag(int g) const {
+    const int sh = 4 * (g & 1);
+    const uint32_t s0 = g < 2 ? a0 : b0, s1 = g < 2 ? a1 : b1;
+    uint32_t c0 = (s0 >> sh) & 0x0F0F0F0Fu;
+    uint32_t c1 = (s1 >> sh) & 0x0F0F0F0Fu;
+    if constexpr (HAS_QH) {
+      c0 |= (qhx << (4 - g)) & 0x10101010u;
+      c1 |= (qhy << (4 - g)) & 0x10101010u;
+    }
+    const half2v scp = g < 2 ? sc01 : sc23, bp = g < 2 ? b01 : b23, mp = g < 2 ? m01 : m23;
+    return decode8(c0, c1, splat(scp[g & 1]), splat(bp[g & 1]), d2, splat(mp[g & 1]));
+  }
+};
+
+// Q6_K half-block decoder (same k-step layout).  w = (q - 32) * (sc * d):
+// (1024 + q) - 1056 = q - 32 exactly, and sc * d is one f16 product of the
+// signed 8-bit scale and d; two roundings in all, with no intermediate
+// beyond the weight's own magnitude for any scale in [-128, 127].
+struct Q6Half {
+  half2v scd01, scd23;          // sc * d of the lane's sub-blocks for k-steps 0, 1 | 2, 3
+  uint32_t la0, la1, lb0, lb1;  // qlA.x, qlA.y, qlB.x, qlB.y
+  uint32_t qhx, qhy;
+
+  __device__ __forceinline__ void init(uint2 qlA, uint2 qlB, uint2 qh, uint2 sc, uint32_t dbits,
+                                       int kq) {
+    // sub-block of k-step g within the half: 2g + kq/2 (bytes p, 2 + p of
+    // sc.x and p, 2 + p of sc.y, p = kq/2), offset to unsigned for the magic
+    const uint32_t p = (uint32_t)(kq >> 1);
+    const uint32_t sel = p | ((p + 2) << 8) | ((p + 4) << 16) | ((p + 6) << 24);
+    const uint32_t u = __builtin_amdgcn_perm(sc.y, sc.x, sel) ^ 0x80808080u;
+    const half2v k1152 = splat((f16)1152.f);
+    const half2v d2 = splat(__builtin_bit_cast(f16, (uint16_t)(dbits & 0xFFFF)));
+    scd01 = (magic_pair(u, 0x04010400u) - k1152) * d2;
+    scd23 = (magic_pair(u, 0x04030402u) - k1152) * d2;
+    la0 = qlA.x; la1 = qlA.y; lb0 = qlB.x; lb1 = qlB.y;
+    qhx = qh.x;
+    qhy = qh.y;
+  }
+  __device__ __forceinline__ half8v frag(int g) const {
+    const int sh = 4 * (g >> 1);
+    const uint32_t s0 = (g & 1) ? lb0 : la0, s1 = (g & 1) ? lb1 : la1;
+    const uint32_t hx = g < 3 ? (qhx << (4 - 2 * g)) : (qhx >> 2);
+    const uint32_t hy = g < 3 ? (qhy << (4 - 2 * g)) : (qhy >> 2);
+    const uint32_t c0 = ((s0 >> sh) & 0x0F0F0F0Fu) | (hx & 0x30303030u);
+    const uint32_t c1 = ((s1 >> sh) & 0x0F0F0F0Fu) | (hy & 0x30303030u);
+    const half2v scd = splat((g < 2 ? scd01 : scd23)[g & 1]);
+    const half2v k1056 = splat((f16)1056.f);
+    const half2v p0 = (magic_pair(c0, 0x04010400u) - k1056) * scd;
+    const half2v p1 = (magic_pair(c0, 0x04030402u) - k1056) * scd;
+    const half2v p2 = (magic_pair(c1, 0x04010400u) - k1056) * scd;
+    const half2v p3 = (magic_pair(c1, 0x04030402u) - k1056) * scd;
+    return make_frag(p0, p1, p2, p3);
+  }
+};
 
 __device__ __forceinline__ void decode_q5k_half(const RawQ5& r, int hb, half8v out[4]) {
-  decode_q45k_half<true>(r, r.qh, hb, out);
+  Q45Half<true> h;
+  h.init(r.hdr, r.qsA, r.qsB, r.qh, hb);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) out[g] = h.frag(g);
 }
 __device__ __forceinline__ void decode_q4k_half(const RawQ4& r, int hb, half8v out[4]) {
-  decode_q45k_half<false>(r, uint2{0u, 0u}, hb, out);
-}
-
-__device__ __forceinline__ void decode_q6k_half(const RawQ6& r, int kq, half8v out[4]) {
-  const f16 d = __builtin_bit_cast(f16, (uint16_t)(r.d & 0xFFFF));
-  const half2v d2 = splat(d);
-  const half2v zero2 = splat((f16)0.f);
-  const uint32_t srcx[4] = {r.qlA.x, r.qlB.x, r.qlA.x, r.qlB.x};
-  const uint32_t srcy[4] = {r.qlA.y, r.qlB.y, r.qlA.y, r.qlB.y};
+  Q45Half<false> h;
+  h.init(r.hdr, r.qsA, r.qsB, uint2{0u, 0u}, hb);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int sh = 4 * (g >> 1);
-    const uint32_t c0 = ((srcx[g] >> sh) & 0x0F0F0F0Fu) | (((r.qh.x >> (2 * g)) & 0x03030303u) << 4);
-    const uint32_t c1 = ((srcy[g] >> sh) & 0x0F0F0F0Fu) | (((r.qh.y >> (2 * g)) & 0x03030303u) << 4);
-    // sub-block of values 32g + 8kq .. +7 within the half: 2g + kq/2
-    const int si = 2 * g + (kq >> 1);
-    const uint32_t scw = si < 4 ? r.sc.x : r.sc.y;
-    const int sc = sext8(scw >> (8 * (si & 3)));
-    const half2v sc2 = splat((f16)(float)sc);
-    const half2v bias2 = splat((f16)(float)(-1056 * sc));
-    out[g] = decode8(c0, c1, sc2, bias2, d2, zero2);
-  }
+  for (int g = 0; g < 4; ++g) out[g] = h.frag(g);
+}
+__device__ __forceinline__ void decode_q6k_half(const RawQ6& r, int kq, half8v out[4]) {
+  Q6Half h;
+  h.init(r.qlA, r.qlB, r.qh, r.sc, r.d, kq);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) out[g] = h.frag(g);
 }
 
 

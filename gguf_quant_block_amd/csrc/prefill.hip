@@ -129,22 +129,22 @@ prefill_dma_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   // workgroups sharing activation or weight rows start at different stages
   const int rot = nst > 0 ? (nt + mt) % nst : 0;
   const int wave = threadIdx.x >> 6;
-  if (wave >= 4 && wave < 4 + DMA_ALOADERS) {
+  if (wave >= DMA_CWAVES && wave < DMA_CWAVES + DMA_ALOADERS) {
     auto arow = [&](int r) {
       int m = m0 + r;
       m = m < M ? m : M - 1;
       return A + (size_t)m * K;
     };
-    dma_load_a<QT, MT, MT>(arow, smem, s_begin, s_end, rot, wave - 4);
+    dma_load_a<QT, MT, MT>(arow, smem, s_begin, s_end, rot, wave - DMA_CWAVES);
     return;
   }
-  if (wave == 4 + DMA_ALOADERS) {
+  if (wave == DMA_CWAVES + DMA_ALOADERS) {
     dma_load_w<QT, MT, true>(W, N, K, n0, smem, s_begin, s_end, rot);
     return;
   }
-  floatx4 acc[MT][2];
+  floatx4 acc[MT][DMA_NTW];
   dma_compute<QT, MT, MT, true>(N, K, n0, smem, s_begin, s_end, rot, acc);
-  prefill_epilogue<MT, 2>(acc, R, Y, P, M, N, m0, n0, sp, splits);
+  prefill_epilogue<MT, DMA_NTW>(acc, R, Y, P, M, N, m0, n0, sp, splits);
 }
 
 // Y = sum over splits of P + R, rounded once to f16.

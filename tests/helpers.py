@@ -33,3 +33,21 @@ def case(qtype, M, N, K, cfg, idx, with_r=True):
 
 DECODE_TOL = 1e-3      # max relative error vs the int8-emulating oracle
 PREFILL_TOL = 2e-3     # relative Frobenius error vs the float64 oracle
+
+
+def extreme_scales(w, qtype, seed):
+    """Blocks w with their sub-block scales pushed to the format's limits
+    (Q6_K int8 scales in {-128, 127} on about half the sub-blocks, the rest
+    uniform over all 256 values; Q4_K / Q5_K: all six-bit scales and mins 63
+    on every other block), so that intermediate magnitudes are exercised."""
+    g = np.random.default_rng(seed)
+    bb = {"q4_k": 144, "q5_k": 176, "q6_k": 210}[qtype]
+    blk = w.reshape(-1, bb).copy()
+    if qtype == "q6_k":
+        sc = g.integers(-128, 128, size=(blk.shape[0], 16))
+        ext = g.random(size=sc.shape) < 0.5
+        sc = np.where(ext, np.where(g.random(size=sc.shape) < 0.5, -128, 127), sc)
+        blk[:, 192:208] = sc.astype(np.int8).view(np.uint8)
+    else:
+        blk[::2, 4:16] = 0xFF
+    return blk.reshape(w.shape)

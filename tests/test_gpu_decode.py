@@ -14,7 +14,7 @@ import pytest
 from gguf_quant_block_amd import synth
 from oracle import fc as ofc
 from oracle import kquant as okq
-from helpers import DECODE_TOL, PREFILL_TOL, case, maxrel, relfro
+from helpers import DECODE_TOL, PREFILL_TOL, case, extreme_scales, maxrel, relfro
 
 pytestmark = pytest.mark.gpu
 
@@ -153,6 +153,16 @@ def test_gemv_parity(gpu_lib, qtype, M, N, K):
     y = _host(_fc(w, qtype, N, K)(_dev(A), None if R is None else _dev(R))).astype(np.float64)
     ref = ofc.fc_ref_int8(A, w, qtype, R)
     assert maxrel(y, ref) <= DECODE_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M", [1, 5])
+def test_gemv_extreme_scales(gpu_lib, qtype, M):
+    N, K = 96, 2048
+    w, A, R = case(qtype, M, N, K, 65, M)
+    w = extreme_scales(w, qtype, M)
+    y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
+    assert maxrel(y, ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

@@ -15,7 +15,7 @@ import pytest
 from gguf_quant_block_amd import synth
 from oracle import fc as ofc
 from oracle import kquant as okq
-from helpers import PREFILL_TOL, relfro
+from helpers import PREFILL_TOL, extreme_scales, relfro
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +80,17 @@ def test_moe_small(gpu_lib, qtype, a_per_slot, E, N, K, T, top_k):
     ref = ofc.moe_ref(A, w, qtype, ids, a_per_slot)
     assert relfro(y, ref) <= PREFILL_TOL
     _check_experts(y, w, qtype, A, ids, a_per_slot, range(E))
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_moe_extreme_scales(gpu_lib, qtype):
+    E, N, K, T, top_k = 8, 128, 512, 60, 2
+    w, A, ids = _moe_case(qtype, E, N, K, T, top_k, False, 45, 0)
+    w = extreme_scales(w, qtype, 3)
+    _, y = _run(w, qtype, A, ids, False)
+    y = _host(y)
+    assert np.all(np.isfinite(y))
+    _check_experts(y, w, qtype, A, ids, False, range(E))
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

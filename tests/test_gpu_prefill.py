@@ -12,7 +12,7 @@ import pytest
 from gguf_quant_block_amd import synth
 from oracle import fc as ofc
 from oracle import kquant as okq
-from helpers import PREFILL_TOL, case, relfro
+from helpers import PREFILL_TOL, case, extreme_scales, relfro
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +71,19 @@ def test_prefill_in_place_residual(gpu_lib, qtype):
     Rd = _dev(R)
     _fc(w, qtype, N, K)(_dev(A), Rd, out=Rd)
     assert relfro(_host(Rd), ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M", [16, 200])
+def test_prefill_extreme_scales(gpu_lib, qtype, M):
+    # scales at the limits of each format (Q6_K: -128 and 127) keep every
+    # intermediate of the f16 decode finite
+    N, K = 160, 1024
+    w, A, R = case(qtype, M, N, K, 64, M)
+    w = extreme_scales(w, qtype, M)
+    y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
+    assert np.all(np.isfinite(y))
+    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
 
 
 def test_prefill_error_is_f16_sized(gpu_lib):
