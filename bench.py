@@ -20,6 +20,10 @@ One step = one pass of the hot path over one batch of synthetic input:
   * the widened paths, reported beside the headline: Q4_K decode (the same
     layer set, 8 layers of weights) and Q4_K prefill at M = 512, and the f32
     activation path (Q5_K decode GEMV on f32 A, R and Y, 8 layers).
+After the timed steps (outside them), the dequantise-once comparison path
+(weights decoded to f16, then a rocBLAS GEMM) is timed against the direct
+prefill path on the four prefill FCs at M = 512, 1024 and 2048, eagerly with
+HIP events on the current stream.
 Each phase is captured once as a HIP graph and replayed; HIP events on the
 replay stream time the phases.  `value` is the decode phase's weight bytes /
 decode time.  Weights and activations are resident in HBM before timing.
@@ -101,6 +105,46 @@ def cpu_baseline():
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{CPU_LAYERS} layers of the Q5_K Phi-3.5-mini layer set (qkv, o_proj, gate_up, down) at M=1, "
                       f"int8-emulating float64 oracle, {total_bytes / 1e6:.1f} MB of weights in {dt:.1f} s"}
+
+
+def scratch_comparison(prefill, dev, iters=10):
+    """TFLOPS of the direct prefill path and of the dequantise-once path (f16
+    weights + rocBLAS GEMM, the residual as beta*C) on the prefill FCs, per M."""
+    import torch
+    from gguf_quant_block_amd import synth
+
+    out = {"workload": "Q5_K and Q6_K, [8192,2048] and [2048,8192], fused residual; "
+                       "dequantise-once = the weights decoded to an f16 buffer on every call "
+                       "(not retained), then rocBLAS gemm_ex (f16 in, f32 compute)"}
+    for M in (512, 1024, 2048):
+        res = {}
+        for path in ("prefill", "scratch"):
+            flops, calls = 0, []
+            for fc, _, _, _ in prefill:
+                K, N = fc.K, fc.N
+                A = torch.from_numpy(synth.normal_f16((M, K), synth.rng(8, M, synth.TAG_A))).to(dev)
+                R = torch.from_numpy(synth.normal_f16((M, N), synth.rng(8, M, synth.TAG_R))).to(dev)
+                Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                calls.append((fc, A, R, Y))
+                flops += 2 * M * N * K
+            for fc, *_ in calls:
+                fc.set_path(path)
+            for fc, A, R, Y in calls:
+                fc(A, R, out=Y)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                for fc, A, R, Y in calls:
+                    fc(A, R, out=Y)
+            e1.record()
+            torch.cuda.synchronize()
+            s = e0.elapsed_time(e1) / 1e3 / iters
+            res[path + "_tflops"] = round(flops / s / 1e12, 1)
+            for fc, *_ in calls:
+                fc.set_path("auto")
+        out[f"m{M}"] = {"direct_tflops": res["prefill_tflops"], "dequant_once_tflops": res["scratch_tflops"]}
+    return out
 
 
 def pmc_target(dev):
@@ -457,6 +501,7 @@ def main():
         },
         "wall_s": round(wall, 3),
     }
+    line["scratch_comparison"] = scratch_comparison(prefill, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -10,6 +10,8 @@
 
 #include <new>
 
+#include <rocblas/rocblas.h>
+
 #include "fc_gguf.h"
 #include "internal.h"
 
@@ -21,8 +23,10 @@ struct fc_gguf {
   int path = FC_GGUF_PATH_AUTO;
   int device = 0;
   int num_cu = 256;
-  void* ws = nullptr;           // device workspace (split-K partials, MoE bucketing)
+  void* ws = nullptr;           // device workspace (split-K partials, MoE bucketing, the
+                                // dequantised f16 weights of the scratch path)
   size_t ws_bytes = 0;
+  rocblas_handle blas = nullptr;  // created on the first scratch-path call
   hipError_t last = hipSuccess;
 };
 
@@ -49,6 +53,7 @@ int default_path() {
   if (!p) return FC_GGUF_PATH_AUTO;
   if (!strcmp(p, "decode")) return FC_GGUF_PATH_DECODE;
   if (!strcmp(p, "prefill")) return FC_GGUF_PATH_PREFILL;
+  if (!strcmp(p, "scratch")) return FC_GGUF_PATH_SCRATCH;
   return FC_GGUF_PATH_AUTO;
 }
 
@@ -133,6 +138,32 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
   return FC_GGUF_OK;
 }
 
+// The dequantise-once comparison path: the weights decoded to f16 in the
+// handle's workspace, then one rocBLAS GEMM with the residual as beta * C.
+// Row-major Y[M,N] = A[M,K] . W16[N,K]^T is, column-major, Y^T = W16^T^T . A^T:
+// op(A) = transpose of the K x N column-major W16, op(B) = the K x M A.
+int run_scratch(fc_gguf* h, const fcg::f16* a, const fcg::f16* r, fcg::f16* y, int64_t M,
+                hipStream_t st) {
+  const int N = (int)h->N, K = (int)h->K;
+  int rc = ensure_ws(h, (size_t)N * K * sizeof(fcg::f16));
+  if (rc != FC_GGUF_OK) return rc;
+  if (!h->blas && rocblas_create_handle(&h->blas) != rocblas_status_success) {
+    h->blas = nullptr;
+    return FC_GGUF_EHIP;
+  }
+  hipError_t e = fcg::launch_dequant_f16(h->qtype, h->w, (fcg::f16*)h->ws, N, K, st);
+  if (e != hipSuccess) return hip_fail(h, e);
+  if (rocblas_set_stream(h->blas, st) != rocblas_status_success) return FC_GGUF_EHIP;
+  const float alpha = 1.f, beta = r ? 1.f : 0.f;
+  const void* c = r ? (const void*)r : (const void*)y;
+  const rocblas_status s = rocblas_gemm_ex(
+      h->blas, rocblas_operation_transpose, rocblas_operation_none, N, (rocblas_int)M, K, &alpha,
+      h->ws, rocblas_datatype_f16_r, K, a, rocblas_datatype_f16_r, K, &beta, c,
+      rocblas_datatype_f16_r, N, y, rocblas_datatype_f16_r, N, rocblas_datatype_f32_r,
+      rocblas_gemm_algo_standard, 0, 0);
+  return s == rocblas_status_success ? FC_GGUF_OK : FC_GGUF_EHIP;
+}
+
 // Validation shared by fc_gguf_run and fc_gguf_run_f32 (element size es).
 int check_run(fc_gguf_t h, const void* A, int64_t M, const void* R, const void* Y, size_t es) {
   if (!h || M < 0) return FC_GGUF_EINVAL;
@@ -194,13 +225,14 @@ int fc_gguf_destroy(fc_gguf_t h) {
   hipDeviceSynchronize();
   if (h->w) hipFree(h->w);
   if (h->ws) hipFree(h->ws);
+  if (h->blas) rocblas_destroy_handle(h->blas);
   delete h;
   return FC_GGUF_OK;
 }
 
 int fc_gguf_set_path(fc_gguf_t h, int path) {
   if (!h) return FC_GGUF_EINVAL;
-  if (path < FC_GGUF_PATH_AUTO || path > FC_GGUF_PATH_PREFILL) return FC_GGUF_EUNSUPPORTED;
+  if (path < FC_GGUF_PATH_AUTO || path > FC_GGUF_PATH_SCRATCH) return FC_GGUF_EUNSUPPORTED;
   h->path = path;
   return FC_GGUF_OK;
 }
@@ -228,6 +260,8 @@ int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, v
   if (path == FC_GGUF_PATH_DECODE) {
     e = run_decode(h, a, r, y, M, st, &rc);
     if (rc != FC_GGUF_OK) return rc;
+  } else if (path == FC_GGUF_PATH_SCRATCH) {
+    return run_scratch(h, a, r, y, M, st);
   } else {
     int mt, nt, splits;
     fcg::prefill_choose(h->qtype, (int)M, N, K, h->num_cu, &mt, &nt, &splits);

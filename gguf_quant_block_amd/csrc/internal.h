@@ -26,6 +26,9 @@ hipError_t launch_debug_quantize(const void* A, bool f32, int M, int K, int8_t* 
 hipError_t launch_debug_int_dots(int qtype, const uint8_t* W, const int8_t* qa, int M, int N, int K,
                                  int* S, hipStream_t st);
 
+// dequantise-once comparison path: tiled weights -> row-major f16 W16[N, K]
+hipError_t launch_dequant_f16(int qtype, const uint8_t* W, f16* out, int N, int K, hipStream_t st);
+
 // prefill path
 void prefill_choose(int qtype, int M, int N, int K, int num_cu, int* mt, int* nt, int* splits);
 size_t prefill_workspace_bytes(int M, int N, int splits);

@@ -36,7 +36,10 @@
  *   - `stream` is a hipStream_t (NULL = the null stream).  run calls are
  *     asynchronous and stream-ordered; kernel faults surface at the caller's
  *     next synchronisation.  A handle owns a workspace, so one handle must not
- *     be run concurrently on two streams.
+ *     be run concurrently on two streams.  The workspace grows (and moves)
+ *     when a call needs more than earlier calls did: a HIP graph that
+ *     captured earlier calls of the handle must then be captured again, so
+ *     capture after a call at the largest row count and path.
  */
 #ifndef FC_GGUF_H
 #define FC_GGUF_H
@@ -54,10 +57,14 @@ typedef struct fc_gguf* fc_gguf_t;
 #define FC_GGUF_Q5_K 5   /* 176 B per 256 values: d, dmin, 12 B scales/mins, qh[32], qs[128] */
 #define FC_GGUF_Q6_K 6   /* 210 B per 256 values: ql[128], qh[64], sc[16] (int8), d */
 
-/* Path override (fc_gguf_set_path; default from env FC_GGUF_PATH=auto|decode|prefill). */
+/* Path override (fc_gguf_set_path; default from env FC_GGUF_PATH=auto|decode|prefill|scratch). */
 #define FC_GGUF_PATH_AUTO    0   /* M < 8 -> decode, else prefill */
 #define FC_GGUF_PATH_DECODE  1   /* int8 GEMV for any M (rows taken in chunks of at most 7) */
 #define FC_GGUF_PATH_PREFILL 2   /* f16 matrix-core path for any M >= 1 */
+#define FC_GGUF_PATH_SCRATCH 3   /* comparison only: weights dequantised to an f16 buffer in the
+                                    handle's workspace (N*K*2 bytes), then a rocBLAS GEMM with the
+                                    residual as beta*C (the page's path for devices without the
+                                    decode-once kernel; never chosen by AUTO) */
 
 /* Error codes. */
 #define FC_GGUF_OK            0

@@ -86,6 +86,28 @@ def test_prefill_extreme_scales(gpu_lib, qtype, M):
     assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
 
 
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M,N,K,with_r", [(1, 96, 512, True), (37, 200, 768, False), (512, 384, 2048, True)])
+def test_scratch_path_parity(gpu_lib, qtype, M, N, K, with_r):
+    # the dequantise-once comparison path (f16 weights + library GEMM)
+    w, A, R = case(qtype, M, N, K, 66, M + N, with_r=with_r)
+    fcg = _fc(w, qtype, N, K)
+    fcg.set_path("scratch")
+    y = _host(fcg(_dev(A), None if R is None else _dev(R)))
+    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+
+
+def test_scratch_path_in_place_and_extreme_scales(gpu_lib):
+    M, N, K = 24, 128, 1024
+    w, A, R = case("q6_k", M, N, K, 67, 0)
+    w = extreme_scales(w, "q6_k", 9)
+    fcg = _fc(w, "q6_k", N, K)
+    fcg.set_path("scratch")
+    Rd = _dev(R)
+    fcg(_dev(A), Rd, out=Rd)
+    assert relfro(_host(Rd), ofc.fc_gguf_ref(A, w, "q6_k", R)) <= PREFILL_TOL
+
+
 def test_prefill_error_is_f16_sized(gpu_lib):
     # the error is the expected f16-rounding size, far inside the tolerance
     M, N, K = 256, 256, 2048
