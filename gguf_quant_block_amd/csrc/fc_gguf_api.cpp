@@ -89,8 +89,9 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
   const size_t nblk = (size_t)N * (size_t)(K / 256);
   if (nblk > ((size_t)1 << 31) / 256) return FC_GGUF_ERANGE;
   const size_t src_bytes = nblk * (size_t)bb;                        // one canonical matrix
-  // one device matrix (tiled for single-matrix handles, canonical for grouped ones)
-  const size_t expert_bytes = fcg::layout_bytes(qtype, grouped == 0, (int)N, (int)K);
+  // one device matrix in the tiled layout (grouped handles: one per expert)
+  const bool tiled = grouped == 0 || fcg::GROUPED_TILED;
+  const size_t expert_bytes = fcg::layout_bytes(qtype, tiled, (int)N, (int)K);
 
   fc_gguf* h = new (std::nothrow) fc_gguf();
   if (!h) return FC_GGUF_ENOMEM;
@@ -124,7 +125,7 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
     src = staging;
   }
   for (int64_t x = 0; e == hipSuccess && x < E; ++x)
-    e = fcg::launch_weight_layout(qtype, grouped == 0, src + x * src_bytes,
+    e = fcg::launch_weight_layout(qtype, tiled, src + x * src_bytes,
                                   h->w + x * expert_bytes, (int)N, (int)K, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (staging) hipFree(staging);

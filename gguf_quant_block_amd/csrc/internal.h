@@ -36,6 +36,7 @@ hipError_t launch_prefill(int qtype, const uint8_t* W, const f16* A, const f16* 
                           int M, int N, int K, int mt, int nt, int splits, hipStream_t st);
 
 // grouped (MoE) path
+constexpr bool GROUPED_TILED = true;   // grouped handles use the tiled layout, per expert
 constexpr int MOE_MAX_E = 4096;   // experts per grouped handle (bucketing counts live in LDS)
 size_t moe_workspace_bytes(int E, int T, int top_k);
 hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, int N, int K,

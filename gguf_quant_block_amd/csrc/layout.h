@@ -4,7 +4,7 @@
 // holds row n's K/256 blocks in order).  Every block is cut into 16-byte
 // pieces.
 //
-// Tiled layout (single-matrix handles, read by the decode and prefill paths):
+// Tiled layout (every handle; the decode, prefill and grouped paths read it):
 // the block grid is cut into tiles of 16 rows x 4 blocks (64 blocks; the row
 // count is padded to a multiple of 16 and the blocks per row to a multiple
 // of 4 with zero bytes).  Tiles are numbered row-tile major,
@@ -21,9 +21,10 @@
 //         Transformation), each over the padded block count: QL P = 8,
 //         QH P = 4, SC P = 1; D holds 2 bytes per block at t * 128 + l * 2.
 //
-// Canonical layout (grouped handles, whose expert tiles read whole rows):
-// blocks b = n * (K/256) + kb in order, padded to a multiple of 64 blocks;
-// Q4_K / Q5_K blocks as in the file, Q6_K as the four planes in block order.
+// Canonical layout (an option of the layout transform and of the
+// register-staged tile; no handle stores it): blocks
+// b = n * (K/256) + kb in order, padded to a multiple of 64 blocks; Q4_K /
+// Q5_K blocks as in the file, Q6_K as the four planes in block order.
 #pragma once
 
 #include <stddef.h>

@@ -1,8 +1,7 @@
 // Weight layout transform, run once when a handle is created: canonical GGUF
 // blocks (array of structures, row-major) -> the tiled device layout of
-// layout.h (single-matrix handles) or the canonical device layout (Q4_K /
-// Q5_K blocks in order, Q6_K row-major planes; grouped handles, whose expert
-// tiles read rows).
+// layout.h (every handle; grouped handles per expert) or the canonical device
+// layout (Q4_K / Q5_K blocks in order, Q6_K row-major planes).
 //
 // OpenVINO PR #39119, section Transformation: Q6_K blocks are regrouped into
 // the planes QL | QH | SC | D with unchanged size and contents; here every

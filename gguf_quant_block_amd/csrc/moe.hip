@@ -205,10 +205,10 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
   const int S = K / (KSTAGE * MOE_SH);
   const int rot = (ti + nt) % S;           // spread concurrent loads over K
   // (active halves rounded up to 1, 2, 4 or MT)
-  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, false, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act == 2 || MT == 2) tile_mainloop<QT, MT, NT, (MT < 2 ? MT : 2), false, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act <= 4 || MT == 4) tile_mainloop<QT, MT, NT, (MT < 4 ? MT : 4), false, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
-  else tile_mainloop<QT, MT, NT, MT, false, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, GROUPED_TILED, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act == 2 || MT == 2) tile_mainloop<QT, MT, NT, (MT < 2 ? MT : 2), GROUPED_TILED, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act <= 4 || MT == 4) tile_mainloop<QT, MT, NT, (MT < 4 ? MT : 4), GROUPED_TILED, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else tile_mainloop<QT, MT, NT, MT, GROUPED_TILED, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
 
 #pragma unroll
   for (int i = 0; i < MT; ++i) {

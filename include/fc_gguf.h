@@ -165,13 +165,12 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
  *   super-block of row n, cut into 16-byte pieces.  Q4_K / Q5_K: one plane
  *   of P = 9 / 11 pieces per block.  Q6_K: planes QL (P = 8) | QH (P = 4) |
  *   SC (P = 1) | D (2 bytes per block), each over the same padded block count.
- *   Single-matrix handles are tiled: rows padded with zero bytes to a multiple
- *   of 16 and blocks per row to a multiple of 4 (KBp); tile
- *   t = (n/16)*(KBp/4) + kb/4 holds 16 rows x 4 blocks, piece p of block
- *   (n, kb) at (t*P + p)*1024 + l*16 within its plane, l = (kb%4)*16 + n%16;
- *   D at t*128 + l*2.  Grouped handles keep the blocks in order
- *   b = n*(K/256) + kb, padded with zero bytes to a multiple of 64 blocks:
- *   piece p of block b at b*16*P + 16*p; D at 2*b.
+ *   Every matrix is tiled: rows padded with zero bytes to a multiple of 16
+ *   and blocks per row to a multiple of 4 (KBp); tile t = (n/16)*(KBp/4) +
+ *   kb/4 holds 16 rows x 4 blocks, piece p of block (n, kb) at
+ *   (t*P + p)*1024 + l*16 within its plane, l = (kb%4)*16 + n%16; D at
+ *   t*128 + l*2.  Grouped handles hold their experts' matrices one after
+ *   another.
  */
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s,
                            int32_t* T, void* stream);

@@ -51,3 +51,42 @@ def extreme_scales(w, qtype, seed):
     else:
         blk[::2, 4:16] = 0xFF
     return blk.reshape(w.shape)
+
+
+def tile_bytes(plane, N, KB, P, fill=0):
+    """Canonical plane bytes [N*KB, 16*P] (block (n, kb) at row n*KB + kb) ->
+    the tiled device order: tiles of 16 rows x 4 blocks (rows padded to 16,
+    blocks per row to 4), tile t = (n/16)*(KBp/4) + kb/4 stored piece-major,
+    the blocks of a piece in the order (kb % 4)*16 + n % 16."""
+    Np, KBp = -(-N // 16) * 16, -(-KB // 4) * 4
+    x = np.full((Np, KBp, P, 16), fill, dtype=plane.dtype)
+    x[:N, :KB] = plane.reshape(N, KB, P, 16)
+    return x.reshape(Np // 16, 16, KBp // 4, 4, P, 16).transpose(0, 2, 4, 3, 1, 5).reshape(-1)
+
+
+def _tile_d(d, N, KB):
+    """Q6_K d bytes [N*KB, 2] -> tiled: 128 bytes per tile, slot (kb % 4)*16 + n % 16."""
+    Np, KBp = -(-N // 16) * 16, -(-KB // 4) * 4
+    x = np.zeros((Np, KBp, 2), dtype=d.dtype)
+    x[:N, :KB] = d.reshape(N, KB, 2)
+    return x.reshape(Np // 16, 16, KBp // 4, 4, 2).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+def expected_device_bytes(w, qtype, N, K):
+    """The library's device copy of canonical blocks w[N, K/256*B] in the tiled
+    layout: Q4_K / Q5_K blocks as one plane of 9 / 11 pieces; Q6_K planes
+    QL | QH | SC | D (the oracle's regroup), each tiled the same way."""
+    KB = K // 256
+    if qtype == "q4_k":
+        return tile_bytes(w.reshape(-1, 144), N, KB, 9)
+    if qtype == "q5_k":
+        return tile_bytes(w.reshape(-1, 176), N, KB, 11)
+    from oracle import kquant as okq
+    planes = okq.q6k_regroup(w)
+    nblk = N * KB
+    ql = planes[:128 * nblk].reshape(nblk, 128)
+    qh = planes[128 * nblk:192 * nblk].reshape(nblk, 64)
+    sc = planes[192 * nblk:208 * nblk].reshape(nblk, 16)
+    d = planes[208 * nblk:].reshape(nblk, 2)
+    return np.concatenate([tile_bytes(ql, N, KB, 8), tile_bytes(qh, N, KB, 4), tile_bytes(sc, N, KB, 1),
+                           _tile_d(d, N, KB)])

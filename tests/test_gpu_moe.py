@@ -15,7 +15,7 @@ import pytest
 from gguf_quant_block_amd import synth
 from oracle import fc as ofc
 from oracle import kquant as okq
-from helpers import PREFILL_TOL, extreme_scales, relfro
+from helpers import PREFILL_TOL, expected_device_bytes, extreme_scales, relfro
 
 pytestmark = pytest.mark.gpu
 
@@ -124,29 +124,23 @@ def test_moe_invalid_ids_give_zero_rows(gpu_lib, qtype):
 
 @pytest.mark.parametrize("qtype", QTYPES)
 def test_grouped_device_layout_bytes(gpu_lib, qtype):
-    # grouped handles keep every plane in block order, per expert, padded to
-    # a multiple of 64 blocks
+    # grouped handles tile every expert's matrix like a single-matrix handle
+    # (16 rows x 4 blocks, rows and blocks per row padded), experts one after
+    # another
     from gguf_quant_block_amd.binding import FcGguf
-    E, N, K = 3, 5, 512
-    bb = {"q4_k": 144, "q5_k": 176, "q6_k": 210}[qtype]
+    E, N, K = 3, 5, 768
     w = synth.blocks(qtype, E * N, K, synth.rng(44, 0, 0)).reshape(E, N, -1)
     got = _host(FcGguf(N, K, qtype, w, experts=E).debug_weights())
-    nblk = N * K // 256
-    per = 64 * bb
+    exp = [expected_device_bytes(w[e], qtype, N, K) for e in range(E)]
+    per = exp[0].size
     assert got.size == E * per
     for e in range(E):
-        blocks = w[e].reshape(nblk, bb)
-        pad = np.zeros((64, bb), dtype=np.uint8)
-        pad[:nblk] = blocks
-        if qtype != "q6_k":
-            exp = pad.reshape(-1)
-        else:
-            exp = np.concatenate([pad[:, :128].reshape(-1), pad[:, 128:192].reshape(-1),
-                                  pad[:, 192:208].reshape(-1), pad[:, 208:].reshape(-1)])
-            # the plane split agrees with the oracle's regroup on the real blocks
-            planes = okq.q6k_regroup(w[e])
-            assert np.array_equal(exp[:128 * nblk], planes[:128 * nblk])
-        assert np.array_equal(got[e * per:(e + 1) * per], exp)
+        assert np.array_equal(got[e * per:(e + 1) * per], exp[e])
+    if qtype == "q6_k":
+        # the plane split agrees with the oracle's regroup
+        planes = okq.q6k_regroup(w[0])
+        assert np.array_equal(np.sort(exp[0][:16 * 4 * 128]), np.sort(np.concatenate(
+            [planes[:128 * N * 3], np.zeros(128 * (64 - N * 3), np.uint8)])))
 
 
 def test_moe_empty_and_repeat(gpu_lib):
