@@ -39,13 +39,10 @@ namespace fcg {
 #ifndef FCG_DMA_ALOADERS
 #define FCG_DMA_ALOADERS 1
 #endif
-#ifndef FCG_DMA_CWAVES
-#define FCG_DMA_CWAVES 4
-#endif
 constexpr int DMA_SLOTS = FCG_DMA_SLOTS;          // LDS ring depth (stages)
 constexpr int DMA_ALOADERS = FCG_DMA_ALOADERS;    // waves loading the activation tile
-constexpr int DMA_CWAVES = FCG_DMA_CWAVES;        // compute waves (4 or 8)
-constexpr int DMA_NTW = 8 / DMA_CWAVES;           // 16-row weight sub-tiles per compute wave
+constexpr int DMA_CWAVES = 4;                    // compute waves
+constexpr int DMA_NTW = 2;                        // 16-row weight sub-tiles per compute wave
 constexpr int DMA_THREADS = 64 * (DMA_CWAVES + DMA_ALOADERS + 1);
 
 template <int QT, int MT>
@@ -75,6 +72,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A compute wave's end-of-stage barrier: its LDS reads of the slot have
+// returned (lgkmcnt(0)) before it arrives, since a loader may refill the slot
+// as soon as the barrier opens.  (s_waitcnt immediate, gfx9 encoding: vmcnt
+// 63, expcnt 7, lgkmcnt 0.)
+__device__ __forceinline__ void compute_stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -183,23 +191,70 @@ __device__ __forceinline__ void dma_load_w(const uint8_t* W, int N, int K, int n
   }
 }
 
+// The half-block decoder of a weight type.
+template <int QT> struct HalfDec { using type = Q6Half; };
+template <> struct HalfDec<QT_Q5K> { using type = Q45Half<true>; };
+template <> struct HalfDec<QT_Q4K> { using type = Q45Half<false>; };
+
+// Per-half setup of the lane's decoders for stage s, whose weight pieces sit
+// at Ws: the pieces of rows nloc[j] that the lane's k-quarter kq reads.  IL:
+// the weights are in the tiled layout (selects which half of a Q6_K d word
+// is the row's).
+template <int QT, int MT, bool IL>
+__device__ __forceinline__ void dma_dec_init(typename HalfDec<QT>::type (&h)[DMA_NTW],
+                                             const uint8_t* Ws, const int (&nloc)[DMA_NTW],
+                                             const int (&rn)[DMA_NTW], int s, int KB, int kq) {
+  using C = DmaCfg<QT, MT>;
+  const int hb = s & 1, kb = s >> 1, sub = 8 * (kq & 1), pq = kq >> 1;
+#pragma unroll
+  for (int j = 0; j < DMA_NTW; ++j) {
+    auto pc = [&](int q) { return Ws + (q * 128 + nloc[j]) * 16; };
+    if constexpr (QT == QT_Q5K) {
+      h[j].init(*(const uint4*)pc(0), *(const uint2*)(pc(3 + pq) + sub),
+                *(const uint2*)(pc(5 + pq) + sub), *(const uint2*)(pc(1 + pq) + sub), hb);
+    } else if constexpr (QT == QT_Q4K) {
+      h[j].init(*(const uint4*)pc(0), *(const uint2*)(pc(1 + pq) + sub),
+                *(const uint2*)(pc(3 + pq) + sub), uint2{0u, 0u}, hb);
+    } else {
+      const uint32_t dw = *(const uint32_t*)(Ws + C::WP * 128 * 16 + 4 * nloc[j]);
+      // the row's half of the word: tiled, the blocks of rows n and n ^ 1
+      // share it; canonical, the blocks b and b ^ 1
+      const int half = IL ? (rn[j] & 1) : (int)(((size_t)rn[j] * KB + kb) & 1);
+      h[j].init(*(const uint2*)(pc(pq) + sub), *(const uint2*)(pc(2 + pq) + sub),
+                *(const uint2*)(pc(4 + pq) + sub), *(const uint2*)(pc(6) + 8 * hb),
+                dw >> (16 * half), kq);
+    }
+  }
+}
+
 // Compute waves 0-3: acc[i][j] += C[n][m] of the 16x16 sub-tiles (half
-// i < MTA, weight sub-tile j of the wave's 32 rows) over the stages.  IL:
-// the weights are in the tiled layout (selects which half of a d word is
-// the row's).
+// i < MTA, weight sub-tile j of the wave's 32 rows) over the stages.  Wave w
+// owns weight rows 32w .. 32w + 31.
+//
+// Software pipeline, one k-step deep: while the matrix cores run the MFMAs
+// of k-step g, the wave reads the activation operands of its next k-step and
+// decodes that k-step's weight fragments (the VALU work overlaps the matrix
+// cores).  The stage barrier sits before the last k-step of the stage, once
+// the wave has read everything it needs from the slot; right after it,
+// the next stage's raw pieces and first operands are read and its decoders
+// set up, still under those MFMAs.  (After the last stage the same reads hit
+// a slot whose contents are never used.)  Each k-step is one scheduling
+// region: its LDS reads first, then each MFMA followed by a few VALU
+// instructions.
 template <int QT, int MT, int MTA, bool IL>
 __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t* smem, int s_begin,
                                             int s_end, int rot, floatx4 (&acc)[MT][DMA_NTW]) {
-  constexpr int NTW = DMA_NTW;
+  constexpr int NTW = DMA_NTW, KS = 4;        // k-steps per stage
   using C = DmaCfg<QT, MT>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kq = lane >> 4, sub = 8 * (kq & 1), pq = kq >> 1;
+  using Dec = typename HalfDec<QT>::type;
+  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6;
+  const int kq = lane >> 4;
   const int nst = s_end - s_begin;
   const int KB = K >> 8;
   int nloc[NTW], rn[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
-    nloc[j] = wave * 16 * NTW + 16 * j + (lane & 15);
+    nloc[j] = wn * 16 * NTW + 16 * j + (lane & 15);
     const int n = n0 + nloc[j];
     rn[j] = n < N ? n : N - 1;                      // the row the loader fetched
   }
@@ -207,69 +262,63 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
   for (int i = 0; i < MTA; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (nst <= 0) {
+    stage_barrier();
+    return;
+  }
+  // activation operands of k-step g of the stage in slot As
+  auto lda = [&](const uint8_t* As, int g, half8v* af) {
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+      const int r = 16 * i + (lane & 15);
+      af[i] = *(const half8v*)(As + (r * 16 + ((4 * g + kq) ^ (r & 15))) * 16);
+    }
+  };
 
   stage_barrier();                                  // stage 0 has landed
+  Dec h[NTW];
+  half8v wc[NTW], afc[MTA];
+  lda(smem, 0, afc);
+  dma_dec_init<QT, MT, IL>(h, smem + C::A_BYTES, nloc, rn, dma_stage(0, s_begin, nst, rot), KB, kq);
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) wc[j] = h[j].frag(0);
+
   for (int t = 0; t < nst; ++t) {
-    const int s = dma_stage(t, s_begin, nst, rot);
-    const int hb = s & 1, kb = s >> 1;
     const uint8_t* As = smem + (t % DMA_SLOTS) * C::SLOT;
-    const uint8_t* Ws = As + C::A_BYTES;
-    // activation operands of k-step g, read one k-step ahead of their MFMAs
-    // (the first k-step's before the weight decode, to overlap its latency)
-    auto lda = [&](int g, half8v* af) {
 #pragma unroll
-      for (int i = 0; i < MTA; ++i) {
-        const int r = 16 * i + (lane & 15);
-        af[i] = *(const half8v*)(As + (r * 16 + ((4 * g + kq) ^ (r & 15))) * 16);
-      }
-    };
-    half8v afc[MTA], afn[MTA];
-    lda(0, afc);
-    asm volatile("" ::: "memory");                  // keep the reads ahead of their use
-    half8v wf[NTW][4];
+    for (int gg = 0; gg < KS; ++gg) {
+      half8v wnext[NTW], afn[MTA];
+      if (gg + 1 < KS) {
+        lda(As, gg + 1, afn);
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      auto pc = [&](int q) { return Ws + (q * 128 + nloc[j]) * 16; };
-      if constexpr (QT == QT_Q5K) {
-        RawQ5 r;
-        r.hdr = *(const uint4*)pc(0);
-        r.qh = *(const uint2*)(pc(1 + pq) + sub);
-        r.qsA = *(const uint2*)(pc(3 + pq) + sub);
-        r.qsB = *(const uint2*)(pc(5 + pq) + sub);
-        decode_q5k_half(r, hb, wf[j]);
-      } else if constexpr (QT == QT_Q4K) {
-        RawQ4 r;
-        r.hdr = *(const uint4*)pc(0);
-        r.qsA = *(const uint2*)(pc(1 + pq) + sub);
-        r.qsB = *(const uint2*)(pc(3 + pq) + sub);
-        decode_q4k_half(r, hb, wf[j]);
+        for (int j = 0; j < NTW; ++j) wnext[j] = h[j].frag(gg + 1);
       } else {
-        RawQ6 r;
-        r.qlA = *(const uint2*)(pc(pq) + sub);
-        r.qlB = *(const uint2*)(pc(2 + pq) + sub);
-        r.qh = *(const uint2*)(pc(4 + pq) + sub);
-        r.sc = *(const uint2*)(pc(6) + 8 * hb);
-        const uint32_t dw = *(const uint32_t*)(Ws + C::WP * 128 * 16 + 4 * nloc[j]);
-        // the row's half of the word: tiled, the blocks of rows n and n ^ 1
-        // share it; canonical, the blocks b and b ^ 1
-        const int half = IL ? (rn[j] & 1) : (int)(((size_t)rn[j] * KB + kb) & 1);
-        r.d = dw >> (16 * half);
-        decode_q6k_half(r, kq, wf[j]);
-      }
-    }
+        compute_stage_barrier();                    // slot t read; stage t + 1 landed
+        const uint8_t* An = smem + ((t + 1) % DMA_SLOTS) * C::SLOT;
+        lda(An, 0, afn);
+        dma_dec_init<QT, MT, IL>(h, An + C::A_BYTES, nloc, rn,
+                                 dma_stage(t + 1, s_begin, nst, rot), KB, kq);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (g + 1 < 4) lda(g + 1, afn);
-      asm volatile("" ::: "memory");
+        for (int j = 0; j < NTW; ++j) wnext[j] = h[j].frag(0);
+      }
 #pragma unroll
       for (int i = 0; i < MTA; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j][g], afc[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc[j], afc[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) wc[j] = wnext[j];
 #pragma unroll
       for (int i = 0; i < MTA; ++i) afc[i] = afn[i];
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+      for (int k = 0; k < MTA * NTW; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (gg + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    stage_barrier();                                // done reading this slot; next one landed
   }
 }
 

@@ -102,14 +102,13 @@ struct Q45Half {
 
   __device__ __forceinline__ void init(uint4 hdr, uint2 qsA, uint2 qsB, uint2 qh, int hb) {
     const uint32_t w0 = hdr.y, w1 = hdr.z, w2 = hdr.w;
-    uint32_t scb, mb;   // bytes g = 0..3: scale / min of sub-block 4hb + g
-    if (hb == 0) {
-      scb = w0 & 0x3F3F3F3Fu;
-      mb = w1 & 0x3F3F3F3Fu;
-    } else {
-      scb = (w2 & 0x0F0F0F0Fu) | ((w0 >> 2) & 0x30303030u);
-      mb = ((w2 >> 4) & 0x0F0F0F0Fu) | ((w1 >> 2) & 0x30303030u);
-    }
+    // bytes g = 0..3: scale / min of sub-block 4hb + g (selected without a
+    // branch, so that the setup schedules freely among the matrix-core work)
+    const uint32_t hi = 0u - (uint32_t)hb;
+    const uint32_t scb = (w0 & 0x3F3F3F3Fu & ~hi) |
+                         (((w2 & 0x0F0F0F0Fu) | ((w0 >> 2) & 0x30303030u)) & hi);
+    const uint32_t mb = (w1 & 0x3F3F3F3Fu & ~hi) |
+                        ((((w2 >> 4) & 0x0F0F0F0Fu) | ((w1 >> 2) & 0x30303030u)) & hi);
     const half2v k1024 = splat((f16)1024.f), nk = splat((f16)-1024.f);
     sc01 = magic_pair(scb, 0x04010400u) - k1024;
     sc23 = magic_pair(scb, 0x04030402u) - k1024;

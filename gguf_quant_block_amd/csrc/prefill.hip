@@ -21,14 +21,15 @@
 
 namespace fcg {
 
-// Epilogue of a tile: lane holds C[n = 4*(lane>>4) + r][m = lane & 15] of each
-// 16x16 sub-tile; + R and one f16 rounding, or f32 split-K partials.
+// Epilogue of a wave's sub-tiles: lane holds C[n = 4*(lane>>4) + r][m = lane & 15]
+// of each 16x16 sub-tile (i, j), whose first row is m0 + 16 i and first
+// column n0 + 16 j; + R and one f16 rounding, or f32 split-K partials.
 template <int MT, int NT>
 __device__ __forceinline__ void prefill_epilogue(const floatx4 (&acc)[MT][NT],
                                                  const f16* __restrict__ R, f16* __restrict__ Y,
                                                  float* __restrict__ P, int M, int N, int m0,
                                                  int n0, int sp, int splits) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int kq = lane >> 4;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
@@ -36,7 +37,7 @@ __device__ __forceinline__ void prefill_epilogue(const floatx4 (&acc)[MT][NT],
     if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int n = n0 + wave * 16 * NT + 16 * j + 4 * kq;
+      const int n = n0 + 16 * j + 4 * kq;
       if (n >= N) continue;
       const floatx4 v = acc[i][j];
       if (splits > 1) {
@@ -106,7 +107,7 @@ prefill_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   const int rot = nst > 0 ? (nt + mt) % nst : 0;
   tile_mainloop<QT, MT, NT, MT, true, 1>(W, N, K, n0, s_begin, s_end, rot, rows, As, acc);
 
-  prefill_epilogue<MT, NT>(acc, R, Y, P, M, N, m0, n0, sp, splits);
+  prefill_epilogue<MT, NT>(acc, R, Y, P, M, N, m0, n0 + wave * 16 * NT, sp, splits);
 }
 
 // The same tile with loader waves and an LDS ring (mfma_dma.h).
@@ -144,7 +145,7 @@ prefill_dma_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   }
   floatx4 acc[MT][DMA_NTW];
   dma_compute<QT, MT, MT, true>(N, K, n0, smem, s_begin, s_end, rot, acc);
-  prefill_epilogue<MT, DMA_NTW>(acc, R, Y, P, M, N, m0, n0, sp, splits);
+  prefill_epilogue<MT, DMA_NTW>(acc, R, Y, P, M, N, m0, n0 + wave * 16 * DMA_NTW, sp, splits);
 }
 
 // Y = sum over splits of P + R, rounded once to f16.
