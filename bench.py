@@ -55,7 +55,7 @@ CPU_LAYERS = 6               # oracle sample: about 10-30 s on one core
 
 def gemv_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemv.hip", "common.h"):
+    for f in ("gemv.hip", "quant.h", "common.h", "layout.h"):
         with open(os.path.join(ROOT, "gguf_quant_block_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libfcgguf.so")
 Q4_K, Q5_K, Q6_K = 4, 5, 6
 QTYPES = {"q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
-PATHS = {"auto": 0, "decode": 1, "prefill": 2, "scratch": 3}
+PATHS = {"auto": 0, "decode": 1, "prefill": 2, "scratch": 3, "int8": 4}
 
 _lib = None
 _lock = threading.Lock()

@@ -29,7 +29,8 @@ CFLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["fc_gguf_api.cpp", "layout.hip", "gemv.hip", "prefill.hip", "moe.hip", "dequant.hip"]
+SOURCES = ["fc_gguf_api.cpp", "layout.hip", "gemv.hip", "prefill.hip", "prefill_i8.hip", "moe.hip",
+           "dequant.hip"]
 
 
 def _compile(src: str) -> str:

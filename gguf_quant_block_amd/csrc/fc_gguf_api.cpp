@@ -24,7 +24,8 @@ struct fc_gguf {
   int device = 0;
   int num_cu = 256;
   void* ws = nullptr;           // device workspace (split-K partials, MoE bucketing, the
-                                // dequantised f16 weights of the scratch path)
+                                // dequantised f16 weights of the scratch path, the int8
+                                // path's quantised activations)
   size_t ws_bytes = 0;
   rocblas_handle blas = nullptr;  // created on the first scratch-path call
   hipError_t last = hipSuccess;
@@ -54,6 +55,7 @@ int default_path() {
   if (!strcmp(p, "decode")) return FC_GGUF_PATH_DECODE;
   if (!strcmp(p, "prefill")) return FC_GGUF_PATH_PREFILL;
   if (!strcmp(p, "scratch")) return FC_GGUF_PATH_SCRATCH;
+  if (!strcmp(p, "int8")) return FC_GGUF_PATH_INT8;
   return FC_GGUF_PATH_AUTO;
 }
 
@@ -233,7 +235,7 @@ int fc_gguf_destroy(fc_gguf_t h) {
 
 int fc_gguf_set_path(fc_gguf_t h, int path) {
   if (!h) return FC_GGUF_EINVAL;
-  if (path < FC_GGUF_PATH_AUTO || path > FC_GGUF_PATH_SCRATCH) return FC_GGUF_EUNSUPPORTED;
+  if (path < FC_GGUF_PATH_AUTO || path > FC_GGUF_PATH_INT8) return FC_GGUF_EUNSUPPORTED;
   h->path = path;
   return FC_GGUF_OK;
 }
@@ -263,6 +265,12 @@ int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, v
     if (rc != FC_GGUF_OK) return rc;
   } else if (path == FC_GGUF_PATH_SCRATCH) {
     return run_scratch(h, a, r, y, M, st);
+  } else if (path == FC_GGUF_PATH_INT8) {
+    int mt, nt, splits;
+    fcg::prefill_choose(h->qtype, (int)M, N, K, h->num_cu, &mt, &nt, &splits);
+    rc = ensure_ws(h, fcg::prefill_i8_workspace_bytes((int)M, N, K, splits));
+    if (rc != FC_GGUF_OK) return rc;
+    e = fcg::launch_prefill_i8(h->qtype, h->w, a, r, y, h->ws, (int)M, N, K, mt, splits, st);
   } else {
     int mt, nt, splits;
     fcg::prefill_choose(h->qtype, (int)M, N, K, h->num_cu, &mt, &nt, &splits);

@@ -31,12 +31,12 @@
 #include "common.h"
 #include "internal.h"
 #include "layout.h"
+#include "quant.h"
 
 namespace fcg {
 
 constexpr int GEMV_MAX_WAVES = 8;
 constexpr int GEMV_MAX_THREADS = 64 * GEMV_MAX_WAVES;
-constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23: x + magic rounds x to an integer, ties to even
 
 // ------------------------------------------------------ LDS layout ----
 
@@ -87,89 +87,7 @@ __device__ __forceinline__ int qa_chunk(int m, int KBp, int kb, int t) {
 }
 
 // ------------------------------------------------ activation quantisation --
-// Per-32 int8 quantisation (OpenVINO PR #39119, sections Transformation and
-// Implementation: dynamic quantisation in groups of 32 for the int8 GEMV;
-// f16 activations, and f32 activations at any row count, take this path).
-// Symmetric: s = amax/127, inv = 127/amax (IEEE-correct f32 divisions),
-// code = round-half-even(fl32(a * inv)); |fl32(a * inv)| <= 127.5 so no clamp
-// is needed.  An all-zero group, or an f32 group so small that 127/amax
-// overflows (amax < 127/FLT_MAX), gives s = 0 and codes 0.
-//
-// One lane quantises one 32-value group (64 bytes of f16 or 128 of f32):
-//   q[0 .. 8):   packed int8 codes of the group's values
-//   tsum:        sum of the group's 32 codes
-//   thalf[0,1]:  sums of the group's first and second 16 codes
-// round-half-even(fl32(a * inv)) in the low byte of the result.  The product
-// is rounded to f32 first and only then rounded to an integer (adding 1.5*2^23
-// rounds to the nearest integer, ties to even, for |x| < 2^22); the empty asm
-// keeps the compiler from fusing the two into one fma, which would round the
-// exact product once and differ on ties.
-__device__ __forceinline__ uint32_t rne_code(float a, float inv) {
-  float p = a * inv;
-  asm volatile("" : "+v"(p));
-  return __builtin_bit_cast(uint32_t, p + RNE_MAGIC);
-}
-
-// 16-byte loads per 32-value group of activations of type AT
-template <class AT>
-constexpr int act_u4() { return (int)sizeof(AT) * 2; }
-
-template <class AT>
-__device__ __forceinline__ void quant_group(const uint4* raw, uint32_t* q, float& s, int& tsum,
-                                            int* thalf) {
-  constexpr int U4 = act_u4<AT>();
-  uint32_t w[4 * U4];
-#pragma unroll
-  for (int i = 0; i < U4; ++i) {
-    w[4 * i] = raw[i].x; w[4 * i + 1] = raw[i].y; w[4 * i + 2] = raw[i].z; w[4 * i + 3] = raw[i].w;
-  }
-  auto value = [&](int i) -> float {
-    if constexpr (std::is_same<AT, f16>::value) return h2f(w[i >> 1] >> (16 * (i & 1)));
-    else return __builtin_bit_cast(float, w[i]);
-  };
-  float amax;
-  if constexpr (std::is_same<AT, f16>::value) {
-    half2v m2 = {(f16)0.f, (f16)0.f};
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(half2v, w[j] & 0x7FFF7FFFu));
-    amax = fmaxf((float)m2[0], (float)m2[1]);
-  } else {
-    amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, __builtin_bit_cast(float, w[j] & 0x7FFFFFFFu));
-  }
-  float inv = 0.f;
-  s = 0.f;
-  if (amax > 0.f) {
-    inv = __fdiv_rn(127.0f, amax);
-    if (inv <= 3.402823466e38f) s = __fdiv_rn(amax, 127.0f);   // inv finite
-    else inv = 0.f;
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    // four values -> four rounded floats -> the low byte of each is the code
-    const uint32_t r0 = rne_code(value(4 * c), inv);
-    const uint32_t r1 = rne_code(value(4 * c + 1), inv);
-    const uint32_t r2 = rne_code(value(4 * c + 2), inv);
-    const uint32_t r3 = rne_code(value(4 * c + 3), inv);
-    const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x0c0c0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(r3, r2, 0x0c0c0400u);
-    q[c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-  }
-  // code sums: 16-value halves and the group total
-  int a = 0, b = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a = dot4((int)q[i], 0x01010101, a);
-#pragma unroll
-  for (int i = 4; i < 8; ++i) b = dot4((int)q[i], 0x01010101, b);
-  thalf[0] = a;
-  thalf[1] = b;
-  tsum = a + b;
-}
-
-// Quantisation of MR rows of A into the LDS layout by the whole workgroup of
-// nt threads: thread tid takes the 32-value groups (tasks) tid, tid + nt, ...
+// Per-32 int8 quantisatioakes the 32-value groups (tasks) tid, tid + nt, ...
 // The activation loads of the first qpre<AT>() rounds are issued before the
 // weight loads, so the quantisation waits only for them (loads complete in
 // order) while the weights are still in flight.

@@ -34,6 +34,15 @@ void prefill_choose(int qtype, int M, int N, int K, int num_cu, int* mt, int* nt
 size_t prefill_workspace_bytes(int M, int N, int splits);
 hipError_t launch_prefill(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, float* P,
                           int M, int N, int K, int mt, int nt, int splits, hipStream_t st);
+// Y = sum over splits of P[split][M*N] + R, one f16 rounding
+hipError_t launch_splitk_reduce(const float* P, const f16* R, f16* Y, long long MN, int splits,
+                                hipStream_t st);
+
+// int8 matrix-core prefill variant (tile and splits from prefill_choose); ws
+// holds prefill_i8_workspace_bytes(M, N, K, splits) bytes
+size_t prefill_i8_workspace_bytes(int M, int N, int K, int splits);
+hipError_t launch_prefill_i8(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y,
+                             void* ws, int M, int N, int K, int mt, int splits, hipStream_t st);
 
 // grouped (MoE) path
 constexpr bool GROUPED_TILED = true;   // grouped handles use the tiled layout, per expert

@@ -51,6 +51,7 @@ struct DmaCfg {
   static constexpr int BN = 128;
   static constexpr int WP = QT == QT_Q4K ? 5 : 7;   // weight pieces per row per stage
   static constexpr int A_BYTES = BM * 256;
+  static constexpr int W_OFF = A_BYTES;             // the weight pieces within a slot
   static constexpr int W_BYTES = WP * BN * 16 + (QT == QT_Q6K ? BN * 4 : 0);
   static constexpr int SLOT = A_BYTES + W_BYTES;
   static constexpr int LDS = DMA_SLOTS * SLOT;
@@ -139,10 +140,10 @@ __device__ __forceinline__ void dma_load_a(ARow arow, uint8_t* smem, int s_begin
 // Loader wave 5: the weight pieces of the tile's 128 rows (rows past N are
 // clamped to N - 1: loaded, never stored).  In the tiled layout (IL) each
 // piece load of the wave is four contiguous 256-byte runs (16 rows each).
-template <int QT, int MT, bool IL>
+// C: the slot layout (SLOT bytes per slot, the pieces at W_OFF, WP of them).
+template <int QT, int MT, bool IL, class C = DmaCfg<QT, MT>>
 __device__ __forceinline__ void dma_load_w(const uint8_t* W, int N, int K, int n0, uint8_t* smem,
                                            int s_begin, int s_end, int rot) {
-  using C = DmaCfg<QT, MT>;
   constexpr int NI = 2 * C::WP + (QT == QT_Q6K ? 2 : 0);
   const int lane = threadIdx.x & 63;
   const int nst = s_end - s_begin;
@@ -156,7 +157,7 @@ __device__ __forceinline__ void dma_load_w(const uint8_t* W, int N, int K, int n
   auto issue = [&](int t) {
     const int s = dma_stage(t, s_begin, nst, rot);
     const int kb = s >> 1, hb = s & 1;
-    uint8_t* base = smem + (t % DMA_SLOTS) * C::SLOT + C::A_BYTES;
+    uint8_t* base = smem + (t % DMA_SLOTS) * C::SLOT + C::W_OFF;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n = rn[h];

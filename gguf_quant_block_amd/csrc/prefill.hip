@@ -159,6 +159,13 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ P, const f16* __r
   Y[i] = (f16)y;
 }
 
+hipError_t launch_splitk_reduce(const float* P, const f16* R, f16* Y, long long MN, int splits,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, P,
+                     R, Y, MN, splits);
+  return hipGetLastError();
+}
+
 template <int QT, int MT, int NT>
 static hipError_t launch_prefill_t(const uint8_t* W, const f16* A, const f16* R, f16* Y, float* P,
                                    int M, int N, int K, int splits, hipStream_t st) {
@@ -186,10 +193,7 @@ static hipError_t launch_prefill_t(const uint8_t* W, const f16* A, const f16* R,
 #endif
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  const long long MN = (long long)M * N;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, P,
-                     R, Y, MN, splits);
-  return hipGetLastError();
+  return launch_splitk_reduce(P, R, Y, (long long)M * N, splits, st);
 }
 
 void prefill_choose(int qtype, int M, int N, int K, int num_cu, int* mt, int* nt, int* splits) {

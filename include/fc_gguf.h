@@ -57,7 +57,8 @@ typedef struct fc_gguf* fc_gguf_t;
 #define FC_GGUF_Q5_K 5   /* 176 B per 256 values: d, dmin, 12 B scales/mins, qh[32], qs[128] */
 #define FC_GGUF_Q6_K 6   /* 210 B per 256 values: ql[128], qh[64], sc[16] (int8), d */
 
-/* Path override (fc_gguf_set_path; default from env FC_GGUF_PATH=auto|decode|prefill|scratch). */
+/* Path override (fc_gguf_set_path; default from env
+   FC_GGUF_PATH=auto|decode|prefill|scratch|int8). */
 #define FC_GGUF_PATH_AUTO    0   /* M < 8 -> decode, else prefill */
 #define FC_GGUF_PATH_DECODE  1   /* int8 GEMV for any M (rows taken in chunks of at most 7) */
 #define FC_GGUF_PATH_PREFILL 2   /* f16 matrix-core path for any M >= 1 */
@@ -65,6 +66,13 @@ typedef struct fc_gguf* fc_gguf_t;
                                     handle's workspace (N*K*2 bytes), then a rocBLAS GEMM with the
                                     residual as beta*C (the page's path for devices without the
                                     decode-once kernel; never chosen by AUTO) */
+#define FC_GGUF_PATH_INT8    4   /* variant: per-32 int8 activations (the decode path's
+                                    quantisation, a pass of its own) times the integer codes on
+                                    int8 matrix cores, scales applied per 32-value group in f32;
+                                    computes what the decode path computes, at any M (its
+                                    results are checked against the int8 emulation, not the
+                                    fp64 FC); workspace: M rounded up to 128 times (K + K/4)
+                                    bytes plus the split-K partials; never chosen by AUTO */
 
 /* Error codes. */
 #define FC_GGUF_OK            0
