@@ -48,6 +48,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense f16 matrix cores
+INT8_MFMA_PEAK_TOPS = 5033.2    # MI355X dense int8 matrix cores
 LAYERS = 32
 MOE_COPIES = 7               # 7 x 165 MB per expert FC: the weights stream from HBM
 CPU_LAYERS = 6               # oracle sample: about 10-30 s on one core
@@ -144,6 +145,49 @@ def scratch_comparison(prefill, dev, iters=10):
             for fc, *_ in calls:
                 fc.set_path("auto")
         out[f"m{M}"] = {"direct_tflops": res["prefill_tflops"], "dequant_once_tflops": res["scratch_tflops"]}
+    return out
+
+
+def int8_comparison(prefill, dev, iters=10):
+    """The int8 matrix-core prefill variant (FC_GGUF_PATH_INT8: per-32 int8
+    activations, integer MFMA per group, f32 scale algebra) against the f16
+    prefill path on the same prefill FCs at M = 512, eager launches timed with
+    HIP events; int8 multiply-adds counted as 2 ops."""
+    import torch
+    from gguf_quant_block_amd import synth
+
+    M = 512
+    out = {"workload": "Q5_K and Q6_K, [8192,2048] and [2048,8192], M=512, fused residual; "
+                       "the variant's quantisation pass included",
+           "peak_int8_tops": INT8_MFMA_PEAK_TOPS}
+    for path in ("prefill", "int8"):
+        ops, calls = 0, []
+        for fc, _, _, _ in prefill:
+            K, N = fc.K, fc.N
+            A = torch.from_numpy(synth.normal_f16((M, K), synth.rng(9, M, synth.TAG_A))).to(dev)
+            R = torch.from_numpy(synth.normal_f16((M, N), synth.rng(9, M, synth.TAG_R))).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            calls.append((fc, A, R, Y))
+            ops += 2 * M * N * K
+        for fc, *_ in calls:
+            fc.set_path(path)
+        for fc, A, R, Y in calls:
+            fc(A, R, out=Y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            for fc, A, R, Y in calls:
+                fc(A, R, out=Y)
+        e1.record()
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) / 1e3 / iters
+        key = "f16_prefill" if path == "prefill" else "int8_mfma"
+        out[key + "_tops"] = round(ops / s / 1e12, 1)
+        out[key + "_us_per_fc"] = round(s * 1e6 / len(calls), 2)
+        for fc, *_ in calls:
+            fc.set_path("auto")
+    out["int8_frac_of_int8_peak"] = round(out["int8_mfma_tops"] / INT8_MFMA_PEAK_TOPS, 4)
     return out
 
 
@@ -502,6 +546,7 @@ def main():
         "wall_s": round(wall, 3),
     }
     line["scratch_comparison"] = scratch_comparison(prefill, dev)
+    line["int8_comparison"] = int8_comparison(prefill, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -284,11 +284,19 @@ __device__ __forceinline__ void i8_compute(int N, int K, int n0, const uint8_t* 
         if constexpr (QT == QT_Q6K) w[j] = h[j].codes(g);
         else w[j] = h[j].template codes<QT == QT_Q5K>(g);
       }
+      // the k-step's activation codes and group scales, all read first
+      long av[MT];
+      floatx4 sv[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const int r = 16 * i + (lane & 15);
-        const long a = *(const long*)(As + r * 128 + (((2 * g + pq) ^ (r & 7)) << 4) + sub);
-        const floatx4 s4 = *(const floatx4*)(Ss + g * BM + 16 * i + 4 * kq);
+        av[i] = *(const long*)(As + r * 128 + (((2 * g + pq) ^ (r & 7)) << 4) + sub);
+        sv[i] = *(const floatx4*)(Ss + g * BM + 16 * i + 4 * kq);
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const long a = av[i];
+        const floatx4 s4 = sv[i];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
           if constexpr (QT == QT_Q6K) {
@@ -310,6 +318,15 @@ __device__ __forceinline__ void i8_compute(int N, int K, int n0, const uint8_t* 
           }
         }
       }
+      // one scheduling region per k-step: the LDS reads, then each MFMA
+      // followed by a share of the scale arithmetic
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * MT, 0);
+#pragma unroll
+      for (int k = 0; k < MT * NTW * (QT == QT_Q6K ? 2 : 1); ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, QT == QT_Q6K ? 7 : 12, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (QT != QT_Q6K) {
       // the min term of the stage's four groups is itself a small matrix
