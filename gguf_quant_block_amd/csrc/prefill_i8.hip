@@ -46,6 +46,8 @@ namespace fcg {
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int I8_MROUND = 128;   // rows of the group-major scale arrays are padded to this
+constexpr int I8_CWAVES = 4;     // compute waves (weight rows 32w .. 32w + 31), then the two loaders
+constexpr int I8_THREADS = 64 * (I8_CWAVES + 2);
 
 // ----------------------------------------------------------- quantisation --
 
@@ -372,7 +374,7 @@ __device__ __forceinline__ void i8_epilogue(const floatx4 (&acc)[MT][DMA_NTW],
 }
 
 template <int QT, int MT>
-__global__ void __launch_bounds__(DMA_THREADS)
+__global__ void __launch_bounds__(I8_THREADS)
 prefill_i8_kernel(const uint8_t* W, const int8_t* qa, const float* sT, const float* uT,
                   const f16* __restrict__ R, f16* __restrict__ Y, float* __restrict__ P, int M,
                   int N, int K, int Mp, int tiles_m, int tiles_n, int splits,
@@ -400,11 +402,11 @@ prefill_i8_kernel(const uint8_t* W, const int8_t* qa, const float* sT, const flo
   const int nst = s_end - s_begin;
   const int rot = nst > 0 ? (nt + mt) % nst : 0;
   const int wave = threadIdx.x >> 6;
-  if (wave == DMA_CWAVES) {
+  if (wave == I8_CWAVES) {
     i8_load_a<QT, MT>(qa, sT, uT, M, K, Mp, m0, smem, s_begin, s_end, rot);
     return;
   }
-  if (wave == DMA_CWAVES + 1) {
+  if (wave == I8_CWAVES + 1) {
     dma_load_w<QT, MT, true, I8Cfg<QT, MT>>(W, N, K, n0, smem, s_begin, s_end, rot);
     return;
   }
@@ -427,7 +429,6 @@ static hipError_t launch_i8_t(const uint8_t* W, const int8_t* qa, const float* s
                               const f16* R, f16* Y, float* P, int M, int N, int K, int Mp,
                               int splits, hipStream_t st) {
   constexpr int BM = 16 * MT, BN = 128;
-  static_assert(DMA_ALOADERS == 1 && DMA_CWAVES == 4, "one activation loader, four compute waves");
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
   const int S_total = K / KSTAGE;
@@ -442,7 +443,7 @@ static hipError_t launch_i8_t(const uint8_t* W, const int8_t* qa, const float* s
     if (ea != hipSuccess) return ea;
     attr_set = true;
   }
-  hipLaunchKernelGGL((prefill_i8_kernel<QT, MT>), dim3(grid), dim3(DMA_THREADS), lds, st, W, qa, sT,
+  hipLaunchKernelGGL((prefill_i8_kernel<QT, MT>), dim3(grid), dim3(I8_THREADS), lds, st, W, qa, sT,
                      uT, R, Y, P, M, N, K, Mp, tiles_m, tiles_n, splits, per);
   return hipGetLastError();
 }
