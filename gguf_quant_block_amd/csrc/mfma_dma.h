@@ -9,9 +9,12 @@
 // three stages, so two stages of loads are in flight while one computes, and
 // no register holds data in flight.
 //
-// Workgroup: 384 threads.  Waves 0-3 compute (wave w owns weight rows
-// 32w .. 32w+31 of the 128-row tile); wave 4 loads the activation tile, wave
-// 5 the weight pieces.  A stage is half a super-block (128 values of K).
+// Workgroup: 640 threads.  Waves 0-7 compute (wave w owns weight rows
+// 16w .. 16w+15 of the 128-row tile: two compute waves per SIMD, each reading
+// every activation operand of the stage, so the LDS reads double while each
+// weight is still decoded once; a lone wave issues VALU only about every 7
+// cycles, two per SIMD about every 4); wave 8 loads the activation tile,
+// wave 9 the weight pieces.  A stage is half a super-block (128 values of K).
 // LDS stage slot:
 //   A: BM rows x 16 chunks of 16 B; chunk c of row r sits at position
 //      c ^ (r & 15) of the row, so that the 16 rows of an MFMA operand read
@@ -41,8 +44,8 @@ namespace fcg {
 #endif
 constexpr int DMA_SLOTS = FCG_DMA_SLOTS;          // LDS ring depth (stages)
 constexpr int DMA_ALOADERS = FCG_DMA_ALOADERS;    // waves loading the activation tile
-constexpr int DMA_CWAVES = 4;                    // compute waves
-constexpr int DMA_NTW = 2;                        // 16-row weight sub-tiles per compute wave
+constexpr int DMA_CWAVES = 8;                    // compute waves
+constexpr int DMA_NTW = 8 / DMA_CWAVES;           // 16-row weight sub-tiles per compute wave
 constexpr int DMA_THREADS = 64 * (DMA_CWAVES + DMA_ALOADERS + 1);
 
 template <int QT, int MT>
@@ -95,7 +98,7 @@ __device__ __forceinline__ int dma_stage(int t, int s_begin, int nst, int rot) {
   return s_begin + u;
 }
 
-// Loader wave 4: the activation tile.  arow(r) points at the activation row
+// Loader wave DMA_CWAVES: the activation tile.  arow(r) points at the activation row
 // of tile row r (any valid row for rows past the tile's end).  Only the
 // first MTA halves are loaded.
 template <int QT, int MT, int MTA, class ARow>
@@ -137,7 +140,7 @@ __device__ __forceinline__ void dma_load_a(ARow arow, uint8_t* smem, int s_begin
   }
 }
 
-// Loader wave 5: the weight pieces of the tile's 128 rows (rows past N are
+// Loader wave DMA_CWAVES + 1: the weight pieces of the tile's 128 rows (rows past N are
 // clamped to N - 1: loaded, never stored).  In the tiled layout (IL) each
 // piece load of the wave is four contiguous 256-byte runs (16 rows each).
 // C: the slot layout (SLOT bytes per slot, the pieces at W_OFF, WP of them).
@@ -228,9 +231,9 @@ __device__ __forceinline__ void dma_dec_init(typename HalfDec<QT>::type (&h)[DMA
   }
 }
 
-// Compute waves 0-3: acc[i][j] += C[n][m] of the 16x16 sub-tiles (half
-// i < MTA, weight sub-tile j of the wave's 32 rows) over the stages.  Wave w
-// owns weight rows 32w .. 32w + 31.
+// Compute waves: acc[i][j] += C[n][m] of the 16x16 sub-tiles (half i < MTA,
+// weight sub-tile j of the wave's 16 NTW rows) over the stages.  Wave w owns
+// weight rows 16 NTW w .. 16 NTW (w + 1) - 1.
 //
 // Software pipeline, one k-step deep: while the matrix cores run the MFMAs
 // of k-step g, the wave reads the activation operands of its next k-step and

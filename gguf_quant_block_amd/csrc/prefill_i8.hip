@@ -18,10 +18,11 @@
 //     the scale s and u = s * T (T the sum of the group's 32 codes) stored
 //     group-major, sT[K/32][Mp], uT[K/32][Mp] (Mp = M rounded up to 128; the
 //     padding rows hold zeros).
-//   * prefill_i8_kernel: the loader-wave tile of the f16 prefill (mfma_dma.h:
-//     wave 4 streams the activation codes and their scales, wave 5 the weight
-//     pieces, into a ring of three LDS stages; waves 0-3 compute, wave w on
-//     weight rows 32w .. 32w + 31).  Per k-step (32 values = one activation
+//   * prefill_i8_kernel: the loader-wave structure of the f16 prefill
+//     (mfma_dma.h) with four compute waves: wave 4 streams the activation
+//     codes and their scales, wave 5 the weight pieces (the f16 path's
+//     loader), into a ring of three LDS stages; waves 0-3 compute, wave w on
+//     weight rows 32w .. 32w + 31.  Per k-step (32 values = one activation
 //     group) a compute wave turns its weight pieces into int8 codes, runs one
 //     int8 MFMA per 16x16 sub-tile (two for Q6_K, whose 16-value sub-blocks
 //     carry their own scales) and adds the group's contribution in f32:
@@ -48,6 +49,7 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 constexpr int I8_MROUND = 128;   // rows of the group-major scale arrays are padded to this
 constexpr int I8_CWAVES = 4;     // compute waves (weight rows 32w .. 32w + 31), then the two loaders
 constexpr int I8_THREADS = 64 * (I8_CWAVES + 2);
+constexpr int I8_NTW = 2;        // 16-row weight sub-tiles per compute wave
 
 // ----------------------------------------------------------- quantisation --
 
@@ -231,8 +233,8 @@ template <> struct I8Dec<QT_Q4K> { using type = Q45I8; };
 // 16j + lane % 16] of the tile, over the stages.
 template <int QT, int MT>
 __device__ __forceinline__ void i8_compute(int N, int K, int n0, const uint8_t* smem, int s_begin,
-                                           int s_end, int rot, floatx4 (&acc)[MT][DMA_NTW]) {
-  constexpr int NTW = DMA_NTW, BM = 16 * MT;
+                                           int s_end, int rot, floatx4 (&acc)[MT][I8_NTW]) {
+  constexpr int NTW = I8_NTW, BM = 16 * MT;
   using C = I8Cfg<QT, MT>;
   using Dec = typename I8Dec<QT>::type;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -350,12 +352,12 @@ __device__ __forceinline__ void i8_compute(int N, int K, int n0, const uint8_t* 
 // Store of a compute wave's sub-tiles: + R and one f16 rounding, or f32
 // split-K partials P[split][M][N].
 template <int MT>
-__device__ __forceinline__ void i8_epilogue(const floatx4 (&acc)[MT][DMA_NTW],
+__device__ __forceinline__ void i8_epilogue(const floatx4 (&acc)[MT][I8_NTW],
                                             const f16* __restrict__ R, f16* __restrict__ Y,
                                             float* __restrict__ P, int M, int N, int m0, int n0,
                                             int sp, int splits) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = n0 + wave * 16 * DMA_NTW + (lane & 15);
+  const int n = n0 + wave * 16 * I8_NTW + (lane & 15);
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -363,7 +365,7 @@ __device__ __forceinline__ void i8_epilogue(const floatx4 (&acc)[MT][DMA_NTW],
       const int m = m0 + 16 * i + 4 * (lane >> 4) + q;
       if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < DMA_NTW; ++j) {
+      for (int j = 0; j < I8_NTW; ++j) {
         const int nn = n + 16 * j;
         if (nn >= N) continue;
         const float v = acc[i][j][q];
@@ -410,7 +412,7 @@ prefill_i8_kernel(const uint8_t* W, const int8_t* qa, const float* sT, const flo
     dma_load_w<QT, MT, true, I8Cfg<QT, MT>>(W, N, K, n0, smem, s_begin, s_end, rot);
     return;
   }
-  floatx4 acc[MT][DMA_NTW];
+  floatx4 acc[MT][I8_NTW];
   i8_compute<QT, MT>(N, K, n0, smem, s_begin, s_end, rot, acc);
   i8_epilogue<MT>(acc, R, Y, P, M, N, m0, n0, sp, splits);
 }
