@@ -147,6 +147,16 @@ def test_forced_decode_for_larger_m(gpu_lib, qtype):
     assert maxrel(y, ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
 
 
+@pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
+def test_gemv_large_k_row_chunks(gpu_lib, qtype):
+    # K = 16384: seven rows' quantised activations exceed one CU's LDS, so the
+    # library takes the rows in chunks of six and one
+    M, N, K = 7, 24, 16384
+    w, A, R = case(qtype, M, N, K, 57, 0)
+    y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
+    assert maxrel(y, ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
+
+
 def test_m_zero_is_noop(gpu_lib):
     import torch
     w, _, _ = case("q6_k", 1, 32, 256, 56, 0)

@@ -42,7 +42,7 @@ def _fc_int8(w, qtype, N, K):
 # every tile size (M = 1 .. 200 -> 16..128-row tiles), split-K grids (small
 # M x N), ragged M and N, K with a padded last tile of blocks (1280, 768)
 SHAPES = [(16, 512, 2048), (1, 37, 768), (8, 100, 3072), (37, 300, 1280), (130, 64, 512),
-          (200, 256, 8192), (64, 1000, 2048)]
+          (200, 256, 8192), (64, 1000, 2048), (8, 48, 256), (24, 64, 14336)]
 
 
 @pytest.mark.parametrize("qtype", QTYPES)

@@ -46,7 +46,7 @@ def test_small_config_m16(gpu_lib, qtype):
 
 @pytest.mark.parametrize("qtype", QTYPES)
 @pytest.mark.parametrize("M,N,K", [(8, 80, 256), (37, 200, 768), (130, 384, 1024), (300, 64, 512),
-                                   (64, 128, 2048), (17, 1000, 512)])
+                                   (64, 128, 2048), (17, 1000, 512), (24, 64, 14336)])
 def test_prefill_ragged(gpu_lib, qtype, M, N, K):
     w, A, R = case(qtype, M, N, K, 60, M * 7 + N)
     y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
