@@ -200,33 +200,37 @@ template <int QT> struct HalfDec { using type = Q6Half; };
 template <> struct HalfDec<QT_Q5K> { using type = Q45Half<true>; };
 template <> struct HalfDec<QT_Q4K> { using type = Q45Half<false>; };
 
-// Per-half setup of the lane's decoders for stage s, whose weight pieces sit
-// at Ws: the pieces of rows nloc[j] that the lane's k-quarter kq reads.  IL:
-// the weights are in the tiled layout (selects which half of a Q6_K d word
-// is the row's).
+// Per-half setup of the lane's decoders for stage s.  Pointers into the
+// stage's slot: W0 the lane's row (weight sub-tile 0) in piece 0, W1 that row
+// plus the lane's sub-block within a piece (k-quarter kq: piece pair kq / 2,
+// half kq & 1), W2 the aligned Q6_K d word of that row.  Sub-tile j lies 16
+// rows further on.  IL: the weights are in the tiled layout (selects which
+// half of a Q6_K d word is the row's).
 template <int QT, int MT, bool IL>
 __device__ __forceinline__ void dma_dec_init(typename HalfDec<QT>::type (&h)[DMA_NTW],
-                                             const uint8_t* Ws, const int (&nloc)[DMA_NTW],
-                                             const int (&rn)[DMA_NTW], int s, int KB, int kq) {
+                                             const uint8_t* W0, const uint8_t* W1,
+                                             const uint8_t* W2, const int (&rn)[DMA_NTW], int s,
+                                             int KB, int kq) {
   using C = DmaCfg<QT, MT>;
-  const int hb = s & 1, kb = s >> 1, sub = 8 * (kq & 1), pq = kq >> 1;
+  constexpr int PB = C::BN * 16;                    // bytes of one piece over the tile's rows
+  const int hb = s & 1, kb = s >> 1;
 #pragma unroll
   for (int j = 0; j < DMA_NTW; ++j) {
-    auto pc = [&](int q) { return Ws + (q * 128 + nloc[j]) * 16; };
+    const uint8_t* p0 = W0 + 256 * j;
+    const uint8_t* p1 = W1 + 256 * j;
     if constexpr (QT == QT_Q5K) {
-      h[j].init(*(const uint4*)pc(0), *(const uint2*)(pc(3 + pq) + sub),
-                *(const uint2*)(pc(5 + pq) + sub), *(const uint2*)(pc(1 + pq) + sub), hb);
+      h[j].init(*(const uint4*)p0, *(const uint2*)(p1 + 3 * PB), *(const uint2*)(p1 + 5 * PB),
+                *(const uint2*)(p1 + PB), hb);
     } else if constexpr (QT == QT_Q4K) {
-      h[j].init(*(const uint4*)pc(0), *(const uint2*)(pc(1 + pq) + sub),
-                *(const uint2*)(pc(3 + pq) + sub), uint2{0u, 0u}, hb);
+      h[j].init(*(const uint4*)p0, *(const uint2*)(p1 + PB), *(const uint2*)(p1 + 3 * PB),
+                uint2{0u, 0u}, hb);
     } else {
-      const uint32_t dw = *(const uint32_t*)(Ws + C::WP * 128 * 16 + 4 * nloc[j]);
+      const uint32_t dw = *(const uint32_t*)(W2 + 64 * j);
       // the row's half of the word: tiled, the blocks of rows n and n ^ 1
       // share it; canonical, the blocks b and b ^ 1
       const int half = IL ? (rn[j] & 1) : (int)(((size_t)rn[j] * KB + kb) & 1);
-      h[j].init(*(const uint2*)(pc(pq) + sub), *(const uint2*)(pc(2 + pq) + sub),
-                *(const uint2*)(pc(4 + pq) + sub), *(const uint2*)(pc(6) + 8 * hb),
-                dw >> (16 * half), kq);
+      h[j].init(*(const uint2*)p1, *(const uint2*)(p1 + 2 * PB), *(const uint2*)(p1 + 4 * PB),
+                *(const uint2*)(p0 + 6 * PB + 8 * hb), dw >> (16 * half), kq);
     }
   }
 }
@@ -270,25 +274,51 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
     stage_barrier();
     return;
   }
+  // The lane's LDS read offsets within a slot, the same for every stage:
+  // la[g] the activation operand of k-step g for row half 0 (row half i is
+  // 4096 i further on), lw0 / lw1 / lw2 the weight pointers of
+  // dma_dec_init.  The empty asm hides how they were made, so that each
+  // address in the loop is one add of the slot's offset (the compiler
+  // otherwise rebuilds every address from the stage index, at two VALU
+  // instructions apiece).
+  uint32_t la[KS];
+  const int l15 = lane & 15;
+#pragma unroll
+  for (int g = 0; g < KS; ++g) {
+    la[g] = (16 * l15 + ((4 * g + kq) ^ l15)) * 16;
+    asm("" : "+v"(la[g]));
+  }
+  uint32_t lw0 = C::A_BYTES + 16 * nloc[0];
+  uint32_t lw1 = lw0 + C::BN * 16 * (kq >> 1) + 8 * (kq & 1);
+  uint32_t lw2 = C::A_BYTES + C::WP * C::BN * 16 + 4 * nloc[0];
+  asm("" : "+v"(lw0));
+  asm("" : "+v"(lw1));
+  asm("" : "+v"(lw2));
   // activation operands of k-step g of the stage in slot As
   auto lda = [&](const uint8_t* As, int g, half8v* af) {
 #pragma unroll
-    for (int i = 0; i < MTA; ++i) {
-      const int r = 16 * i + (lane & 15);
-      af[i] = *(const half8v*)(As + (r * 16 + ((4 * g + kq) ^ (r & 15))) * 16);
-    }
+    for (int i = 0; i < MTA; ++i) af[i] = *(const half8v*)(As + la[g] + 4096 * i);
+  };
+  auto dec_init = [&](Dec (&hh)[NTW], const uint8_t* Ss, int t) {
+    dma_dec_init<QT, MT, IL>(hh, Ss + lw0, Ss + lw1, Ss + lw2, rn,
+                             dma_stage(t, s_begin, nst, rot), KB, kq);
   };
 
   stage_barrier();                                  // stage 0 has landed
   Dec h[NTW];
   half8v wc[NTW], afc[MTA];
   lda(smem, 0, afc);
-  dma_dec_init<QT, MT, IL>(h, smem + C::A_BYTES, nloc, rn, dma_stage(0, s_begin, nst, rot), KB, kq);
+  dec_init(h, smem, 0);
 #pragma unroll
   for (int j = 0; j < NTW; ++j) wc[j] = h[j].frag(0);
 
   for (int t = 0; t < nst; ++t) {
-    const uint8_t* As = smem + (t % DMA_SLOTS) * C::SLOT;
+    // the slot offsets, hidden likewise (the compiler would split t % 3
+    // into two running sums and apply each to every address)
+    uint32_t so = (t % DMA_SLOTS) * C::SLOT, sn = ((t + 1) % DMA_SLOTS) * C::SLOT;
+    asm("" : "+s"(so));
+    asm("" : "+s"(sn));
+    const uint8_t* As = smem + so;
 #pragma unroll
     for (int gg = 0; gg < KS; ++gg) {
       half8v wnext[NTW], afn[MTA];
@@ -298,10 +328,9 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
         for (int j = 0; j < NTW; ++j) wnext[j] = h[j].frag(gg + 1);
       } else {
         compute_stage_barrier();                    // slot t read; stage t + 1 landed
-        const uint8_t* An = smem + ((t + 1) % DMA_SLOTS) * C::SLOT;
+        const uint8_t* An = smem + sn;
         lda(An, 0, afn);
-        dma_dec_init<QT, MT, IL>(h, An + C::A_BYTES, nloc, rn,
-                                 dma_stage(t + 1, s_begin, nst, rot), KB, kq);
+        dec_init(h, An, t + 1);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) wnext[j] = h[j].frag(0);
       }
