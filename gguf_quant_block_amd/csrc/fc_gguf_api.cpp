@@ -168,8 +168,17 @@ int run_scratch(fc_gguf* h, const fcg::f16* a, const fcg::f16* r, fcg::f16* y, i
 }
 
 // Validation shared by fc_gguf_run and fc_gguf_run_f32 (element size es).
+// FC_GGUF_OK when the current device is the handle's (its weights, workspace
+// and launches all live there).
+int check_device(fc_gguf_t h) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FC_GGUF_EHIP;
+  return dev == h->device ? FC_GGUF_OK : FC_GGUF_EDEVICE;
+}
+
 int check_run(fc_gguf_t h, const void* A, int64_t M, const void* R, const void* Y, size_t es) {
   if (!h || M < 0) return FC_GGUF_EINVAL;
+  if (const int rc = check_device(h); rc != FC_GGUF_OK) return rc;
   if (h->E != 1) return FC_GGUF_EINVAL;            // grouped handles use run_grouped
   if (M == 0) return FC_GGUF_OK;
   if (!A || !Y) return FC_GGUF_EINVAL;
@@ -225,10 +234,16 @@ int fc_gguf_create_grouped(int64_t E, int64_t N, int64_t K, int qtype, const voi
 
 int fc_gguf_destroy(fc_gguf_t h) {
   if (!h) return FC_GGUF_OK;
+  // the handle's device, whichever is current: its work must end before the
+  // memory is freed
+  int cur = -1;
+  const bool switched = hipGetDevice(&cur) == hipSuccess && cur != h->device &&
+                        hipSetDevice(h->device) == hipSuccess;
   hipDeviceSynchronize();
   if (h->w) hipFree(h->w);
   if (h->ws) hipFree(h->ws);
   if (h->blas) rocblas_destroy_handle(h->blas);
+  if (switched) hipSetDevice(cur);
   delete h;
   return FC_GGUF_OK;
 }
@@ -299,6 +314,7 @@ int fc_gguf_run_f32(fc_gguf_t h, const float* A, int64_t M, const float* R, floa
 int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, const int32_t* ids,
                         int top_k, void* Y, void* stream) {
   if (!h || T < 0) return FC_GGUF_EINVAL;
+  if (const int rc = check_device(h); rc != FC_GGUF_OK) return rc;
   if (T == 0) return FC_GGUF_OK;
   if (!A || !ids || !Y || top_k <= 0 || top_k > h->E || (a_per_slot != 0 && a_per_slot != 1))
     return FC_GGUF_EINVAL;
@@ -339,6 +355,7 @@ int fc_gguf_debug_quantize_f32(const float* A, int64_t M, int64_t K, int8_t* qa,
 
 int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S, void* stream) {
   if (!h || M < 0 || h->E != 1) return FC_GGUF_EINVAL;
+  if (const int rc = check_device(h); rc != FC_GGUF_OK) return rc;
   if (M == 0) return FC_GGUF_OK;
   if (!qa || !S || !aligned(qa, 16)) return FC_GGUF_EINVAL;
   const int ns = (int)(h->K / (h->qtype == FC_GGUF_Q6_K ? 16 : 32));
@@ -350,6 +367,7 @@ int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S,
 
 int fc_gguf_debug_weights(fc_gguf_t h, void* dst, void* stream) {
   if (!h || !dst) return FC_GGUF_EINVAL;
+  if (const int rc = check_device(h); rc != FC_GGUF_OK) return rc;
   hipError_t e = hipMemcpyAsync(dst, h->w, h->expert_bytes * (size_t)h->E, hipMemcpyDeviceToDevice,
                                 (hipStream_t)stream);
   return e == hipSuccess ? FC_GGUF_OK : hip_fail(h, e);
@@ -363,6 +381,7 @@ const char* fc_gguf_strerror(int code) {
     case FC_GGUF_ENOMEM: return "device allocation failed";
     case FC_GGUF_EHIP: return "HIP runtime or launch error";
     case FC_GGUF_ERANGE: return "size exceeds an internal limit";
+    case FC_GGUF_EDEVICE: return "the current device is not the handle's device";
     default: return "unknown error";
   }
 }

@@ -458,13 +458,11 @@ static hipError_t launch_gemv_t(const uint8_t* W, const AT* A, const AT* R, AT* 
   const size_t lds = gemv_layout<QT>(MR, tiled_kb(K / QK), nw).total;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = gemv_kernel<QT, MR, AT>;
-  // raise the dynamic-LDS limit once per instantiation (to the CU's 160 KB)
-  static bool attr_set = false;
-  if (lds > 65536 && !attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024);
+  // raise the dynamic-LDS limit (to the CU's 160 KB) once per device
+  static std::atomic<uint64_t> lds_raised{0};
+  if (lds > 65536) {
+    hipError_t e = raise_lds_limit((const void*)kern, 160 * 1024, lds_raised);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int rt = gemv_rt(K);
   const int grid = (tiled_rows(N) / TILE_ROWS + rt - 1) / rt;

@@ -3,10 +3,27 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+
+#include <atomic>
 #include <stdint.h>
 
 namespace fcg {
 typedef _Float16 f16;
+
+// Raises kern's dynamic-LDS limit to `bytes` on the current device, once per
+// device: the limit is an attribute of the function on each device.  `done`
+// (one per kernel instantiation) holds a bit per device id; ids past 63 are
+// set on every call.
+inline hipError_t raise_lds_limit(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // canonical AoS blocks of an [N, K] matrix -> a device layout of layout.h,
 // tiled or canonical (the destination holds layout_bytes(...) bytes)

@@ -178,13 +178,9 @@ static hipError_t launch_prefill_t(const uint8_t* W, const f16* A, const f16* R,
 #if FCG_PREFILL_DMA
   static_assert(NT == 2, "the loader-wave tile is 128 weight rows wide");
   constexpr int lds = DmaCfg<QT, MT>::LDS;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t ea = hipFuncSetAttribute((const void*)prefill_dma_kernel<QT, MT>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (ea != hipSuccess) return ea;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  hipError_t ea = raise_lds_limit((const void*)prefill_dma_kernel<QT, MT>, lds, lds_raised);
+  if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL((prefill_dma_kernel<QT, MT>), dim3(grid), dim3(DMA_THREADS), lds, st, W, A, R,
                      Y, P, M, N, K, tiles_m, tiles_n, splits, per);
 #else

@@ -438,13 +438,9 @@ static hipError_t launch_i8_t(const uint8_t* W, const int8_t* qa, const float* s
   const int grid = tiles_m * tiles_n * splits;
   constexpr int lds = I8Cfg<QT, MT>::LDS;
   static_assert(lds <= 160 * 1024, "LDS ring");
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t ea = hipFuncSetAttribute((const void*)prefill_i8_kernel<QT, MT>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (ea != hipSuccess) return ea;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  hipError_t ea = raise_lds_limit((const void*)prefill_i8_kernel<QT, MT>, lds, lds_raised);
+  if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL((prefill_i8_kernel<QT, MT>), dim3(grid), dim3(I8_THREADS), lds, st, W, qa, sT,
                      uT, R, Y, P, M, N, K, Mp, tiles_m, tiles_n, splits, per);
   return hipGetLastError();

@@ -31,7 +31,10 @@
  *   - Return value: 0 on success, a negative FC_GGUF_E* code on failure;
  *     fc_gguf_strerror() describes it.  Nothing is launched on failure.
  *   - "device" pointers are HIP device memory of the current device;
- *     "host" pointers are ordinary host memory.
+ *     "host" pointers are ordinary host memory.  A handle lives on the device
+ *     that was current at its creation: every call that launches work on it
+ *     (run, run_f32, run_grouped, debug_int_dots, debug_weights) needs that
+ *     device current and returns FC_GGUF_EDEVICE otherwise.
  *   - f16 is IEEE binary16; all matrices are row-major and contiguous.
  *   - `stream` is a hipStream_t (NULL = the null stream).  run calls are
  *     asynchronous and stream-ordered; kernel faults surface at the caller's
@@ -81,6 +84,7 @@ typedef struct fc_gguf* fc_gguf_t;
 #define FC_GGUF_ENOMEM       -3  /* device allocation failed */
 #define FC_GGUF_EHIP         -4  /* a HIP runtime call or kernel launch failed */
 #define FC_GGUF_ERANGE       -5  /* a size exceeds an internal limit (e.g. 32-bit indexing) */
+#define FC_GGUF_EDEVICE      -6  /* the current device is not the one the handle was created on */
 
 /*
  * Create a handle for one weight matrix W[N,K].
@@ -120,7 +124,8 @@ int fc_gguf_run_f32(fc_gguf_t h, const float* A, int64_t M, const float* R, floa
 /* Force a path (FC_GGUF_PATH_*); the testing switch of the FC primitive. */
 int fc_gguf_set_path(fc_gguf_t h, int path);
 
-/* Frees the handle and its device memory; NULL is accepted. Synchronises the device. */
+/* Frees the handle and its device memory; NULL is accepted.  Synchronises the
+ * handle's device (made current for the call if another one is). */
 int fc_gguf_destroy(fc_gguf_t h);
 
 /* N, K, qtype, and the byte size of the device weights of a handle (any may be

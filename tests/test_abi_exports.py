@@ -32,9 +32,10 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_strerror_codes(L):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.fc_gguf_strerror(code)
     assert L.fc_gguf_strerror(-1) == b"invalid argument"
+    assert b"device" in L.fc_gguf_strerror(-6)
 
 
 def test_host_validation_without_gpu(L):
