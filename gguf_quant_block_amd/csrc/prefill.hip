@@ -12,6 +12,8 @@
 // sharing weight columns land on the same XCD (one L2 per XCD).
 #include "common.h"
 #include "internal.h"
+
+#include <type_traits>
 #include "mfma_tile.h"
 #include "mfma_dma.h"
 
@@ -148,21 +150,62 @@ prefill_dma_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   prefill_epilogue<MT, DMA_NTW>(acc, R, Y, P, M, N, m0, n0 + wave * 16 * DMA_NTW, sp, splits);
 }
 
-// Y = sum over splits of P + R, rounded once to f16.
+// Y = sum over splits of P + R, rounded once to f16.  V consecutive outputs
+// per thread (4 when M*N is a multiple of 4: 16-byte partial loads, 8-byte
+// R and Y accesses).  The partial sums are added in split order, so the
+// result does not depend on V; each thread issues the loads of up to eight
+// splits before adding them, so that their latencies overlap.
+template <int V>
 __global__ void splitk_reduce_kernel(const float* __restrict__ P, const f16* __restrict__ R,
                                      f16* __restrict__ Y, long long MN, int splits) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int U = 8;                              // splits in flight per thread
+  const long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (i >= MN) return;
-  float y = 0.f;
-  for (int s = 0; s < splits; ++s) y += P[(size_t)s * MN + i];
-  if (R) y += (float)R[i];
-  Y[i] = (f16)y;
+  using PT = typename std::conditional<V == 4, float4, float>::type;
+  float y[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) y[v] = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += U) {
+    PT p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + u < splits) p[u] = *(const PT*)(P + (size_t)(s0 + u) * MN + i);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < splits) {
+        const float* pu = (const float*)&p[u];
+#pragma unroll
+        for (int v = 0; v < V; ++v) y[v] += pu[v];
+      }
+    }
+  }
+  if constexpr (V == 4) {
+    if (R) {
+      const uint2 r = *(const uint2*)(R + i);
+      const f16* rh = (const f16*)&r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) y[v] += (float)rh[v];
+    }
+    f16 o[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v] = (f16)y[v];
+    *(uint2*)(Y + i) = *(const uint2*)o;
+  } else {
+    if (R) y[0] += (float)R[i];
+    Y[i] = (f16)y[0];
+  }
 }
 
 hipError_t launch_splitk_reduce(const float* P, const f16* R, f16* Y, long long MN, int splits,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st, P,
-                     R, Y, MN, splits);
+  if (MN % 4 == 0) {
+    const long long n = MN / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel<4>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       P, R, Y, MN, splits);
+  } else {
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st,
+                       P, R, Y, MN, splits);
+  }
   return hipGetLastError();
 }
 
