@@ -21,6 +21,7 @@ struct fc_gguf {
   uint8_t* w = nullptr;         // device weights (Q4_K / Q5_K blocks; Q6_K planes; per expert)
   size_t expert_bytes = 0;      // bytes of one [N, K] matrix
   int path = FC_GGUF_PATH_AUTO;
+  int decode_rows = 8;                // AUTO: M < decode_rows -> decode path
   int device = 0;
   int num_cu = 256;
   void* ws = nullptr;           // device workspace (split-K partials, MoE bucketing, the
@@ -57,6 +58,17 @@ int default_path() {
   if (!strcmp(p, "scratch")) return FC_GGUF_PATH_SCRATCH;
   if (!strcmp(p, "int8")) return FC_GGUF_PATH_INT8;
   return FC_GGUF_PATH_AUTO;
+}
+
+// AUTO's row threshold: FC_GGUF_DECODE_ROWS if it holds an integer in
+// [0, 2^20], else the page's 8.
+int default_decode_rows() {
+  const char* p = getenv("FC_GGUF_DECODE_ROWS");
+  if (!p || !*p) return 8;
+  char* end = nullptr;
+  const long v = strtol(p, &end, 10);
+  if (*end != '\0' || v < 0 || v > (1L << 20)) return 8;
+  return (int)v;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -103,6 +115,7 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
   h->qtype = qtype;
   h->expert_bytes = expert_bytes;
   h->path = default_path();
+  h->decode_rows = default_decode_rows();
   hipError_t e = hipGetDevice(&h->device);
   if (e == hipSuccess)
     e = hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device);
@@ -270,7 +283,8 @@ int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, v
   const int N = (int)h->N, K = (int)h->K;
   hipStream_t st = (hipStream_t)stream;
   int path = h->path;
-  if (path == FC_GGUF_PATH_AUTO) path = M < 8 ? FC_GGUF_PATH_DECODE : FC_GGUF_PATH_PREFILL;
+  if (path == FC_GGUF_PATH_AUTO)
+    path = M < h->decode_rows ? FC_GGUF_PATH_DECODE : FC_GGUF_PATH_PREFILL;
   const fcg::f16* a = (const fcg::f16*)A;
   const fcg::f16* r = (const fcg::f16*)R;
   fcg::f16* y = (fcg::f16*)Y;

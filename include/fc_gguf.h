@@ -62,7 +62,11 @@ typedef struct fc_gguf* fc_gguf_t;
 
 /* Path override (fc_gguf_set_path; default from env
    FC_GGUF_PATH=auto|decode|prefill|scratch|int8). */
-#define FC_GGUF_PATH_AUTO    0   /* M < 8 -> decode, else prefill */
+#define FC_GGUF_PATH_AUTO    0   /* M < D -> decode, else prefill; D = 8 (the page's row
+                                    threshold) unless the environment variable
+                                    FC_GGUF_DECODE_ROWS held another integer >= 0 when the
+                                    handle was created (on MI355X the prefill path is the
+                                    faster one from about 5 rows for most shapes) */
 #define FC_GGUF_PATH_DECODE  1   /* int8 GEMV for any M (rows taken in chunks of at most 7) */
 #define FC_GGUF_PATH_PREFILL 2   /* f16 matrix-core path for any M >= 1 */
 #define FC_GGUF_PATH_SCRATCH 3   /* comparison only: weights dequantised to an f16 buffer in the
@@ -121,7 +125,9 @@ int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, v
 int fc_gguf_run_f32(fc_gguf_t h, const float* A, int64_t M, const float* R, float* Y,
                     void* stream);
 
-/* Force a path (FC_GGUF_PATH_*); the testing switch of the FC primitive. */
+/* Force a path (FC_GGUF_PATH_*); the testing switch of the FC primitive.  The
+ * environment variable FC_GGUF_PATH (auto | decode | prefill | scratch | int8),
+ * read at create, sets a handle's initial path. */
 int fc_gguf_set_path(fc_gguf_t h, int path);
 
 /* Frees the handle and its device memory; NULL is accepted.  Synchronises the

@@ -130,3 +130,28 @@ def test_prefill_full_size_sampled(gpu_lib, qtype, shape, M):
     cols = np.unique(np.concatenate([cols, [0, N - 1]]))
     ref = ofc.fc_ref(A, okq.dequantize(w[cols], qtype), R[:, cols])
     assert relfro(y[:, cols], ref) <= PREFILL_TOL
+
+
+def test_auto_row_threshold_from_env(gpu_lib, monkeypatch):
+    # AUTO sends M < 8 rows to the decode path (the page's threshold) unless
+    # FC_GGUF_DECODE_ROWS, read when the handle is created, says otherwise
+    qtype, M, N, K = "q5_k", 6, 256, 1024
+    w, A, R = case(qtype, M, N, K, 91, 0)
+    monkeypatch.delenv("FC_GGUF_PATH", raising=False)
+    got = {}
+    for env in (None, "5", "junk"):
+        if env is None:
+            monkeypatch.delenv("FC_GGUF_DECODE_ROWS", raising=False)
+        else:
+            monkeypatch.setenv("FC_GGUF_DECODE_ROWS", env)
+        got[env] = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
+    monkeypatch.delenv("FC_GGUF_DECODE_ROWS", raising=False)
+    forced = {}
+    for p in ("decode", "prefill"):
+        f = _fc(w, qtype, N, K)
+        f.set_path(p)
+        forced[p] = _host(f(_dev(A), _dev(R)))
+    assert not np.array_equal(forced["decode"], forced["prefill"])
+    assert np.array_equal(got[None], forced["decode"])
+    assert np.array_equal(got["junk"], forced["decode"])
+    assert np.array_equal(got["5"], forced["prefill"])
