@@ -290,8 +290,9 @@ def main():
         traffic_summary(*args.traffic_summary)
         return
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU; the FC shards along N with no exchange "
-              "(see DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU (across GPUs the FC would shard along N, each GPU "
+              "computing its own output columns with no exchange); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
