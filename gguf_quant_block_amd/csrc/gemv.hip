@@ -87,7 +87,8 @@ __device__ __forceinline__ int qa_chunk(int m, int KBp, int kb, int t) {
 }
 
 // ------------------------------------------------ activation quantisation --
-// Per-32 int8 quantisatioakes the 32-value groups (tasks) tid, tid + nt, ...
+// Per-32 int8 quantisation of the activations: thread tid takes the 32-value
+// groups (tasks) tid, tid + nt, ...
 // The activation loads of the first qpre<AT>() rounds are issued before the
 // weight loads, so the quantisation waits only for them (loads complete in
 // order) while the weights are still in flight.
