@@ -218,6 +218,26 @@ def pmc_target(dev):
     print("pmc target done", flush=True)
 
 
+def pmc_prefill_target(dev):
+    """Counter-collection target for the prefill kernel: the Q5_K FC on
+    [8192, 2048] at M = 512 (one workgroup per CU, no split-K), ten eager
+    launches."""
+    import torch
+    from gguf_quant_block_amd import synth
+    from gguf_quant_block_amd.binding import FcGguf
+    N, K = synth.PREFILL_SHAPES[0]
+    M = 512
+    w = torch.from_numpy(synth.q5k_blocks(N, K, synth.rng(2, 0, synth.TAG_BLOCKS))).to(dev)
+    A = torch.from_numpy(synth.normal_f16((M, K), synth.rng(2, 0, synth.TAG_A))).to(dev)
+    R = torch.from_numpy(synth.normal_f16((M, N), synth.rng(2, 0, synth.TAG_R))).to(dev)
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    fc = FcGguf(N, K, "q5_k", w)
+    for _ in range(10):
+        fc(A, R, out=Y)
+    torch.cuda.synchronize()
+    print("pmc prefill target done", flush=True)
+
+
 CALIB_BYTES = 256 << 20
 
 
@@ -283,6 +303,9 @@ def main():
     ap.add_argument("--pmc-target", action="store_true",
                     help="run the decode sweep eagerly (4 shapes x 4 weight copies x 3 passes) and a "
                          "256 MiB device copy of known size, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--pmc-prefill-target", action="store_true",
+                    help="run the Q5_K [8192, 2048] prefill FC at M = 512 ten times eagerly, for "
+                         "rocprofv3 --pmc counter passes over the prefill kernel")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from the two counter passes over --pmc-target")
     args = ap.parse_args()
@@ -307,6 +330,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.pmc_target:
         pmc_target(dev)
+        return
+    if args.pmc_prefill_target:
+        pmc_prefill_target(dev)
         return
 
     # ---- decode workload: 32 layers x 4 FCs, Q5_K, M = 1, residual fused ----
