@@ -179,3 +179,24 @@ def test_moe_full_size_q6k(gpu_lib, which, a_per_slot):
     sample = np.unique(np.concatenate([hot, cold, g.choice(rest, size=min(8, rest.size), replace=False)]))
     assert hot.size >= 4
     _check_experts(y, w, "q6_k", A, ids, a_per_slot, sample)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_moe_random(gpu_lib, seed):
+    # seeded random grouped cases: expert count, shape, tokens, top_k, routing
+    # skew and row sharing drawn at random; every expert checked on its own
+    g = np.random.default_rng(5000 + seed)
+    qtype = QTYPES[g.integers(len(QTYPES))]
+    E = int(g.integers(1, 65))
+    N = int(g.integers(1, 600))
+    K = 256 * int(g.integers(1, 9))
+    T = int(g.integers(1, 160))
+    top_k = int(g.integers(1, min(E, 8) + 1))
+    a_per_slot = bool(g.integers(2))
+    s = float(g.uniform(0.0, 2.0))
+    w, A, ids = _moe_case(qtype, E, N, K, T, top_k, a_per_slot, 41, seed, s=s)
+    _, y = _run(w, qtype, A, ids, a_per_slot)
+    y = _host(y)
+    assert np.isfinite(y).all()
+    assert relfro(y, ofc.moe_ref(A, w, qtype, ids, a_per_slot)) <= PREFILL_TOL
+    _check_experts(y, w, qtype, A, ids, a_per_slot, np.unique(ids))
