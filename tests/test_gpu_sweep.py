@@ -1,8 +1,9 @@
-"""Seeded random sweep: qtype, N, K, M, path and residual drawn at random
-(N up to 1499, K up to 4096, M over the tile ladder's edges), each case
-checked against the oracle with its path's bar: the int8 emulation within
-1e-3 (max relative) for the decode and int8 paths, the fp64 FC within 2e-3
-(relative Frobenius) for the prefill path."""
+"""Seeded random sweep: qtype, N, K, M, path (with f32 activations as a
+path of its own) and residual drawn at random (N up to 1499, K up to 4096, M
+over the tile ladder's edges), each case checked against the oracle with its
+path's bar: the int8 emulation within 1e-3 (max relative) for the decode,
+f32 and int8 paths, the fp64 FC within 2e-3 (relative Frobenius) for the
+prefill and dequantise-once paths."""
 
 import numpy as np
 import pytest
@@ -13,29 +14,33 @@ from helpers import DECODE_TOL, PREFILL_TOL, case, maxrel, relfro
 pytestmark = pytest.mark.gpu
 
 MS = [1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 64, 100, 129, 200]
-PATHS = ["auto", "decode", "prefill", "int8"]
+PATHS = ["auto", "decode", "prefill", "int8", "scratch", "f32"]
 
 
 def _draw(seed):
     g = np.random.default_rng(seed)
     return (["q4_k", "q5_k", "q6_k"][g.integers(3)], int(g.integers(1, 1500)),
-            256 * int(g.integers(1, 17)), int(g.choice(MS)), PATHS[g.integers(4)],
+            256 * int(g.integers(1, 17)), int(g.choice(MS)), PATHS[g.integers(len(PATHS))],
             bool(g.integers(2)))
 
 
-@pytest.mark.parametrize("seed", range(100))
+@pytest.mark.parametrize("seed", range(120))
 def test_random_case(gpu_lib, seed):
     import torch
     from gguf_quant_block_amd.binding import FcGguf
     qtype, N, K, M, path, with_r = _draw(1000 + seed)
     w, A, R = case(qtype, M, N, K, 700, seed, with_r=with_r)
+    if path == "f32":
+        A = A.astype(np.float32)
+        R = None if R is None else R.astype(np.float32)
     f = FcGguf(N, K, qtype, w)
-    f.set_path(path)
+    if path != "f32":
+        f.set_path(path)
     y = f(torch.from_numpy(A).cuda(), None if R is None else torch.from_numpy(R).cuda())
     torch.cuda.synchronize()
     y = y.cpu().numpy()
     assert np.isfinite(y).all()
-    if path in ("decode", "int8") or (path == "auto" and M < 8):
+    if path in ("decode", "int8", "f32") or (path == "auto" and M < 8):
         assert maxrel(y, ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
     else:
         assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
