@@ -9,12 +9,14 @@
 // three stages, so two stages of loads are in flight while one computes, and
 // no register holds data in flight.
 //
-// Workgroup: 640 threads.  Waves 0-7 compute (wave w owns weight rows
-// 16w .. 16w+15 of the 128-row tile: two compute waves per SIMD, each reading
-// every activation operand of the stage, so the LDS reads double while each
-// weight is still decoded once; a lone wave issues VALU only about every 7
-// cycles, two per SIMD about every 4); wave 8 loads the activation tile,
-// wave 9 the weight pieces.  A stage is half a super-block (128 values of K).
+// Workgroup: 640 threads.  Eight compute waves (compute wave c owns weight
+// rows 16c .. 16c+15 of the 128-row tile: two compute waves per SIMD, each
+// reading every activation operand of the stage, so the LDS reads double
+// while each weight is still decoded once; a lone wave issues VALU only about
+// every 7 cycles, two per SIMD about every 4) and two loader waves, one for
+// the activation tile and one for the weight pieces.  The loaders are the
+// workgroup's first waves (dma_role), the oldest in issue arbitration.  A
+// stage is half a super-block (128 values of K).
 // LDS stage slot:
 //   A: BM rows x 16 chunks of 16 B; chunk c of row r sits at position
 //      c ^ (r & 15) of the row, so that the 16 rows of an MFMA operand read
@@ -91,6 +93,15 @@ __device__ __forceinline__ void compute_stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The role of this thread's wave: compute waves 0 .. DMA_CWAVES - 1, then the
+// activation loaders, then the weight loader.  Hardware waves 0 ..
+// DMA_ALOADERS are the loaders and hardware wave DMA_ALOADERS + 1 + c is
+// compute wave c, so that the loaders win issue arbitration (ties go to the
+// older wave) and their loads are never held behind the compute waves.
+__device__ __forceinline__ int dma_role() {
+  return ((int)(threadIdx.x >> 6) + DMA_CWAVES) % (DMA_CWAVES + DMA_ALOADERS + 1);
+}
+
 // stage t of the loop -> stage of K (rotated start, wrapping)
 __device__ __forceinline__ int dma_stage(int t, int s_begin, int nst, int rot) {
   int u = t + rot;
@@ -98,7 +109,7 @@ __device__ __forceinline__ int dma_stage(int t, int s_begin, int nst, int rot) {
   return s_begin + u;
 }
 
-// Loader wave DMA_CWAVES: the activation tile.  arow(r) points at the activation row
+// The activation loader (role DMA_CWAVES): the activation tile.  arow(r) points at the activation row
 // of tile row r (any valid row for rows past the tile's end).  Only the
 // first MTA halves are loaded.
 template <int QT, int MT, int MTA, class ARow>
@@ -140,7 +151,7 @@ __device__ __forceinline__ void dma_load_a(ARow arow, uint8_t* smem, int s_begin
   }
 }
 
-// Loader wave DMA_CWAVES + 1: the weight pieces of the tile's 128 rows (rows past N are
+// The weight loader (role DMA_CWAVES + 1): the weight pieces of the tile's 128 rows (rows past N are
 // clamped to N - 1: loaded, never stored).  In the tiled layout (IL) each
 // piece load of the wave is four contiguous 256-byte runs (16 rows each).
 // C: the slot layout (SLOT bytes per slot, the pieces at W_OFF, WP of them).
@@ -255,7 +266,7 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
   constexpr int NTW = DMA_NTW, KS = 4;        // k-steps per stage
   using C = DmaCfg<QT, MT>;
   using Dec = typename HalfDec<QT>::type;
-  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wn = dma_role();
   const int kq = lane >> 4;
   const int nst = s_end - s_begin;
   const int KB = K >> 8;

@@ -131,7 +131,7 @@ prefill_dma_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   const int nst = s_end - s_begin;
   // workgroups sharing activation or weight rows start at different stages
   const int rot = nst > 0 ? (nt + mt) % nst : 0;
-  const int wave = threadIdx.x >> 6;
+  const int wave = dma_role();
   if (wave >= DMA_CWAVES && wave < DMA_CWAVES + DMA_ALOADERS) {
     auto arow = [&](int r) {
       int m = m0 + r;
