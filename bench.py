@@ -238,6 +238,29 @@ def pmc_prefill_target(dev):
     print("pmc prefill target done", flush=True)
 
 
+def pmc_moe_target(dev):
+    """Counter-collection target for the grouped path: the benchmark's first
+    routing and weight copy, gate/up then down, three eager calls each."""
+    import torch
+    from gguf_quant_block_amd import synth
+    from gguf_quant_block_amd.binding import FcGguf
+    m = synth.MOE
+    E, T, top_k = m["E"], m["T"], m["top_k"]
+    ids = torch.from_numpy(synth.moe_routing(T, E, top_k, synth.rng(5, 0, synth.TAG_ROUTING),
+                                             s=m["zipf_s"])).to(dev)
+    for fi, (which, per_slot) in enumerate((("gate_up", False), ("down", True))):
+        N, K = m[which]
+        w = torch.from_numpy(synth.q6k_blocks(E * N, K, synth.rng(5, fi, synth.TAG_BLOCKS))).to(dev)
+        fc = FcGguf(N, K, "q6_k", w, experts=E)
+        shape = (T, top_k, K) if per_slot else (T, K)
+        A = torch.from_numpy(synth.normal_f16(shape, synth.rng(5, fi, synth.TAG_A))).to(dev)
+        Y = torch.empty((T, top_k, N), dtype=torch.float16, device=dev)
+        for _ in range(3):
+            fc.grouped(A, ids, per_slot, out=Y)
+        torch.cuda.synchronize()
+    print("pmc moe target done", flush=True)
+
+
 CALIB_BYTES = 256 << 20
 
 
@@ -306,6 +329,9 @@ def main():
     ap.add_argument("--pmc-prefill-target", action="store_true",
                     help="run the Q5_K [8192, 2048] prefill FC at M = 512 ten times eagerly, for "
                          "rocprofv3 --pmc counter passes over the prefill kernel")
+    ap.add_argument("--pmc-moe-target", action="store_true",
+                    help="run the benchmark's Q6_K grouped calls (gate/up, down) three times each "
+                         "eagerly, for rocprofv3 --pmc counter passes over the grouped kernel")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from the two counter passes over --pmc-target")
     args = ap.parse_args()
@@ -333,6 +359,9 @@ def main():
         return
     if args.pmc_prefill_target:
         pmc_prefill_target(dev)
+        return
+    if args.pmc_moe_target:
+        pmc_moe_target(dev)
         return
 
     # ---- decode workload: 32 layers x 4 FCs, Q5_K, M = 1, residual fused ----
