@@ -78,7 +78,7 @@ int ensure_ws(fc_gguf* h, size_t bytes) {
   if (h->ws) {
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(h, e);
-    hipFree(h->ws);
+    (void)hipFree(h->ws);
     h->ws = nullptr;
     h->ws_bytes = 0;
   }
@@ -143,10 +143,10 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
     e = fcg::launch_weight_layout(qtype, tiled, src + x * src_bytes,
                                   h->w + x * expert_bytes, (int)N, (int)K, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (staging) hipFree(staging);
+  if (staging) (void)hipFree(staging);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    hipFree(h->w);
+    (void)hipFree(h->w);
     delete h;
     return FC_GGUF_EHIP;
   }
@@ -252,11 +252,11 @@ int fc_gguf_destroy(fc_gguf_t h) {
   int cur = -1;
   const bool switched = hipGetDevice(&cur) == hipSuccess && cur != h->device &&
                         hipSetDevice(h->device) == hipSuccess;
-  hipDeviceSynchronize();
-  if (h->w) hipFree(h->w);
-  if (h->ws) hipFree(h->ws);
+  (void)hipDeviceSynchronize();                    // best effort: the handle goes anyway
+  if (h->w) (void)hipFree(h->w);
+  if (h->ws) (void)hipFree(h->ws);
   if (h->blas) rocblas_destroy_handle(h->blas);
-  if (switched) hipSetDevice(cur);
+  if (switched) (void)hipSetDevice(cur);
   delete h;
   return FC_GGUF_OK;
 }

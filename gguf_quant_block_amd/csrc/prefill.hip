@@ -90,8 +90,7 @@ prefill_kernel(const uint8_t* W, const f16* A, const f16* __restrict__ R,
   if (s_end > S_total) s_end = S_total;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int kq = lane >> 4;
+  const int wave = tid >> 6;
 
   TileRows<MT> rows;
 #pragma unroll

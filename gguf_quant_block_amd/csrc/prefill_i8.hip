@@ -234,6 +234,7 @@ template <> struct I8Dec<QT_Q4K> { using type = Q45I8; };
 template <int QT, int MT>
 __device__ __forceinline__ void i8_compute(int N, int K, int n0, const uint8_t* smem, int s_begin,
                                            int s_end, int rot, floatx4 (&acc)[MT][I8_NTW]) {
+  (void)K;                                          // stages are counted by the caller
   constexpr int NTW = I8_NTW, BM = 16 * MT;
   using C = I8Cfg<QT, MT>;
   using Dec = typename I8Dec<QT>::type;
