@@ -1,8 +1,10 @@
-"""Build the HIP library libfcgguf.so in-tree for gfx950 (hipcc).
+"""Build the HIP libraries in-tree for gfx950 (hipcc).
 
 Usage: python -m gguf_quant_block_amd.build [--jobs N]
-Each translation unit under csrc/ is compiled to an object in _build/ and the
-objects are linked into gguf_quant_block_amd/libfcgguf.so.  Always rebuilds.
+Each translation unit under csrc/ is compiled to an object in _build/; the FC
+library's objects are linked into gguf_quant_block_amd/libfcgguf.so, and the
+benchmark's ceiling kernels (csrc/ceilings.hip) into libfcgceil.so.  Always
+rebuilds.
 """
 
 from __future__ import annotations
@@ -19,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfcgguf.so")
+CEIL_LIB = os.path.join(PKG, "libfcgceil.so")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -31,6 +34,7 @@ CFLAGS = [
 ]
 SOURCES = ["fc_gguf_api.cpp", "layout.hip", "gemv.hip", "prefill.hip", "prefill_i8.hip", "moe.hip",
            "dequant.hip"]
+CEIL_SOURCES = ["ceilings.hip"]
 
 
 def _compile(src: str) -> str:
@@ -45,21 +49,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, 8))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    # rocBLAS serves only the dequantise-once comparison path
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
-           "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+def _link(objs, out, libs):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, *libs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(out)} failed")
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 4, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, 8))) as ex:
+        objs = list(ex.map(_compile, SOURCES + CEIL_SOURCES))
+    n = len(SOURCES)
+    # rocBLAS serves only the dequantise-once comparison path
+    _link(objs[:n], LIB, ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"])
+    _link(objs[n:], CEIL_LIB, [])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEIL_LIB}")
     return LIB
 
 

@@ -26,7 +26,7 @@ __device__ __forceinline__ uint64_t ld8(const uint8_t* p) { return *(const uint6
 template <int QT>
 __global__ void __launch_bounds__(256)
 dequant_f16_kernel(const uint8_t* __restrict__ W, f16* __restrict__ out, int N, int K) {
-  const WMap<true> L(N, K);
+  const WMap L(N, K);
   const int KB = L.KB;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long long)N * KB * 32) return;

@@ -22,6 +22,7 @@ struct fc_gguf {
   size_t expert_bytes = 0;      // bytes of one [N, K] matrix
   int path = FC_GGUF_PATH_AUTO;
   int decode_rows = 8;                // AUTO: M < decode_rows -> decode path
+  int prefill_kernel = 0;             // fcg::PREFILL_KERNEL_*: which prefill kernel
   int device = 0;
   int num_cu = 256;
   void* ws = nullptr;           // device workspace (split-K partials, MoE bucketing, the
@@ -71,18 +72,42 @@ int default_decode_rows() {
   return (int)v;
 }
 
+// FC_GGUF_PREFILL_KERNEL=dma|lds forces one of the two prefill kernels at
+// every row count (testing); anything else leaves the choice to the row count.
+int default_prefill_kernel() {
+  const char* p = getenv("FC_GGUF_PREFILL_KERNEL");
+  if (p && !strcmp(p, "dma")) return fcg::PREFILL_KERNEL_DMA;
+  if (p && !strcmp(p, "lds")) return fcg::PREFILL_KERNEL_LDS;
+  return fcg::PREFILL_KERNEL_AUTO;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int ensure_ws(fc_gguf* h, size_t bytes) {
+// FC_GGUF_TEST_FAIL_ALLOC names allocations that fail on purpose, so that
+// tests can reach the FC_GGUF_ENOMEM paths: "create" (the weights of a new
+// handle), "workspace" (growing a handle's workspace) or "all".  Read at
+// every allocation.
+bool fail_alloc(const char* what) {
+  const char* p = getenv("FC_GGUF_TEST_FAIL_ALLOC");
+  if (!p || !*p) return false;
+  return !strcmp(p, "all") || !strcmp(p, what);
+}
+
+// Grow the handle's workspace to `bytes` on the call's stream.  The old
+// buffer is released and the new one taken from the device's stream-ordered
+// pool (hipFreeAsync / hipMallocAsync on `st`), so the growth waits only for
+// the work already queued on that stream (the last user of the old buffer:
+// a handle is never run on two streams at once) and no other stream stalls.
+int ensure_ws(fc_gguf* h, size_t bytes, hipStream_t st) {
   if (bytes <= h->ws_bytes) return FC_GGUF_OK;
+  if (fail_alloc("workspace")) return FC_GGUF_ENOMEM;
   if (h->ws) {
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return hip_fail(h, e);
-    (void)hipFree(h->ws);
+    const hipError_t e = hipFreeAsync(h->ws, st);
     h->ws = nullptr;
     h->ws_bytes = 0;
+    if (e != hipSuccess) return hip_fail(h, e);
   }
-  hipError_t e = hipMalloc(&h->ws, bytes);
+  hipError_t e = hipMallocAsync(&h->ws, bytes, st);
   if (e != hipSuccess) {
     h->ws = nullptr;
     h->last = e;
@@ -104,8 +129,7 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
   if (nblk > ((size_t)1 << 31) / 256) return FC_GGUF_ERANGE;
   const size_t src_bytes = nblk * (size_t)bb;                        // one canonical matrix
   // one device matrix in the tiled layout (grouped handles: one per expert)
-  const bool tiled = grouped == 0 || fcg::GROUPED_TILED;
-  const size_t expert_bytes = fcg::layout_bytes(qtype, tiled, (int)N, (int)K);
+  const size_t expert_bytes = fcg::layout_bytes(qtype, (int)N, (int)K);
 
   fc_gguf* h = new (std::nothrow) fc_gguf();
   if (!h) return FC_GGUF_ENOMEM;
@@ -116,6 +140,7 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
   h->expert_bytes = expert_bytes;
   h->path = default_path();
   h->decode_rows = default_decode_rows();
+  h->prefill_kernel = default_prefill_kernel();
   hipError_t e = hipGetDevice(&h->device);
   if (e == hipSuccess)
     e = hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device);
@@ -124,7 +149,7 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
     return FC_GGUF_EHIP;
   }
   const size_t total = expert_bytes * (size_t)E;
-  e = hipMalloc(&h->w, total);
+  e = fail_alloc("create") ? hipErrorOutOfMemory : hipMalloc(&h->w, total);
   if (e != hipSuccess) {
     delete h;
     return FC_GGUF_ENOMEM;
@@ -140,7 +165,7 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
     src = staging;
   }
   for (int64_t x = 0; e == hipSuccess && x < E; ++x)
-    e = fcg::launch_weight_layout(qtype, tiled, src + x * src_bytes,
+    e = fcg::launch_weight_layout(qtype, src + x * src_bytes,
                                   h->w + x * expert_bytes, (int)N, (int)K, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (staging) (void)hipFree(staging);
@@ -161,7 +186,7 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
 int run_scratch(fc_gguf* h, const fcg::f16* a, const fcg::f16* r, fcg::f16* y, int64_t M,
                 hipStream_t st) {
   const int N = (int)h->N, K = (int)h->K;
-  int rc = ensure_ws(h, (size_t)N * K * sizeof(fcg::f16));
+  int rc = ensure_ws(h, (size_t)N * K * sizeof(fcg::f16), st);
   if (rc != FC_GGUF_OK) return rc;
   if (!h->blas && rocblas_create_handle(&h->blas) != rocblas_status_success) {
     h->blas = nullptr;
@@ -254,7 +279,10 @@ int fc_gguf_destroy(fc_gguf_t h) {
                         hipSetDevice(h->device) == hipSuccess;
   (void)hipDeviceSynchronize();                    // best effort: the handle goes anyway
   if (h->w) (void)hipFree(h->w);
-  if (h->ws) (void)hipFree(h->ws);
+  if (h->ws) {                                     // from the stream-ordered pool
+    (void)hipFreeAsync(h->ws, nullptr);
+    (void)hipStreamSynchronize(nullptr);
+  }
   if (h->blas) rocblas_destroy_handle(h->blas);
   if (switched) (void)hipSetDevice(cur);
   delete h;
@@ -297,19 +325,18 @@ int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, v
   } else if (path == FC_GGUF_PATH_INT8) {
     int mt, nt, splits;
     fcg::prefill_choose(h->qtype, (int)M, N, K, h->num_cu, &mt, &nt, &splits);
-    rc = ensure_ws(h, fcg::prefill_i8_workspace_bytes((int)M, N, K, splits));
+    rc = ensure_ws(h, fcg::prefill_i8_workspace_bytes((int)M, N, K, splits), st);
     if (rc != FC_GGUF_OK) return rc;
     e = fcg::launch_prefill_i8(h->qtype, h->w, a, r, y, h->ws, (int)M, N, K, mt, splits, st);
   } else {
-    int mt, nt, splits;
-    fcg::prefill_choose(h->qtype, (int)M, N, K, h->num_cu, &mt, &nt, &splits);
-    const size_t need = fcg::prefill_workspace_bytes((int)M, N, splits);
+    const fcg::PrefillPlan plan = fcg::prefill_plan(h->qtype, (int)M, N, K, h->num_cu,
+                                                    h->prefill_kernel);
+    const size_t need = fcg::prefill_workspace_bytes((int)M, N, plan.splits);
     if (need) {
-      rc = ensure_ws(h, need);
+      rc = ensure_ws(h, need, st);
       if (rc != FC_GGUF_OK) return rc;
     }
-    e = fcg::launch_prefill(h->qtype, h->w, a, r, y, (float*)h->ws, (int)M, N, K, mt, nt, splits,
-                            st);
+    e = fcg::launch_prefill(plan, h->qtype, h->w, a, r, y, (float*)h->ws, (int)M, N, K, st);
   }
   if (e != hipSuccess) return hip_fail(h, e);
   return FC_GGUF_OK;
@@ -337,7 +364,7 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, c
     return FC_GGUF_ERANGE;
   if (!aligned(A, 16) || !aligned(Y, 8) || !aligned(ids, 4)) return FC_GGUF_EINVAL;
   const size_t need = fcg::moe_workspace_bytes((int)h->E, (int)T, top_k);
-  const int rc = ensure_ws(h, need);
+  const int rc = ensure_ws(h, need, (hipStream_t)stream);
   if (rc != FC_GGUF_OK) return rc;
   hipError_t e = fcg::launch_moe(h->qtype, h->w, h->expert_bytes, (int)h->E, (int)h->N, (int)h->K,
                                  (const fcg::f16*)A, (int)T, a_per_slot, ids, top_k, (fcg::f16*)Y,

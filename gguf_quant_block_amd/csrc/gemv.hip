@@ -53,19 +53,11 @@ struct GemvLayout {
   size_t rec, part, total;
 };
 
-#ifndef FCG_GEMV_RT
-#define FCG_GEMV_RT 1
-#endif
-// Row tiles per workgroup and waves per row tile for K: one wave per 4-block
-// tile of a row tile, at most 8 waves in all.
-__host__ __device__ inline int gemv_rt(int K) {
-  (void)K;
-  return FCG_GEMV_RT;
-}
+// Waves per workgroup (one row tile) for K: one wave per 4-block tile of the
+// row tile, at most 8.
 __host__ __device__ inline int gemv_waves(int K) {
-  const int g = tiled_kb(K / QK) / TILE_KB, rt = gemv_rt(K);
-  const int per = g < GEMV_MAX_WAVES / rt ? g : GEMV_MAX_WAVES / rt;
-  return per * rt;
+  const int g = tiled_kb(K / QK) / TILE_KB;
+  return g < GEMV_MAX_WAVES ? g : GEMV_MAX_WAVES;
 }
 
 // LDS: qa int8 [MR][KBp] records of QA_REC bytes (256 codes + 16 bytes of
@@ -321,7 +313,7 @@ struct GemvBlock {
 #define FCG_KEEP_ORDER() asm volatile("" ::: "memory")
 
 template <int QT>
-__device__ __forceinline__ void load_block(const uint8_t* W, const WMap<true>& L, int n, int kb,
+__device__ __forceinline__ void load_block(const uint8_t* W, const WMap& L, int n, int kb,
                                            GemvBlock& b) {
   if constexpr (QT != QT_Q6K) {
     constexpr int P = block_bytes_of(QT) / 16;
@@ -364,28 +356,26 @@ __device__ __forceinline__ void barrier_after_lds_writes() {
   asm volatile("" ::: "memory");
 }
 
-// Workgroup = RT row tiles (16 weight rows each), nw = RT * per waves: wave
-// w works on row tile w % RT, on its tiles w / RT, w / RT + per, ...  Each
-// thread issues its activation loads, then the loads of its lane's first
+// Workgroup = one row tile (16 weight rows), nw waves: wave w works on its
+// tiles w, w + nw, ...  Each thread issues its activation loads, then the loads of its lane's first
 // block, quantises its activation groups into LDS (waiting only for the
 // activation loads) and meets the others at the barrier; the weights arrive
 // while this happens.  AT: the type of A, R and Y (f16, or f32 for f32
 // activations).
 template <int QT, int MR, class AT>
 __global__ void __launch_bounds__(GEMV_MAX_THREADS)
-gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R,
-            AT* __restrict__ Y, int N, int K, int RT) {
+gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
+            AT* Y, int N, int K) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const WMap<true> L(N, K);
+  const WMap L(N, K);
   const int KB = L.KB, KBp = L.KBp;
   const int G = KBp / TILE_KB;                        // tiles of a row tile
-  const int nt = blockDim.x, nw = nt >> 6, per = nw / RT;
+  const int nt = blockDim.x, nw = nt >> 6;
   const GemvLayout Ly = gemv_layout<QT>(MR, KBp, nw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rt = wave % RT, g0 = wave / RT;
+  const int g0 = wave;
   const int r = lane % TILE_ROWS, kbq = lane / TILE_ROWS;
-  const int n = (blockIdx.x * RT + rt) * TILE_ROWS + r;   // < tiled_rows(N) when the
-                                                         // row tile exists
+  const int n = blockIdx.x * TILE_ROWS + r;           // < tiled_rows(N)
   uint32_t* rec = (uint32_t*)(smem + Ly.rec);
   float* part_lds = (float*)(smem + Ly.part);
 
@@ -403,12 +393,9 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R
   }
   asm volatile("" ::: "memory");                    // activation and residual loads first
 
-  // the row tile exists unless it is past the last one (a partial workgroup)
-  const bool live = n < tiled_rows(N);
-  const int nl = live ? n : r;                        // row 0's tile stands in
   // the lane's first block (waves without a tile re-read tile 0; never used)
   GemvBlock blk;
-  load_block<QT>(W, L, nl, (g0 < G ? g0 : 0) * TILE_KB + kbq, blk);
+  load_block<QT>(W, L, n, (g0 < G ? g0 : 0) * TILE_KB + kbq, blk);
   asm volatile("" ::: "memory");                    // ... then the weight loads
 
   quant_finish<QT, MR, AT>(A, K, KBp, smem, rec, tid, nt, araw);
@@ -417,9 +404,9 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R
   float part[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) part[m] = 0.f;
-  for (int g = g0; g < G; g += per) {
+  for (int g = g0; g < G; g += nw) {
     const int kb = g * TILE_KB + kbq;
-    if (g != g0) load_block<QT>(W, L, nl, kb, blk);
+    if (g != g0) load_block<QT>(W, L, n, kb, blk);
     if (kb < KB) {
       if constexpr (QT == QT_Q6K)
         q6k_block<MR>(blk.w, blk.w + 32, blk.scv, blk.dbits, kb, KBp, smem, rec, part);
@@ -427,8 +414,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R
         q45k_block<QT, MR>(blk.w, kb, KBp, smem, rec, part);
     }
   }
-  // row sums: the four lanes of a row (kbq = 0..3), then the waves of the
-  // row tile in order
+  // row sums: the four lanes of a row (kbq = 0..3), then the waves in order
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     part[m] += __shfl_xor(part[m], 16, 64);
@@ -439,11 +425,11 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* __restrict__ R
     for (int m = 0; m < MR; ++m) part_lds[(wave * MR + m) * TILE_ROWS + lane] = part[m];
   }
   __syncthreads();
-  if (wave < RT && lane < TILE_ROWS && n < N) {
+  if (wave == 0 && lane < TILE_ROWS && n < N) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       float y = 0.f;
-      for (int w = wave; w < nw; w += RT) y += part_lds[(w * MR + m) * TILE_ROWS + lane];
+      for (int w = 0; w < nw; ++w) y += part_lds[(w * MR + m) * TILE_ROWS + lane];
       if (R) y += (float)rres[m];
       Y[(size_t)m * N + n] = (AT)y;
     }
@@ -465,9 +451,8 @@ static hipError_t launch_gemv_t(const uint8_t* W, const AT* A, const AT* R, AT* 
     hipError_t e = raise_lds_limit((const void*)kern, 160 * 1024, lds_raised);
     if (e != hipSuccess) return e;
   }
-  const int rt = gemv_rt(K);
-  const int grid = (tiled_rows(N) / TILE_ROWS + rt - 1) / rt;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), lds, st, W, A, R, Y, N, K, rt);
+  const int grid = tiled_rows(N) / TILE_ROWS;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), lds, st, W, A, R, Y, N, K);
   return hipGetLastError();
 }
 
@@ -560,7 +545,7 @@ __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_
   const long long gb = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gb >= (long long)N * KB) return;
   const int n = (int)(gb / KB), kb = (int)(gb % KB);
-  const WMap<true> L(N, K);
+  const WMap L(N, K);
   const uint4 ones = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
   if constexpr (QT != QT_Q6K) {
     constexpr int P = block_bytes_of(QT) / 16;

@@ -25,10 +25,10 @@ inline hipError_t raise_lds_limit(const void* kern, int bytes, std::atomic<uint6
   return e;
 }
 
-// canonical AoS blocks of an [N, K] matrix -> a device layout of layout.h,
-// tiled or canonical (the destination holds layout_bytes(...) bytes)
-size_t layout_bytes(int qtype, bool tiled, int N, int K);
-hipError_t launch_weight_layout(int qtype, bool tiled, const uint8_t* src, uint8_t* dst, int N, int K,
+// canonical AoS blocks of an [N, K] matrix -> the tiled device layout of
+// layout.h (the destination holds layout_bytes(...) bytes)
+size_t layout_bytes(int qtype, int N, int K);
+hipError_t launch_weight_layout(int qtype, const uint8_t* src, uint8_t* dst, int N, int K,
                                 hipStream_t st);
 
 // decode path (M in 1..7); A, R, Y all f16, or all f32
@@ -46,11 +46,26 @@ hipError_t launch_debug_int_dots(int qtype, const uint8_t* W, const int8_t* qa, 
 // dequantise-once comparison path: tiled weights -> row-major f16 W16[N, K]
 hipError_t launch_dequant_f16(int qtype, const uint8_t* W, f16* out, int N, int K, hipStream_t st);
 
-// prefill path
+// prefill path: two kernels, the loader-wave tile (16 .. 128 activation rows,
+// weights decoded in the compute waves' registers) and the decode-once tile
+// (128 x 128, weights decoded once into an f16 LDS tile by producer waves);
+// AUTO takes the loader-wave tile at every row count (the faster one on the
+// benchmark shapes), the decode-once tile is forced with
+// FC_GGUF_PREFILL_KERNEL=lds
+constexpr int PREFILL_KERNEL_AUTO = 0;
+constexpr int PREFILL_KERNEL_DMA = 1;
+constexpr int PREFILL_KERNEL_LDS = 2;
+struct PrefillPlan {
+  int kind;       // PREFILL_KERNEL_DMA or PREFILL_KERNEL_LDS
+  int mt;         // activation rows per tile / 16
+  int splits;     // K splits (f32 partials + reduction when > 1)
+  int sb_per;     // super-blocks per split (decode-once tile)
+};
 void prefill_choose(int qtype, int M, int N, int K, int num_cu, int* mt, int* nt, int* splits);
+PrefillPlan prefill_plan(int qtype, int M, int N, int K, int num_cu, int kernel);
 size_t prefill_workspace_bytes(int M, int N, int splits);
-hipError_t launch_prefill(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, float* P,
-                          int M, int N, int K, int mt, int nt, int splits, hipStream_t st);
+hipError_t launch_prefill(const PrefillPlan& p, int qtype, const uint8_t* W, const f16* A,
+                          const f16* R, f16* Y, float* P, int M, int N, int K, hipStream_t st);
 // Y = sum over splits of P[split][M*N] + R, one f16 rounding
 hipError_t launch_splitk_reduce(const float* P, const f16* R, f16* Y, long long MN, int splits,
                                 hipStream_t st);
@@ -62,7 +77,6 @@ hipError_t launch_prefill_i8(int qtype, const uint8_t* W, const f16* A, const f1
                              void* ws, int M, int N, int K, int mt, int splits, hipStream_t st);
 
 // grouped (MoE) path
-constexpr bool GROUPED_TILED = true;   // grouped handles use the tiled layout, per expert
 constexpr int MOE_MAX_E = 4096;   // experts per grouped handle (bucketing counts live in LDS)
 size_t moe_workspace_bytes(int E, int T, int top_k);
 hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, int N, int K,

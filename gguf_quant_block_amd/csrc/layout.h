@@ -20,11 +20,6 @@
 //   Q6_K: the QL | QH | SC | D planes of OpenVINO PR #39119 (section
 //         Transformation), each over the padded block count: QL P = 8,
 //         QH P = 4, SC P = 1; D holds 2 bytes per block at t * 128 + l * 2.
-//
-// Canonical layout (an option of the layout transform and of the
-// register-staged tile; no handle stores it): blocks
-// b = n * (K/256) + kb in order, padded to a multiple of 64 blocks; Q4_K /
-// Q5_K blocks as in the file, Q6_K as the four planes in block order.
 #pragma once
 
 #include <stddef.h>
@@ -32,34 +27,24 @@
 
 namespace fcg {
 
-constexpr int LAYOUT_GROUP = 64;
 constexpr int TILE_ROWS = 16;      // rows per tile
 constexpr int TILE_KB = 4;         // blocks per row per tile
 
-__host__ __device__ inline size_t padded_blocks(size_t nblk) {
-  return (nblk + LAYOUT_GROUP - 1) / LAYOUT_GROUP * LAYOUT_GROUP;
-}
 __host__ __device__ inline int tiled_rows(int N) { return (N + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS; }
 __host__ __device__ inline int tiled_kb(int KB) { return (KB + TILE_KB - 1) / TILE_KB * TILE_KB; }
 
-// Addressing of one [N, K] matrix in the tiled (TILED) or canonical layout.
-template <bool TILED>
+// Addressing of one [N, K] matrix in the tiled layout.
 struct WMap {
   int KB;        // blocks per row
-  int KBp;       // blocks per row as stored (padded to TILE_KB when tiled)
+  int KBp;       // blocks per row as stored (padded to TILE_KB)
   size_t nbt;    // blocks per plane, padding included
 
   __host__ __device__ WMap(int N, int K) {
     KB = K >> 8;
-    if constexpr (TILED) {
-      KBp = tiled_kb(KB);
-      nbt = (size_t)tiled_rows(N) * KBp;
-    } else {
-      KBp = KB;
-      nbt = padded_blocks((size_t)N * KB);
-    }
+    KBp = tiled_kb(KB);
+    nbt = (size_t)tiled_rows(N) * KBp;
   }
-  // tile index and position inside the tile of block (n, kb) (tiled layout)
+  // tile index and position inside the tile of block (n, kb)
   __host__ __device__ size_t tile(int n, int kb) const {
     return (size_t)(n / TILE_ROWS) * (KBp / TILE_KB) + kb / TILE_KB;
   }
@@ -68,8 +53,7 @@ struct WMap {
   }
   // byte offset of 16-byte piece p of block (n, kb) in a plane of P pieces per block
   __host__ __device__ size_t piece(int n, int kb, int P, int p) const {
-    if constexpr (TILED) return ((tile(n, kb) * P + p) << 10) + ((size_t)slot(n, kb) << 4);
-    else return ((size_t)n * KB + kb) * (size_t)(16 * P) + (size_t)(16 * p);
+    return ((tile(n, kb) * P + p) << 10) + ((size_t)slot(n, kb) << 4);
   }
   // Q6_K planes
   __host__ __device__ size_t qh_base() const { return 128 * nbt; }
@@ -77,8 +61,7 @@ struct WMap {
   __host__ __device__ size_t d_base() const { return 208 * nbt; }
   __host__ __device__ size_t sc(int n, int kb) const { return sc_base() + piece(n, kb, 1, 0); }
   __host__ __device__ size_t d(int n, int kb) const {
-    if constexpr (TILED) return d_base() + tile(n, kb) * 128 + (size_t)slot(n, kb) * 2;
-    else return d_base() + ((size_t)n * KB + kb) * 2;
+    return d_base() + tile(n, kb) * 128 + (size_t)slot(n, kb) * 2;
   }
 };
 

@@ -38,14 +38,8 @@
 
 namespace fcg {
 
-#ifndef FCG_DMA_SLOTS
-#define FCG_DMA_SLOTS 3
-#endif
-#ifndef FCG_DMA_ALOADERS
-#define FCG_DMA_ALOADERS 1
-#endif
-constexpr int DMA_SLOTS = FCG_DMA_SLOTS;          // LDS ring depth (stages)
-constexpr int DMA_ALOADERS = FCG_DMA_ALOADERS;    // waves loading the activation tile
+constexpr int DMA_SLOTS = 3;                      // LDS ring depth (stages)
+constexpr int DMA_ALOADERS = 1;                   // waves loading the activation tile
 constexpr int DMA_CWAVES = 8;                    // compute waves
 constexpr int DMA_NTW = 8 / DMA_CWAVES;           // 16-row weight sub-tiles per compute wave
 constexpr int DMA_THREADS = 64 * (DMA_CWAVES + DMA_ALOADERS + 1);
@@ -152,16 +146,16 @@ __device__ __forceinline__ void dma_load_a(ARow arow, uint8_t* smem, int s_begin
 }
 
 // The weight loader (role DMA_CWAVES + 1): the weight pieces of the tile's 128 rows (rows past N are
-// clamped to N - 1: loaded, never stored).  In the tiled layout (IL) each
-// piece load of the wave is four contiguous 256-byte runs (16 rows each).
+// clamped to N - 1: loaded, never stored).  In the tiled layout each piece
+// load of the wave is four contiguous 256-byte runs (16 rows each).
 // C: the slot layout (SLOT bytes per slot, the pieces at W_OFF, WP of them).
-template <int QT, int MT, bool IL, class C = DmaCfg<QT, MT>>
+template <int QT, int MT, class C = DmaCfg<QT, MT>>
 __device__ __forceinline__ void dma_load_w(const uint8_t* W, int N, int K, int n0, uint8_t* smem,
                                            int s_begin, int s_end, int rot) {
   constexpr int NI = 2 * C::WP + (QT == QT_Q6K ? 2 : 0);
   const int lane = threadIdx.x & 63;
   const int nst = s_end - s_begin;
-  const WMap<IL> L(N, K);
+  const WMap L(N, K);
   int rn[2];                                        // the lane's two rows
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -215,16 +209,15 @@ template <> struct HalfDec<QT_Q4K> { using type = Q45Half<false>; };
 // stage's slot: W0 the lane's row (weight sub-tile 0) in piece 0, W1 that row
 // plus the lane's sub-block within a piece (k-quarter kq: piece pair kq / 2,
 // half kq & 1), W2 the aligned Q6_K d word of that row.  Sub-tile j lies 16
-// rows further on.  IL: the weights are in the tiled layout (selects which
-// half of a Q6_K d word is the row's).
-template <int QT, int MT, bool IL>
+// rows further on.
+template <int QT, int MT>
 __device__ __forceinline__ void dma_dec_init(typename HalfDec<QT>::type (&h)[DMA_NTW],
                                              const uint8_t* W0, const uint8_t* W1,
                                              const uint8_t* W2, const int (&rn)[DMA_NTW], int s,
-                                             int KB, int kq) {
+                                             int kq) {
   using C = DmaCfg<QT, MT>;
   constexpr int PB = C::BN * 16;                    // bytes of one piece over the tile's rows
-  const int hb = s & 1, kb = s >> 1;
+  const int hb = s & 1;
 #pragma unroll
   for (int j = 0; j < DMA_NTW; ++j) {
     const uint8_t* p0 = W0 + 256 * j;
@@ -237,9 +230,8 @@ __device__ __forceinline__ void dma_dec_init(typename HalfDec<QT>::type (&h)[DMA
                 uint2{0u, 0u}, hb);
     } else {
       const uint32_t dw = *(const uint32_t*)(W2 + 64 * j);
-      // the row's half of the word: tiled, the blocks of rows n and n ^ 1
-      // share it; canonical, the blocks b and b ^ 1
-      const int half = IL ? (rn[j] & 1) : (int)(((size_t)rn[j] * KB + kb) & 1);
+      // the row's half of the word: the blocks of rows n and n ^ 1 share it
+      const int half = rn[j] & 1;
       h[j].init(*(const uint2*)p1, *(const uint2*)(p1 + 2 * PB), *(const uint2*)(p1 + 4 * PB),
                 *(const uint2*)(p0 + 6 * PB + 8 * hb), dw >> (16 * half), kq);
     }
@@ -260,7 +252,7 @@ __device__ __forceinline__ void dma_dec_init(typename HalfDec<QT>::type (&h)[DMA
 // a slot whose contents are never used.)  Each k-step is one scheduling
 // region: its LDS reads first, then each MFMA followed by a few VALU
 // instructions.
-template <int QT, int MT, int MTA, bool IL>
+template <int QT, int MT, int MTA>
 __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t* smem, int s_begin,
                                             int s_end, int rot, floatx4 (&acc)[MT][DMA_NTW]) {
   constexpr int NTW = DMA_NTW, KS = 4;        // k-steps per stage
@@ -269,7 +261,6 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
   const int lane = threadIdx.x & 63, wn = dma_role();
   const int kq = lane >> 4;
   const int nst = s_end - s_begin;
-  const int KB = K >> 8;
   int nloc[NTW], rn[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
@@ -311,8 +302,8 @@ __device__ __forceinline__ void dma_compute(int N, int K, int n0, const uint8_t*
     for (int i = 0; i < MTA; ++i) af[i] = *(const half8v*)(As + la[g] + 4096 * i);
   };
   auto dec_init = [&](Dec (&hh)[NTW], const uint8_t* Ss, int t) {
-    dma_dec_init<QT, MT, IL>(hh, Ss + lw0, Ss + lw1, Ss + lw2, rn,
-                             dma_stage(t, s_begin, nst, rot), KB, kq);
+    dma_dec_init<QT, MT>(hh, Ss + lw0, Ss + lw1, Ss + lw2, rn,
+                             dma_stage(t, s_begin, nst, rot), kq);
   };
 
   stage_barrier();                                  // stage 0 has landed

@@ -214,15 +214,14 @@ struct TileRows {
 // Main loop of one tile over the stages [s_begin, s_end) of K, walked from
 // stage s_begin + rot (wrapping), for the first MTA (<= MT) 16-row halves of
 // the tile.  W is one weight matrix [N, K] in the tiled device layout of
-// layout.h (IL) or in the canonical one (Q4_K / Q5_K blocks in order; Q6_K
-// row-major QL | QH | SC | D planes).  n0 is its
+// layout.h.  n0 is its
 // first weight row (rows past N are clamped to N - 1: loaded, never stored).
 // acc[i][j] receives C[n][m] of the 16x16 sub-tile (half i < MTA, weight
 // sub-tile j).  A stage is SH half super-blocks (128*SH values of K; stages
 // are numbered in those units).  PD = 1: the next stage's loads are in flight
 // while a stage computes; PD = 2: the next two stages' (three register sets).
 // The loop body has no data-dependent branches.
-template <int QT, int MT, int NT, int MTA, bool IL, int PD, int SH = 1>
+template <int QT, int MT, int NT, int MTA, int PD, int SH = 1>
 __device__ __forceinline__ void tile_mainloop(const uint8_t* W, int N,
                                               int K, int n0, int s_begin, int s_end, int rot,
                                               const TileRows<MT>& rows,
@@ -244,7 +243,7 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, int N,
     nrow[j] = n < N ? n : N - 1;
   }
 
-  const WMap<IL> L(N, K);
+  const WMap L(N, K);
   // raw bytes of the lane's rows for stage s (half-block hb of block kb):
   // 8-byte slices of the 16-byte pieces
   auto load_raw_q5 = [&](int s, RawQ5* raw) {
@@ -420,9 +419,41 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, int N,
   }
 }
 
+// The residual of one lane's 4 consecutive outputs n .. n + 3 of a row r
+// (packed f16; zeros past N).  An epilogue loads all of a lane's residuals
+// before its first store: Y may be R (in-place residual), so the compiler
+// cannot move a residual load above an earlier store, and one load / wait /
+// store round trip per output group would serialise the epilogue on memory
+// latency.  Every output element belongs to one lane, which reads its
+// residual before writing it, so the early loads are exact even in place.
+__device__ __forceinline__ uint2 load4_r(const f16* r, int n, int N) {
+  if (n + 3 < N && ((N & 3) == 0)) return *(const uint2*)(r + n);
+  uint16_t h[4] = {0, 0, 0, 0};
+  for (int q = 0; q < 4 && n + q < N; ++q) h[q] = __builtin_bit_cast(uint16_t, r[n + q]);
+  return make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+}
+
+// f16 store of one lane's 4 consecutive outputs v + (the residual rr, if
+// has_r) of row y at n .. n + 3, each rounded once.
+__device__ __forceinline__ void store4_y(f16* y, int n, int N, const floatx4& v, uint2 rr, bool has_r) {
+  float o4[4] = {v[0], v[1], v[2], v[3]};
+  if (has_r) {
+    o4[0] += h2f(rr.x); o4[1] += h2f(rr.x >> 16);
+    o4[2] += h2f(rr.y); o4[3] += h2f(rr.y >> 16);
+  }
+  if (n + 3 < N && ((N & 3) == 0)) {
+    uint2 o;
+    o.x = (uint32_t)f2h_bits(o4[0]) | ((uint32_t)f2h_bits(o4[1]) << 16);
+    o.y = (uint32_t)f2h_bits(o4[2]) | ((uint32_t)f2h_bits(o4[3]) << 16);
+    *(uint2*)(y + n) = o;
+  } else {
+    for (int q = 0; q < 4 && n + q < N; ++q) y[n + q] = (f16)o4[q];
+  }
+}
+
 // f16 store of one lane's 4 consecutive outputs C[n..n+3] of row y (+ r),
 // each rounded once; n + 3 < N and 8-byte alignment when N % 4 == 0.
-__device__ __forceinline__ void store4_f16(f16* __restrict__ y, const f16* __restrict__ r, int n,
+__device__ __forceinline__ void store4_f16(f16* y, const f16* r, int n,
                                            int N, const floatx4& v) {
   if (n + 3 < N && ((N & 3) == 0)) {
     float o4[4] = {v[0], v[1], v[2], v[3]};

@@ -19,8 +19,12 @@
 //      at once.  Rows are gathered through the pair list: token t = p / top_k
 //      reads A[t] (shared rows) or A[p] (one row per pair), and writes Y[p].
 // The order of the pairs inside one expert's range is unspecified (atomic
-// cursors); it never changes a result, because every output row depends only
-// on its own activation row and its expert's weights.
+// cursors), so the tile and the position within it that a row lands in vary
+// from call to call.  Results do not: every output row depends only on its
+// own activation row and its expert's weights, and the order in which its
+// sum is accumulated (the K stages from a starting stage fixed by the expert
+// and the weight-row tile, the same matrix-core instruction sequence) does
+// not depend on the row's tile or position.
 #include "common.h"
 #include "internal.h"
 #include "mfma_tile.h"
@@ -29,22 +33,14 @@ namespace fcg {
 
 constexpr int MOE_BUCKET_THREADS = 1024;
 constexpr int MOE_NT = 2;                  // BN = 128 weight rows per workgroup
-#ifndef MOE_PD
-#define MOE_PD 1                           // stages of prefetch in the tile main loop
-#endif
-#ifndef MOE_SH
-#define MOE_SH 2                           // half super-blocks per stage
-#endif
+constexpr int MOE_PD = 1;                  // stages of prefetch in the tile main loop
+constexpr int MOE_SH = 2;                  // half super-blocks per stage
 
 // Row tile: 16-row halves, 2 per tile when the routing is very sparse (fewer
 // than 8 pairs per expert on average), 8 when it is dense (64 or more), else 4.
 // Empty halves of a tile are skipped, so a tall tile costs a short expert
 // nothing, while a tall expert decodes its weights fewer times.
-#ifndef MOE_MT_FIXED
 static int moe_mt(int E, long long P) { return P < 8LL * E ? 2 : (P >= 64LL * E ? 8 : 4); }
-#else
-static int moe_mt(int, long long) { return MOE_MT_FIXED; }
-#endif
 
 static long long moe_max_tiles(int E, long long P, int BM) {
   return (P + BM - 1) / BM + (E < P ? E : P);
@@ -203,12 +199,15 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
   floatx4 acc[MT][NT];
   const uint8_t* We = W + (size_t)e * expert_bytes;
   const int S = K / (KSTAGE * MOE_SH);
-  const int rot = (ti + nt) % S;           // spread concurrent loads over K
+  // spread concurrent loads over K: the start stage depends on the expert and
+  // the weight-row tile only, so a row's summation order never depends on
+  // which of its expert's tiles it was scattered to
+  const int rot = (e + nt) % S;
   // (active halves rounded up to 1, 2, 4 or MT)
-  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, GROUPED_TILED, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act == 2 || MT == 2) tile_mainloop<QT, MT, NT, (MT < 2 ? MT : 2), GROUPED_TILED, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
-  else if (mt_act <= 4 || MT == 4) tile_mainloop<QT, MT, NT, (MT < 4 ? MT : 4), GROUPED_TILED, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
-  else tile_mainloop<QT, MT, NT, MT, GROUPED_TILED, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  if (mt_act == 1) tile_mainloop<QT, MT, NT, 1, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act == 2 || MT == 2) tile_mainloop<QT, MT, NT, (MT < 2 ? MT : 2), MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else if (mt_act <= 4 || MT == 4) tile_mainloop<QT, MT, NT, (MT < 4 ? MT : 4), MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
+  else tile_mainloop<QT, MT, NT, MT, MOE_PD, MOE_SH>(We, N, K, n0, 0, S, rot, rows, As, acc);
 
 #pragma unroll
   for (int i = 0; i < MT; ++i) {

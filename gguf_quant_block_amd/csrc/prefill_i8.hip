@@ -354,11 +354,25 @@ __device__ __forceinline__ void i8_compute(int N, int K, int n0, const uint8_t* 
 // split-K partials P[split][M][N].
 template <int MT>
 __device__ __forceinline__ void i8_epilogue(const floatx4 (&acc)[MT][I8_NTW],
-                                            const f16* __restrict__ R, f16* __restrict__ Y,
+                                            const f16* R, f16* Y,
                                             float* __restrict__ P, int M, int N, int m0, int n0,
                                             int sp, int splits) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = n0 + wave * 16 * I8_NTW + (lane & 15);
+  // every residual first, then the stores: Y may be R, so the compiler would
+  // otherwise wait for each residual load right before its store (each
+  // element is read and written by its own lane only, so the early loads are
+  // exact in place)
+  f16 rr[MT][4][I8_NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < I8_NTW; ++j) {
+        const int m = m0 + 16 * i + 4 * (lane >> 4) + q, nn = n + 16 * j;
+        rr[i][q][j] = (R && splits == 1 && m < M && nn < N) ? R[(size_t)m * N + nn] : (f16)0.f;
+      }
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -371,7 +385,7 @@ __device__ __forceinline__ void i8_epilogue(const floatx4 (&acc)[MT][I8_NTW],
         if (nn >= N) continue;
         const float v = acc[i][j][q];
         if (splits > 1) P[((size_t)sp * M + m) * N + nn] = v;
-        else Y[(size_t)m * N + nn] = (f16)(R ? v + (float)R[(size_t)m * N + nn] : v);
+        else Y[(size_t)m * N + nn] = (f16)(R ? v + (float)rr[i][q][j] : v);
       }
     }
 }
@@ -379,7 +393,7 @@ __device__ __forceinline__ void i8_epilogue(const floatx4 (&acc)[MT][I8_NTW],
 template <int QT, int MT>
 __global__ void __launch_bounds__(I8_THREADS)
 prefill_i8_kernel(const uint8_t* W, const int8_t* qa, const float* sT, const float* uT,
-                  const f16* __restrict__ R, f16* __restrict__ Y, float* __restrict__ P, int M,
+                  const f16* R, f16* Y, float* __restrict__ P, int M,
                   int N, int K, int Mp, int tiles_m, int tiles_n, int splits,
                   int stages_per_split) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -410,7 +424,7 @@ prefill_i8_kernel(const uint8_t* W, const int8_t* qa, const float* sT, const flo
     return;
   }
   if (wave == I8_CWAVES + 1) {
-    dma_load_w<QT, MT, true, I8Cfg<QT, MT>>(W, N, K, n0, smem, s_begin, s_end, rot);
+    dma_load_w<QT, MT, I8Cfg<QT, MT>>(W, N, K, n0, smem, s_begin, s_end, rot);
     return;
   }
   floatx4 acc[MT][I8_NTW];

@@ -40,9 +40,21 @@
  *     asynchronous and stream-ordered; kernel faults surface at the caller's
  *     next synchronisation.  A handle owns a workspace, so one handle must not
  *     be run concurrently on two streams.  The workspace grows (and moves)
- *     when a call needs more than earlier calls did: a HIP graph that
- *     captured earlier calls of the handle must then be captured again, so
- *     capture after a call at the largest row count and path.
+ *     when a call needs more than earlier calls did; the growth is
+ *     stream-ordered (hipFreeAsync / hipMallocAsync on the call's stream), so
+ *     it waits for no other stream.  A HIP graph that captured earlier calls
+ *     of the handle must then be captured again, so capture after a call at
+ *     the largest row count and path.
+ *   - Testing switch: the environment variable FC_GGUF_TEST_FAIL_ALLOC =
+ *     create | workspace | all makes the named device allocations fail
+ *     (FC_GGUF_ENOMEM), read at every allocation.
+ *   - Prefill kernel: two f16 matrix-core kernels serve the prefill path: a
+ *     tile whose compute waves decode the weights into their matrix-core
+ *     operand registers (16 .. 128 activation rows, growing with M; the
+ *     default at every M), and a 128 x 128 tile whose producer waves decode
+ *     each block once into an f16 tile in LDS that consumer waves multiply.
+ *     The environment variable FC_GGUF_PREFILL_KERNEL = dma | lds, read when
+ *     a handle is created, forces the first or the second (testing).
  */
 #ifndef FC_GGUF_H
 #define FC_GGUF_H
@@ -157,7 +169,7 @@ int fc_gguf_create_grouped(int64_t E, int64_t N, int64_t K, int qtype, const voi
  * [0, E) produce zero rows.  T == 0 is a no-op.  Matrix-core numerics
  * (f16 weights, f32 accumulation) for every expert, whatever its row count.
  * Two kernels on `stream`: the bucketing of the pairs by expert (into the
- * handle's workspace, grown on first use with hipMalloc) and the grouped FC.
+ * handle's workspace, grown stream-ordered on first use) and the grouped FC.
  * T * top_k <= 2^24.
  */
 int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,

@@ -1,5 +1,7 @@
-"""The C-ABI library loads and exports every symbol include/fc_gguf.h declares
-(CPU only: host-side argument validation, no kernel launches)."""
+"""The C-ABI libraries load and export every symbol their headers declare:
+include/fc_gguf.h (libfcgguf.so, the FC) and include/fc_gguf_ceilings.h
+(libfcgceil.so, the benchmark's ceiling kernels).  CPU only: host-side
+argument validation, no kernel launches."""
 
 import ctypes
 import os
@@ -10,10 +12,10 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "fc_gguf.h")).read()
+def _declared(header="fc_gguf.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fc_gguf_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fc_\w+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -29,6 +31,30 @@ def test_every_declared_symbol_is_exported(L):
     assert len(names) >= 11
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_every_header_has_its_library():
+    # each header under include/ is served by one in-tree library
+    from gguf_quant_block_amd import build
+    libs = {"fc_gguf.h": build.LIB, "fc_gguf_ceilings.h": build.CEIL_LIB}
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(libs)
+    if not os.path.exists(build.CEIL_LIB):
+        build.build()
+    C = ctypes.CDLL(build.CEIL_LIB)
+    names = _declared("fc_gguf_ceilings.h")
+    assert names == ["fc_ceiling_mfma", "fc_ceiling_stream_read"]
+    for n in names:
+        assert hasattr(C, n), n
+    # argument checks (no launch): misaligned or ragged sizes, bad unroll, bad dtype
+    C.fc_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    C.fc_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert C.fc_ceiling_stream_read(None, 16, 1, 1, None, None) == -1
+    assert C.fc_ceiling_stream_read(16, 17, 1, 1, 16, None) == -1
+    assert C.fc_ceiling_stream_read(16, 16, 1, 3, 16, None) == -1
+    assert C.fc_ceiling_stream_read(8, 16, 1, 1, 16, None) == -1
+    assert C.fc_ceiling_mfma(2, 1, 1, 16, None) == -1
+    assert C.fc_ceiling_mfma(0, 0, 1, 16, None) == -1
 
 
 def test_strerror_codes(L):

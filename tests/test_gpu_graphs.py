@@ -3,18 +3,20 @@
 A graph of each entry point (captured after an eager call at the same row
 count, so that no workspace is allocated during capture) is replayed several
 times, with other eager work and synchronisations between the replays, and
-every replay is compared with the eager result: bit for bit where the kernels
-fix their summation order, and within a last-bit tolerance for the grouped
-path, whose row-to-tile assignment inside a hot expert follows the order of
-atomic cursors.  Two handles run concurrently on two streams (default
-priority) give the results they give alone.
+every replay is compared with the eager result bit for bit: every kernel
+fixes its summation order (the grouped path too, whose row-to-tile
+assignment inside a hot expert follows the order of atomic cursors but
+whose per-row summation order does not depend on it).  Two handles run
+concurrently on two streams (default priority) give the results they give
+alone, and a handle whose workspace grows while another stream is busy
+gives the result it gives alone.
 """
 
 import numpy as np
 import pytest
 
 from gguf_quant_block_amd import synth
-from helpers import case, relfro
+from helpers import case
 
 pytestmark = pytest.mark.gpu
 
@@ -117,8 +119,7 @@ def test_graph_replay_grouped(gpu_lib, a_per_slot):
     f.grouped(Ad, idd, a_per_slot, out=out)
     ref = _host(out)
     for y in _replays(lambda: f.grouped(Ad, idd, a_per_slot, out=out), out):
-        assert np.isfinite(y).all()
-        assert relfro(y, ref) <= 1e-3
+        assert np.array_equal(y.view(np.uint16), ref.view(np.uint16))
 
 
 def test_two_handles_on_two_streams(gpu_lib):
@@ -143,3 +144,33 @@ def test_two_handles_on_two_streams(gpu_lib):
         torch.cuda.synchronize()
         assert np.array_equal(_host(ya).view(np.uint16), ref_a.view(np.uint16))
         assert np.array_equal(_host(yb).view(np.uint16), ref_b.view(np.uint16))
+
+
+def test_workspace_growth_with_another_stream_busy(gpu_lib):
+    # the workspace of handle b grows (split-K partials at a larger row
+    # count) on stream sb while stream sa runs handle a; both results equal
+    # their stand-alone results
+    torch = _torch()
+    qtype, N, K = "q6_k", 256, 8192
+    wa, Aa, Ra = case(qtype, 512, 1024, 2048, 100, 0)
+    wb, Ab, Rb = case(qtype, 512, N, K, 100, 1)
+    fa, fb = _fc(wa, qtype, 1024, 2048), _fc(wb, qtype, N, K)
+    Aad, Rad, Abd, Rbd = _dev(Aa), _dev(Ra), _dev(Ab), _dev(Rb)
+    ref_a = _host(fa(Aad, Rad))
+    fb_small = _fc(wb, qtype, N, K)
+    ref_b = _host(fb_small(Abd, Rbd))
+    # grow b's workspace step by step: 16 rows, then 512
+    fb(Abd[:16], Rbd[:16])
+    torch.cuda.synchronize()
+    ya, yb = torch.empty_like(Rad), torch.empty_like(Rbd)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(sa):
+        for _ in range(20):
+            fa(Aad, Rad, out=ya)
+    with torch.cuda.stream(sb):
+        fb(Abd, Rbd, out=yb)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(ya).view(np.uint16), ref_a.view(np.uint16))
+    assert np.array_equal(_host(yb).view(np.uint16), ref_b.view(np.uint16))

@@ -155,3 +155,61 @@ def test_auto_row_threshold_from_env(gpu_lib, monkeypatch):
     assert np.array_equal(got[None], forced["decode"])
     assert np.array_equal(got["junk"], forced["decode"])
     assert np.array_equal(got["5"], forced["prefill"])
+
+
+def _fc_kernel(w, qtype, N, K, kernel, monkeypatch):
+    # FC_GGUF_PREFILL_KERNEL is read when the handle is created
+    monkeypatch.setenv("FC_GGUF_PREFILL_KERNEL", kernel)
+    f = _fc(w, qtype, N, K)
+    monkeypatch.delenv("FC_GGUF_PREFILL_KERNEL", raising=False)
+    return f
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M,N,K", [(8, 80, 256), (16, 128, 512), (130, 200, 768), (129, 257, 1024),
+                                   (256, 384, 2048), (300, 64, 512), (40, 1000, 4096), (513, 130, 256)])
+def test_decode_once_tile_forced(gpu_lib, monkeypatch, qtype, M, N, K):
+    # the decode-once (producer / consumer) tile at any row count: ragged
+    # activation and weight tiles, split-K grids, a single super-block
+    w, A, R = case(qtype, M, N, K, 68, M * 3 + N)
+    f = _fc_kernel(w, qtype, N, K, "lds", monkeypatch)
+    y = _host(f(_dev(A), _dev(R)))
+    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("M", [256, 512])
+def test_loader_wave_tile_forced_at_large_m(gpu_lib, monkeypatch, qtype, M):
+    # the loader-wave tile where AUTO would take the decode-once tile
+    N, K = 384, 1024
+    w, A, R = case(qtype, M, N, K, 69, M)
+    f = _fc_kernel(w, qtype, N, K, "dma", monkeypatch)
+    y = _host(f(_dev(A), _dev(R)))
+    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_decode_once_tile_in_place_and_extreme_scales(gpu_lib, monkeypatch, qtype):
+    M, N, K = 200, 256, 1024
+    w, A, R = case(qtype, M, N, K, 70, 0)
+    w = extreme_scales(w, qtype, 11)
+    f = _fc_kernel(w, qtype, N, K, "lds", monkeypatch)
+    Rd = _dev(R)
+    f(_dev(A), Rd, out=Rd)
+    y = _host(Rd)
+    assert np.all(np.isfinite(y))
+    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+
+
+@pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_decode_once_tile_full_size_sampled(gpu_lib, monkeypatch, qtype, shape):
+    # the decode-once tile on the full-size prefill shapes at M = 512 (a split-K
+    # grid on [2048, 8192]), sampled output columns
+    M = 512
+    N, K = synth.PREFILL_SHAPES[shape]
+    w, A, R = case(qtype, M, N, K, 71, shape)
+    y = _host(_fc_kernel(w, qtype, N, K, "lds", monkeypatch)(_dev(A), _dev(R)))
+    cols = np.unique(np.concatenate([np.arange(0, N, 64), np.arange(63, N, 64), [N - 1]]))
+    ref = ofc.fc_ref(A, okq.dequantize(w[cols], qtype), R[:, cols])
+    assert relfro(y[:, cols], ref) <= PREFILL_TOL
