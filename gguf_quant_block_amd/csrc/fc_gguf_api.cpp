@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <new>
 
 #include <rocblas/rocblas.h>
@@ -36,6 +37,8 @@ struct fc_gguf {
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr size_t kScratchBytes = 512 * 1024;   // fc_gguf_run_grouped_noalloc's scratch per device
+constexpr int kMaxDevices = 64;
 
 int block_bytes(int qtype) {
   switch (qtype) {
@@ -254,6 +257,59 @@ hipError_t run_decode(fc_gguf_t h, const AT* a, const AT* r, AT* y, int64_t M, h
   return e;
 }
 
+// Argument checks of the grouped calls (FC_GGUF_OK also for T == 0).
+int check_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, const int32_t* ids,
+                  int top_k, const void* Y) {
+  if (!h || T < 0) return FC_GGUF_EINVAL;
+  if (const int rc = check_device(h); rc != FC_GGUF_OK) return rc;
+  if (T == 0) return FC_GGUF_OK;
+  if (!A || !ids || !Y || top_k <= 0 || top_k > h->E || (a_per_slot != 0 && a_per_slot != 1))
+    return FC_GGUF_EINVAL;
+  if (T * top_k > ((int64_t)1 << 24) || T * top_k * h->K > ((int64_t)1 << 31) ||
+      T * top_k * h->N > ((int64_t)1 << 31))
+    return FC_GGUF_ERANGE;
+  if (!aligned(A, 16) || !aligned(Y, 8) || !aligned(ids, 4)) return FC_GGUF_EINVAL;
+  return FC_GGUF_OK;
+}
+
+// The bucketing and grouped-FC launches with the bucketing workspace `ws`.
+int launch_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, const int32_t* ids,
+                   int top_k, void* Y, void* ws, hipStream_t st) {
+  hipError_t e = fcg::launch_moe(h->qtype, h->w, h->expert_bytes, (int)h->E, (int)h->N, (int)h->K,
+                                 (const fcg::f16*)A, (int)T, a_per_slot, ids, top_k, (fcg::f16*)Y,
+                                 ws, h->num_cu, st);
+  if (e == hipErrorNotSupported) return FC_GGUF_EUNSUPPORTED;
+  if (e != hipSuccess) return hip_fail(h, e);
+  return FC_GGUF_OK;
+}
+
+}  // namespace
+
+// Scratch of fc_gguf_run_grouped_noalloc: the bucketing workspace (tile list,
+// expert offsets, pair list, tile count) in a static device array, so that
+// the call allocates nothing.  Each GPU holds its own copy for the life of
+// the process.  In host code `fcg_noalloc_scratch` names a host-side stand-in,
+// not the device memory: its device address is taken with
+// hipGetSymbolAddress on the device's first call and kept per device.  The
+// bucketing kernel writes every word the grouped kernel then reads, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t fcg_noalloc_scratch[kScratchBytes];
+
+namespace {
+std::atomic<void*> g_scratch[kMaxDevices];
+
+int scratch_ptr(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return FC_GGUF_ERANGE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // the handle's device is current (checked by the caller)
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(fcg_noalloc_scratch));
+    if (e != hipSuccess || !p) return FC_GGUF_EHIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FC_GGUF_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -354,24 +410,23 @@ int fc_gguf_run_f32(fc_gguf_t h, const float* A, int64_t M, const float* R, floa
 
 int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, const int32_t* ids,
                         int top_k, void* Y, void* stream) {
-  if (!h || T < 0) return FC_GGUF_EINVAL;
-  if (const int rc = check_device(h); rc != FC_GGUF_OK) return rc;
-  if (T == 0) return FC_GGUF_OK;
-  if (!A || !ids || !Y || top_k <= 0 || top_k > h->E || (a_per_slot != 0 && a_per_slot != 1))
-    return FC_GGUF_EINVAL;
-  if (T * top_k > ((int64_t)1 << 24) || T * top_k * h->K > ((int64_t)1 << 31) ||
-      T * top_k * h->N > ((int64_t)1 << 31))
-    return FC_GGUF_ERANGE;
-  if (!aligned(A, 16) || !aligned(Y, 8) || !aligned(ids, 4)) return FC_GGUF_EINVAL;
+  int rc = check_grouped(h, A, T, a_per_slot, ids, top_k, Y);
+  if (rc != FC_GGUF_OK || T == 0) return rc;
   const size_t need = fcg::moe_workspace_bytes((int)h->E, (int)T, top_k);
-  const int rc = ensure_ws(h, need, (hipStream_t)stream);
+  rc = ensure_ws(h, need, (hipStream_t)stream);
   if (rc != FC_GGUF_OK) return rc;
-  hipError_t e = fcg::launch_moe(h->qtype, h->w, h->expert_bytes, (int)h->E, (int)h->N, (int)h->K,
-                                 (const fcg::f16*)A, (int)T, a_per_slot, ids, top_k, (fcg::f16*)Y,
-                                 h->ws, h->num_cu, (hipStream_t)stream);
-  if (e == hipErrorNotSupported) return FC_GGUF_EUNSUPPORTED;
-  if (e != hipSuccess) return hip_fail(h, e);
-  return FC_GGUF_OK;
+  return launch_grouped(h, A, T, a_per_slot, ids, top_k, Y, h->ws, (hipStream_t)stream);
+}
+
+int fc_gguf_run_grouped_noalloc(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
+                                const int32_t* ids, int top_k, void* Y, void* stream) {
+  int rc = check_grouped(h, A, T, a_per_slot, ids, top_k, Y);
+  if (rc != FC_GGUF_OK || T == 0) return rc;
+  if (fcg::moe_workspace_bytes((int)h->E, (int)T, top_k) > kScratchBytes) return FC_GGUF_ERANGE;
+  void* ws = nullptr;
+  rc = scratch_ptr(h->device, &ws);
+  if (rc != FC_GGUF_OK) return rc;
+  return launch_grouped(h, A, T, a_per_slot, ids, top_k, Y, ws, (hipStream_t)stream);
 }
 
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s, int32_t* T,

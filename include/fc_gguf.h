@@ -176,6 +176,22 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
                         const int32_t* ids, int top_k, void* Y, void* stream);
 
 /*
+ * fc_gguf_run_grouped without any allocation, for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments, kernels and
+ * results as fc_gguf_run_grouped, but the bucketing workspace is a static
+ * 512 KB device array of the library (one per GPU, held until the process
+ * ends) instead of the handle's workspace; no hipMalloc, hipFree or other
+ * allocating call is made.  Calls whose bucketing needs more than 512 KB
+ * (about E*8 + T*top_k*4.25 bytes) return FC_GGUF_ERANGE.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, or two host threads) race and must not be issued; calls ordered on
+ * one stream are safe.
+ */
+int fc_gguf_run_grouped_noalloc(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
+                                const int32_t* ids, int top_k, void* Y, void* stream);
+
+/*
  * Test exports: they run the same device code as the decode path.
  *
  * fc_gguf_debug_quantize: the per-32 int8 activation quantisation of the
