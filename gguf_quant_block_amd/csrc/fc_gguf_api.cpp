@@ -232,7 +232,9 @@ int check_run(fc_gguf_t h, const void* A, int64_t M, const void* R, const void* 
 
 // The decode path over M rows: chunks of at most 7 rows (one launch each),
 // smaller when the quantised activations of a chunk would not fit in one CU's
-// LDS.
+// LDS.  At most one or two workgroups per CU: past that, workgroups take
+// several row tiles each, streaming the next one's weights under this one's
+// arithmetic.
 template <class AT>
 hipError_t run_decode(fc_gguf_t h, const AT* a, const AT* r, AT* y, int64_t M, hipStream_t st,
                       int* rc) {
@@ -246,12 +248,15 @@ hipError_t run_decode(fc_gguf_t h, const AT* a, const AT* r, AT* y, int64_t M, h
   hipError_t e = hipSuccess;
   for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += cap) {
     const int mc = (int)(M - m0 < cap ? M - m0 : cap);
+    // measured: one activation row streams best with two workgroups per CU,
+    // several rows (more arithmetic per weight byte) with one
+    const int max_wgs = (mc == 1 ? 2 : 1) * h->num_cu;
     if constexpr (sizeof(AT) == 2)
       e = fcg::launch_gemv(h->qtype, h->w, a + m0 * K, r ? r + m0 * N : nullptr, y + m0 * N, mc, N,
-                           K, st);
+                           K, max_wgs, st);
     else
       e = fcg::launch_gemv_f32(h->qtype, h->w, a + m0 * K, r ? r + m0 * N : nullptr, y + m0 * N, mc,
-                               N, K, st);
+                               N, K, max_wgs, st);
   }
   *rc = FC_GGUF_OK;
   return e;

@@ -33,10 +33,12 @@ hipError_t launch_weight_layout(int qtype, const uint8_t* src, uint8_t* dst, int
 
 // decode path (M in 1..7); A, R, Y all f16, or all f32
 size_t gemv_lds_bytes(int qtype, int M, int K);
+// max_wgs: the most workgroups the launch uses (one per row tile up to it;
+// each then takes every max_wgs-th row tile)
 hipError_t launch_gemv(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, int M,
-                       int N, int K, hipStream_t st);
+                       int N, int K, int max_wgs, hipStream_t st);
 hipError_t launch_gemv_f32(int qtype, const uint8_t* W, const float* A, const float* R, float* Y,
-                           int M, int N, int K, hipStream_t st);
+                           int M, int N, int K, int max_wgs, hipStream_t st);
 // A is f32 if f32, else f16
 hipError_t launch_debug_quantize(const void* A, bool f32, int M, int K, int8_t* qa, float* s, int* T,
                                  hipStream_t st);

@@ -53,30 +53,31 @@ constexpr int I8_NTW = 2;        // 16-row weight sub-tiles per compute wave
 
 // ----------------------------------------------------------- quantisation --
 
-// One thread per (row m < Mp, group g): the decode path's per-32 routine.
+// One thread per 16-byte chunk of the rows m < Mp (the decode path's per-32
+// routine, four lanes per group; rows past M quantise as zeros and store only
+// their zero scales).
 __global__ void __launch_bounds__(256)
 quant_i8_kernel(const f16* __restrict__ A, int M, int K, int Mp, int8_t* __restrict__ qa,
                 float* __restrict__ sT, float* __restrict__ uT) {
-  const int G = K / 32;
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (long long)Mp * G) return;
-  const int m = (int)(t % Mp), g = (int)(t / Mp);
-  float s = 0.f, u = 0.f;
-  if (m < M) {
-    const uint4* src = (const uint4*)(A + (size_t)m * K + 32 * g);
-    uint4 raw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = src[i];
-    uint32_t q[8];
-    int tsum, thalf[2];
-    quant_group<f16>(raw, q, s, tsum, thalf);
-    u = s * (float)tsum;
-    uint4* dst = (uint4*)(qa + (size_t)m * K + 32 * g);
-    dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-    dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+  constexpr int CV = chunk_vals<f16>(), GL = group_lanes<f16>();
+  const int KC = K / CV;                                  // chunks per row
+  const long long nch = (long long)Mp * KC;
+  const long long c = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool valid = c < nch;
+  const int m = valid ? (int)(c / KC) : 0, kc = valid ? (int)(c % KC) : 0;
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (valid && m < M) raw = *(const uint4*)(A + (size_t)m * K + (size_t)kc * CV);
+  uint32_t q[2];
+  float s;
+  int tsum, thalf;
+  quant_chunk<f16>(raw, q, s, tsum, thalf);               // every lane takes part
+  if (!valid) return;
+  if (m < M) *(uint2*)(qa + (size_t)m * K + (size_t)kc * CV) = make_uint2(q[0], q[1]);
+  if (kc % GL == 0) {
+    const int g = kc / GL;
+    sT[(size_t)g * Mp + m] = s;
+    uT[(size_t)g * Mp + m] = s * (float)tsum;
   }
-  sT[(size_t)g * Mp + m] = s;
-  uT[(size_t)g * Mp + m] = u;
 }
 
 // ----------------------------------------------------------- slot layout --
@@ -474,8 +475,8 @@ hipError_t launch_prefill_i8(int qtype, const uint8_t* W, const f16* A, const f1
   p += al((size_t)Mp * (K / 32) * sizeof(float));
   float* P = splits > 1 ? (float*)p : nullptr;
   {
-    const long long tasks = (long long)Mp * (K / 32);
-    hipLaunchKernelGGL(quant_i8_kernel, dim3((unsigned)((tasks + 255) / 256)), dim3(256), 0, st, A,
+    const long long chunks = (long long)Mp * (K / chunk_vals<f16>());
+    hipLaunchKernelGGL(quant_i8_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, A,
                        M, K, Mp, qa, sT, uT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

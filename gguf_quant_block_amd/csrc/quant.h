@@ -1,6 +1,7 @@
 // Per-32 int8 activation quantisation shared by the decode GEMV (fused into
-// its launch) and the int8 matrix-core prefill (a pass of its own): the one
-// routine, so both paths see bit-identical codes and scales.
+// its launch), the int8 matrix-core prefill (a pass of its own) and the
+// debug export: the one routine, so every path sees bit-identical codes and
+// scales.
 #pragma once
 
 #include <type_traits>
@@ -20,34 +21,37 @@ constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23: x + magic rounds x to 
 // is needed.  An all-zero group, or an f32 group so small that 127/amax
 // overflows (amax < 127/FLT_MAX), gives s = 0 and codes 0.
 //
-// One lane quantises one 32-value group (64 bytes of f16 or 128 of f32):
-//   q[0 .. 8):   packed int8 codes of the group's values
-//   tsum:        sum of the group's 32 codes
-//   thalf[0,1]:  sums of the group's first and second 16 codes
-// round-half-even(fl32(a * inv)) in the low byte of the result.  The product
-// is rounded to f32 first and only then rounded to an integer (adding 1.5*2^23
-// rounds to the nearest integer, ties to even, for |x| < 2^22); the empty asm
-// keeps the compiler from fusing the two into one fma, which would round the
-// exact product once and differ on ties.
+// The lanes of a group share it: each lane holds one 16-byte chunk of the
+// group's values (8 f16 values, the group on 4 consecutive lanes; or 4 f32
+// values, on 8 lanes), so that a wave's loads of consecutive chunks are
+// contiguous.  round-half-even(fl32(a * inv)) lands in the low byte of the
+// result.  The product is rounded to f32 first and only then rounded to an
+// integer (adding 1.5*2^23 rounds to the nearest integer, ties to even, for
+// |x| < 2^22); the empty asm keeps the compiler from fusing the two into one
+// fma, which would round the exact product once and differ on ties.
 __device__ __forceinline__ uint32_t rne_code(float a, float inv) {
   float p = a * inv;
   asm volatile("" : "+v"(p));
   return __builtin_bit_cast(uint32_t, p + RNE_MAGIC);
 }
 
-// 16-byte loads per 32-value group of activations of type AT
 template <class AT>
-constexpr int act_u4() { return (int)sizeof(AT) * 2; }
+constexpr int chunk_vals() { return 16 / (int)sizeof(AT); }       // values per 16-byte chunk
+template <class AT>
+constexpr int group_lanes() { return 32 / chunk_vals<AT>(); }     // lanes per 32-value group
 
+// Quantise the lane's chunk: raw = its 16 bytes; the group starts at a lane
+// index that is a multiple of group_lanes<AT>(), and every lane of the wave
+// takes part (cross-lane shuffles).  Out:
+//   q[0 .. chunk_vals/4):  packed int8 codes of the chunk's values
+//   s:                     the group's scale (every lane of the group)
+//   tsum:                  sum of the group's 32 codes (every lane)
+//   thalf:                 sum of the 16 codes of the lane's half of the group
 template <class AT>
-__device__ __forceinline__ void quant_group(const uint4* raw, uint32_t* q, float& s, int& tsum,
-                                            int* thalf) {
-  constexpr int U4 = act_u4<AT>();
-  uint32_t w[4 * U4];
-#pragma unroll
-  for (int i = 0; i < U4; ++i) {
-    w[4 * i] = raw[i].x; w[4 * i + 1] = raw[i].y; w[4 * i + 2] = raw[i].z; w[4 * i + 3] = raw[i].w;
-  }
+__device__ __forceinline__ void quant_chunk(uint4 raw, uint32_t* q, float& s, int& tsum,
+                                            int& thalf) {
+  constexpr int GL = group_lanes<AT>();
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   auto value = [&](int i) -> float {
     if constexpr (std::is_same<AT, f16>::value) return h2f(w[i >> 1] >> (16 * (i & 1)));
     else return __builtin_bit_cast(float, w[i]);
@@ -56,14 +60,16 @@ __device__ __forceinline__ void quant_group(const uint4* raw, uint32_t* q, float
   if constexpr (std::is_same<AT, f16>::value) {
     half2v m2 = {(f16)0.f, (f16)0.f};
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < 4; ++j)
       m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(half2v, w[j] & 0x7FFF7FFFu));
     amax = fmaxf((float)m2[0], (float)m2[1]);
   } else {
     amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, __builtin_bit_cast(float, w[j] & 0x7FFFFFFFu));
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, __builtin_bit_cast(float, w[j] & 0x7FFFFFFFu));
   }
+#pragma unroll
+  for (int off = 1; off < GL; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   float inv = 0.f;
   s = 0.f;
   if (amax > 0.f) {
@@ -71,8 +77,9 @@ __device__ __forceinline__ void quant_group(const uint4* raw, uint32_t* q, float
     if (inv <= 3.402823466e38f) s = __fdiv_rn(amax, 127.0f);   // inv finite
     else inv = 0.f;
   }
+  int p = 0;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < chunk_vals<AT>() / 4; ++c) {
     // four values -> four rounded floats -> the low byte of each is the code
     const uint32_t r0 = rne_code(value(4 * c), inv);
     const uint32_t r1 = rne_code(value(4 * c + 1), inv);
@@ -81,16 +88,13 @@ __device__ __forceinline__ void quant_group(const uint4* raw, uint32_t* q, float
     const uint32_t lo = __builtin_amdgcn_perm(r1, r0, 0x0c0c0400u);
     const uint32_t hi = __builtin_amdgcn_perm(r3, r2, 0x0c0c0400u);
     q[c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    p = dot4((int)q[c], 0x01010101, p);
   }
-  // code sums: 16-value halves and the group total
-  int a = 0, b = 0;
+  // code sums: over the lanes of the half, then of the group
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a = dot4((int)q[i], 0x01010101, a);
-#pragma unroll
-  for (int i = 4; i < 8; ++i) b = dot4((int)q[i], 0x01010101, b);
-  thalf[0] = a;
-  thalf[1] = b;
-  tsum = a + b;
+  for (int off = 1; off < GL / 2; off <<= 1) p += __shfl_xor(p, off, 64);
+  thalf = p;
+  tsum = p + __shfl_xor(p, GL / 2, 64);
 }
 
 }  // namespace fcg
