@@ -90,3 +90,56 @@ def expected_device_bytes(w, qtype, N, K):
     d = planes[208 * nblk:].reshape(nblk, 2)
     return np.concatenate([tile_bytes(ql, N, KB, 8), tile_bytes(qh, N, KB, 4), tile_bytes(sc, N, KB, 1),
                            _tile_d(d, N, KB)])
+
+
+ELEM_GUARD = 1e-2      # element-wise guard beside the Frobenius bar (maxrel metric)
+
+
+def check_fro(y, ref, tol=PREFILL_TOL):
+    """The prefill / MoE bar: relative Frobenius error <= tol, and no single
+    element off by more than ELEM_GUARD of max(|ref|, rms(ref)) (one wrong
+    element among many barely moves the Frobenius norm)."""
+    e, g = relfro(y, ref), maxrel(y, ref)
+    assert e <= tol, f"relative Frobenius error {e:.3e} > {tol}"
+    assert g <= ELEM_GUARD, f"element-wise error {g:.3e} > {ELEM_GUARD}"
+    return e
+
+
+def stratified_cols(N, seed, tile=128, inner=2):
+    """Output columns for sampled full-size checks: of every `tile`-column
+    block, its first and last column and `inner` seeded ones inside."""
+    g = np.random.default_rng(seed)
+    cols = []
+    for c0 in range(0, N, tile):
+        c1 = min(N, c0 + tile)
+        cols += [c0, c1 - 1]
+        cols += list(g.integers(c0, c1, size=inner))
+    return np.unique(np.array(cols, dtype=np.int64))
+
+
+CANARY = 64            # elements of guard bytes on each side of a guarded tensor
+
+
+def guarded(shape, dtype, fill=None, seed=0):
+    """A CUDA tensor of `shape` inside a larger buffer with CANARY elements of
+    a seeded bit pattern on each side.  Returns (tensor, check); check()
+    asserts that both guard regions still hold their pattern."""
+    import torch
+    n = int(np.prod(shape))
+    item = torch.empty((), dtype=dtype).element_size()
+    pat = np.random.default_rng(seed).integers(0, 256, size=2 * CANARY * item, dtype=np.uint8)
+    big = torch.empty(n * item + 2 * CANARY * item, dtype=torch.uint8, device="cuda")
+    big[:CANARY * item] = torch.from_numpy(pat[:CANARY * item]).cuda()
+    big[CANARY * item + n * item:] = torch.from_numpy(pat[CANARY * item:]).cuda()
+    t = big[CANARY * item:CANARY * item + n * item].view(dtype).view(*shape)
+    if fill is not None:
+        t.copy_(torch.as_tensor(np.ascontiguousarray(fill)).to(dtype))
+
+    def check():
+        torch.cuda.synchronize()
+        b = big.cpu().numpy()
+        assert np.array_equal(b[:CANARY * item], pat[:CANARY * item]), "guard bytes before the tensor changed"
+        assert np.array_equal(b[CANARY * item + n * item:], pat[CANARY * item:]), \
+            "guard bytes after the tensor changed"
+
+    return t, check

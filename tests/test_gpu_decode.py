@@ -14,7 +14,7 @@ import pytest
 from gguf_quant_block_amd import synth
 from oracle import fc as ofc
 from oracle import kquant as okq
-from helpers import DECODE_TOL, PREFILL_TOL, case, expected_device_bytes, extreme_scales, maxrel, relfro, tile_bytes as _tile
+from helpers import DECODE_TOL, PREFILL_TOL, case, expected_device_bytes, extreme_scales, check_fro, guarded, maxrel, relfro, tile_bytes as _tile
 
 pytestmark = pytest.mark.gpu
 
@@ -110,11 +110,15 @@ def test_int_dots_bit_exact(gpu_lib, qtype, M, N, K):
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("N,K", [(37, 768), (512, 2048), (100, 3072), (24, 8192)])
 def test_gemv_parity(gpu_lib, qtype, M, N, K):
+    import torch
     with_r = (M + N) % 2 == 0
     w, A, R = case(qtype, M, N, K, 53, 100 * M + N, with_r=with_r)
-    y = _host(_fc(w, qtype, N, K)(_dev(A), None if R is None else _dev(R))).astype(np.float64)
+    # Y inside guard bytes: no store past it
+    Yd, ok = guarded((M, N), torch.float16, seed=M + N)
+    _fc(w, qtype, N, K)(_dev(A), None if R is None else _dev(R), out=Yd)
+    ok()
     ref = ofc.fc_ref_int8(A, w, qtype, R)
-    assert maxrel(y, ref) <= DECODE_TOL
+    assert maxrel(_host(Yd).astype(np.float64), ref) <= DECODE_TOL
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
@@ -129,11 +133,13 @@ def test_gemv_extreme_scales(gpu_lib, qtype, M):
 
 @pytest.mark.parametrize("qtype", QTYPES)
 def test_gemv_in_place_residual(gpu_lib, qtype):
-    M, N, K = 3, 64, 512
+    import torch
+    M, N, K = 3, 70, 512
     w, A, R = case(qtype, M, N, K, 54, 0)
-    Rd = _dev(R)
+    Rd, ok = guarded((M, N), torch.float16, fill=R, seed=3)
     fcg = _fc(w, qtype, N, K)
     fcg(_dev(A), Rd, out=Rd)
+    ok()
     assert maxrel(_host(Rd), ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
 
 
@@ -288,4 +294,4 @@ def test_row_count_changes_between_calls(gpu_lib):
         if M < 8:
             assert maxrel(y, ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL, M
         else:
-            assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL, M
+            check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))

@@ -1,6 +1,7 @@
 """GPU parity of the prefill path (M >= 8) against the float64 oracle.
 
-Relative Frobenius error <= 2e-3 against Y = A.W^T + R with W decoded exactly.
+Relative Frobenius error <= 2e-3 against Y = A.W^T + R with W decoded exactly,
+and no element off by more than 1e-2 of max(|y|, rms(y)).
 Covers every tile step of the M ladder, ragged M and N tails, split-K grids,
 the forced prefill path at M < 8, and the full-size prefill shapes at every
 M on sampled output columns.
@@ -12,7 +13,7 @@ import pytest
 from gguf_quant_block_amd import synth
 from oracle import fc as ofc
 from oracle import kquant as okq
-from helpers import PREFILL_TOL, case, extreme_scales, relfro
+from helpers import PREFILL_TOL, case, check_fro, extreme_scales, guarded, relfro, stratified_cols
 
 pytestmark = pytest.mark.gpu
 
@@ -41,16 +42,23 @@ def test_small_config_m16(gpu_lib, qtype):
     M, N, K = 16, 512, 2048
     w, A, _ = case(qtype, M, N, K, 0, 1, with_r=False)
     y = _host(_fc(w, qtype, N, K)(_dev(A)))
-    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype)) <= PREFILL_TOL
+    check_fro(y, ofc.fc_gguf_ref(A, w, qtype))
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
 @pytest.mark.parametrize("M,N,K", [(8, 80, 256), (37, 200, 768), (130, 384, 1024), (300, 64, 512),
                                    (64, 128, 2048), (17, 1000, 512), (24, 64, 14336)])
 def test_prefill_ragged(gpu_lib, qtype, M, N, K):
+    import torch
     w, A, R = case(qtype, M, N, K, 60, M * 7 + N)
-    y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
-    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+    # Y and R inside guard bytes: no store past Y, nothing written to R
+    Yd, y_ok = guarded((M, N), torch.float16, seed=M)
+    Rd, r_ok = guarded((M, N), torch.float16, fill=R, seed=N)
+    _fc(w, qtype, N, K)(_dev(A), Rd, out=Yd)
+    y_ok()
+    r_ok()
+    assert np.array_equal(_host(Rd).view(np.uint16), R.view(np.uint16))
+    check_fro(_host(Yd), ofc.fc_gguf_ref(A, w, qtype, R))
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
@@ -61,16 +69,18 @@ def test_forced_prefill_for_small_m(gpu_lib, qtype, M):
     fcg = _fc(w, qtype, N, K)
     fcg.set_path("prefill")
     y = _host(fcg(_dev(A), _dev(R)))
-    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+    check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
 def test_prefill_in_place_residual(gpu_lib, qtype):
-    M, N, K = 40, 128, 512
+    import torch
+    M, N, K = 40, 130, 512
     w, A, R = case(qtype, M, N, K, 62, 0)
-    Rd = _dev(R)
+    Rd, ok = guarded((M, N), torch.float16, fill=R, seed=5)
     _fc(w, qtype, N, K)(_dev(A), Rd, out=Rd)
-    assert relfro(_host(Rd), ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+    ok()
+    check_fro(_host(Rd), ofc.fc_gguf_ref(A, w, qtype, R))
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
@@ -83,7 +93,7 @@ def test_prefill_extreme_scales(gpu_lib, qtype, M):
     w = extreme_scales(w, qtype, M)
     y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
     assert np.all(np.isfinite(y))
-    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+    check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
@@ -94,7 +104,7 @@ def test_scratch_path_parity(gpu_lib, qtype, M, N, K, with_r):
     fcg = _fc(w, qtype, N, K)
     fcg.set_path("scratch")
     y = _host(fcg(_dev(A), None if R is None else _dev(R)))
-    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+    check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))
 
 
 def test_scratch_path_in_place_and_extreme_scales(gpu_lib):
@@ -105,7 +115,7 @@ def test_scratch_path_in_place_and_extreme_scales(gpu_lib):
     fcg.set_path("scratch")
     Rd = _dev(R)
     fcg(_dev(A), Rd, out=Rd)
-    assert relfro(_host(Rd), ofc.fc_gguf_ref(A, w, "q6_k", R)) <= PREFILL_TOL
+    check_fro(_host(Rd), ofc.fc_gguf_ref(A, w, "q6_k", R))
 
 
 def test_prefill_error_is_f16_sized(gpu_lib):
@@ -126,10 +136,10 @@ def test_prefill_full_size_sampled(gpu_lib, qtype, shape, M):
     N, K = synth.PREFILL_SHAPES[shape]
     w, A, R = case(qtype, M, N, K, 3, 10 * shape + synth.PREFILL_MS.index(M))
     y = _host(_fc(w, qtype, N, K)(_dev(A), _dev(R)))
-    cols = np.sort(np.random.default_rng(N + M).choice(N, size=160, replace=False))
-    cols = np.unique(np.concatenate([cols, [0, N - 1]]))
+    # every 128-column weight tile: its first and last column and two inside
+    cols = stratified_cols(N, N + M)
     ref = ofc.fc_ref(A, okq.dequantize(w[cols], qtype), R[:, cols])
-    assert relfro(y[:, cols], ref) <= PREFILL_TOL
+    check_fro(y[:, cols], ref)
 
 
 def test_auto_row_threshold_from_env(gpu_lib, monkeypatch):
@@ -174,7 +184,7 @@ def test_decode_once_tile_forced(gpu_lib, monkeypatch, qtype, M, N, K):
     w, A, R = case(qtype, M, N, K, 68, M * 3 + N)
     f = _fc_kernel(w, qtype, N, K, "lds", monkeypatch)
     y = _host(f(_dev(A), _dev(R)))
-    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+    check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
@@ -185,7 +195,7 @@ def test_loader_wave_tile_forced_at_large_m(gpu_lib, monkeypatch, qtype, M):
     w, A, R = case(qtype, M, N, K, 69, M)
     f = _fc_kernel(w, qtype, N, K, "dma", monkeypatch)
     y = _host(f(_dev(A), _dev(R)))
-    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+    check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
@@ -198,7 +208,7 @@ def test_decode_once_tile_in_place_and_extreme_scales(gpu_lib, monkeypatch, qtyp
     f(_dev(A), Rd, out=Rd)
     y = _host(Rd)
     assert np.all(np.isfinite(y))
-    assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+    check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))
 
 
 @pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
@@ -210,6 +220,6 @@ def test_decode_once_tile_full_size_sampled(gpu_lib, monkeypatch, qtype, shape):
     N, K = synth.PREFILL_SHAPES[shape]
     w, A, R = case(qtype, M, N, K, 71, shape)
     y = _host(_fc_kernel(w, qtype, N, K, "lds", monkeypatch)(_dev(A), _dev(R)))
-    cols = np.unique(np.concatenate([np.arange(0, N, 64), np.arange(63, N, 64), [N - 1]]))
+    cols = stratified_cols(N, N + 7)
     ref = ofc.fc_ref(A, okq.dequantize(w[cols], qtype), R[:, cols])
-    assert relfro(y[:, cols], ref) <= PREFILL_TOL
+    check_fro(y[:, cols], ref)

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import fc as ofc
-from helpers import DECODE_TOL, PREFILL_TOL, case, maxrel, relfro
+from helpers import DECODE_TOL, case, check_fro, maxrel
 
 pytestmark = pytest.mark.gpu
 
@@ -43,4 +43,4 @@ def test_random_case(gpu_lib, seed):
     if path in ("decode", "int8", "f32") or (path == "auto" and M < 8):
         assert maxrel(y, ofc.fc_ref_int8(A, w, qtype, R)) <= DECODE_TOL
     else:
-        assert relfro(y, ofc.fc_gguf_ref(A, w, qtype, R)) <= PREFILL_TOL
+        check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))
