@@ -13,7 +13,8 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libfcgguf.so")
+# FC_GGUF_LIB names another build of the library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("FC_GGUF_LIB") or os.path.join(PKG, "libfcgguf.so")
 
 Q4_K, Q5_K, Q6_K = 4, 5, 6
 QTYPES = {"q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}

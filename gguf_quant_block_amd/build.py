@@ -72,6 +72,42 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizer build of the C-ABI layer (argument validation, handle
+# and workspace management): fc_gguf_api.cpp's host code with AddressSanitizer
+# and UndefinedBehaviorSanitizer, linked with the regular kernel objects.  The
+# GPU code is built as usual (each sanitizer flag applies to the host pass
+# only).  Loaded by a process that preloads ASAN_RUNTIME.
+SAN_LIB = os.path.join(BUILD, "san", "libfcgguf_san.so")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime() -> str:
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "amdclang++")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized() -> str:
+    """The host-sanitized library (after build(), whose kernel objects it reuses)."""
+    san = os.path.dirname(SAN_LIB)
+    os.makedirs(san, exist_ok=True)
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "fc_gguf_api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    api = os.path.join(san, "fc_gguf_api.o")
+    cmd = [HIPCC, "-x", "hip", *CFLAGS, "-g", *SAN_HOST, "-c", os.path.join(CSRC, "fc_gguf_api.cpp"),
+           "-o", api]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on the sanitized fc_gguf_api.cpp")
+    _link([api, *objs], SAN_LIB, [*SAN_HOST, "-shared-libsan", "-L/opt/rocm/lib", "-lrocblas",
+                                  "-Wl,-rpath,/opt/rocm/lib"])
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
