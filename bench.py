@@ -15,8 +15,8 @@ fraction of the published peak that bounds it:
   * cfg3  prefill, Q5_K and Q6_K on [8192, 2048] and [2048, 8192] at M = 8,
           64, 128, 256, 512, 2048, residual fused;
   * cfg4  MoE: Q6_K experts, 128 experts, top-8, 256 tokens, Zipf(1.1)
-          routing: bucketing + one grouped launch for gate/up [768, 2048] and
-          for down [2048, 768];
+          routing: gate/up [768, 2048] (bucketing + grouped FC) then down
+          [2048, 768] on the same routing's bucketing (grouped FC only);
   * the widened paths (Q4_K decode and prefill, f32 activations).
 Every case is one phase of the step: a HIP graph of launches over distinct
 device copies of its weights (at least 1 GiB of them per decode shape, 0.5
@@ -417,7 +417,8 @@ def pmc_prefill_target(dev):
 
 def pmc_moe_target(dev):
     """Counter-collection target for the grouped path: the benchmark's first
-    routing and weight copy, gate/up then down, three eager calls each."""
+    routing and weight copy, gate/up then down (on gate/up's bucketing),
+    three eager rounds."""
     import torch
     from gguf_quant_block_amd import synth
     from gguf_quant_block_amd.binding import FcGguf
@@ -425,16 +426,22 @@ def pmc_moe_target(dev):
     E, T, top_k = m["E"], m["T"], m["top_k"]
     ids = torch.from_numpy(synth.moe_routing(T, E, top_k, synth.rng(5, 0, synth.TAG_ROUTING),
                                              s=m["zipf_s"])).to(dev)
+    fcs = []
     for fi, (which, per_slot) in enumerate((("gate_up", False), ("down", True))):
         N, K = m[which]
         w = torch.from_numpy(synth.q6k_blocks(E * N, K, synth.rng(5, fi, synth.TAG_BLOCKS))).to(dev)
-        fc = FcGguf(N, K, "q6_k", w, experts=E)
+        fcs.append((FcGguf(N, K, "q6_k", w, experts=E), per_slot, N, K))
+    calls = []
+    for fc, per_slot, N, K in fcs:
         shape = (T, top_k, K) if per_slot else (T, K)
-        A = torch.from_numpy(synth.normal_f16(shape, synth.rng(5, fi, synth.TAG_A))).to(dev)
-        Y = torch.empty((T, top_k, N), dtype=torch.float16, device=dev)
-        for _ in range(3):
-            fc.grouped(A, ids, per_slot, out=Y)
-        torch.cuda.synchronize()
+        A = torch.from_numpy(synth.normal_f16(shape, synth.rng(5, len(calls), synth.TAG_A))).to(dev)
+        calls.append((fc, A, per_slot, torch.empty((T, top_k, N), dtype=torch.float16, device=dev)))
+    for _ in range(3):
+        # gate/up sorts the routing; down runs on its bucketing
+        (up, A0, p0, Y0), (down, A1, p1, Y1) = calls
+        up.grouped(A0, ids, p0, out=Y0)
+        down.grouped(A1, ids, p1, out=Y1, routed=up)
+    torch.cuda.synchronize()
     print("pmc moe target done", flush=True)
 
 
@@ -507,8 +514,8 @@ class Case:
 
     def run(self):
         if self.grouped:
-            for fc, A, ids, per_slot, Y in self.calls:
-                fc.grouped(A, ids, per_slot, out=Y)
+            for fc, A, ids, per_slot, Y, routed in self.calls:
+                fc.grouped(A, ids, per_slot, out=Y, routed=routed)
         else:
             for fc, A, R, Y in self.calls:
                 fc(A, R, out=Y)
@@ -675,6 +682,7 @@ def main():
         ids_np = synth.moe_routing(T, E, top_k, synth.rng(5, c, synth.TAG_ROUTING), s=m["zipf_s"])
         ids = todev(ids_np)
         nonempty = int((np.bincount(ids_np.ravel(), minlength=E) > 0).sum())
+        up = None
         for fi, (which, per_slot) in enumerate((("gate_up", False), ("down", True))):
             N, K = m[which]
             w = todev(synth.q6k_blocks(E * N, K, synth.rng(5, 10 * c + fi, synth.TAG_BLOCKS)))
@@ -683,7 +691,9 @@ def main():
             shape = (T, top_k, K) if per_slot else (T, K)
             A = todev(synth.normal_f16(shape, synth.rng(5, 10 * c + fi, synth.TAG_A)))
             Y = torch.empty((T, top_k, N), dtype=torch.float16, device=dev)
-            moe_calls.append((fc, A, ids, per_slot, Y))
+            # down runs on gate/up's bucketing of the same routing
+            moe_calls.append((fc, A, ids, per_slot, Y, up))
+            up = fc
             eb = N * (K // 256) * 210
             moe_touched += nonempty * eb
             moe_alg += nonempty * eb + A.numel() * 2 + Y.numel() * 2
@@ -692,7 +702,8 @@ def main():
                     flops=moe_flops, grouped=True,
                     info={"note": "gate/up [768,2048] on token rows + down [2048,768] on pair rows, "
                                   f"{MOE_COPIES} weight copies and routings in rotation; launches = calls "
-                                  "(bucketing + grouped FC each)"})
+                                  "(gate/up: bucketing + grouped FC; down: grouped FC on gate/up's "
+                                  "bucketing, fc_gguf_run_grouped_reuse)"})
     cases.append(moe_case)
 
     # ---- widened paths: Q4_K decode (M = 1) and prefill (M = 512); f32 decode ----

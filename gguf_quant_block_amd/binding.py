@@ -35,6 +35,8 @@ _SIGS = {
     "fc_gguf_run_grouped": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp]),
     "fc_gguf_run_grouped_noalloc": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, ctypes.c_int, _vp,
                                                    _vp]),
+    "fc_gguf_run_grouped_reuse": (ctypes.c_int, [_vp, _vp, _vp, _c_i64, ctypes.c_int, _vp, ctypes.c_int,
+                                                 _vp, _vp]),
     "fc_gguf_set_path": (ctypes.c_int, [_vp, ctypes.c_int]),
     "fc_gguf_destroy": (ctypes.c_int, [_vp]),
     "fc_gguf_info": (ctypes.c_int, [_vp, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64),
@@ -169,19 +171,30 @@ class FcGguf:
         _check(run(self._h, _ptr(A2), M, _ptr(R), _ptr(out), _stream()), "fc_gguf_run")
         return out
 
-    def grouped(self, A, ids, a_per_slot: bool, out=None, noalloc: bool = False):
+    def grouped(self, A, ids, a_per_slot: bool, out=None, noalloc: bool = False, routed=None):
         """MoE: Y[t, j] = A_row(t, j) . W_{ids[t, j]}^T; A f16 [T, K] or [T, top_k, K].
-        noalloc: fc_gguf_run_grouped_noalloc (the library's static scratch, no allocation)."""
+        noalloc: fc_gguf_run_grouped_noalloc (the library's static scratch, no allocation).
+        routed: a grouped FcGguf whose last grouped() call had this same ids tensor:
+        fc_gguf_run_grouped_reuse (its expert bucketing, not sorted again)."""
         torch = _torch()
         assert self.experts is not None, "grouped() needs a handle made with experts=E"
         T, top_k = ids.shape
         assert ids.is_cuda and A.is_cuda and A.dtype == torch.float16
         assert A.shape == ((T, top_k, self.K) if a_per_slot else (T, self.K))
+        if routed is not None:
+            # the same ids memory as the routed call's: no conversion copy
+            assert ids.dtype == torch.int32 and ids.is_contiguous(), "ids: contiguous int32"
         ids = ids.to(torch.int32).contiguous()
         A = A.contiguous()
         if out is None:
             out = torch.empty((T, top_k, self.N), dtype=torch.float16, device=A.device)
         assert out.is_contiguous() and out.dtype == torch.float16 and out.shape == (T, top_k, self.N)
+        if routed is not None:
+            assert not noalloc
+            _check(lib().fc_gguf_run_grouped_reuse(self._h, routed.handle, _ptr(A), T, 1 if a_per_slot else 0,
+                                                   _ptr(ids), top_k, _ptr(out), _stream()),
+                   "fc_gguf_run_grouped_reuse")
+            return out
         run = lib().fc_gguf_run_grouped_noalloc if noalloc else lib().fc_gguf_run_grouped
         _check(run(self._h, _ptr(A), T, 1 if a_per_slot else 0, _ptr(ids), top_k, _ptr(out), _stream()),
                "fc_gguf_run_grouped_noalloc" if noalloc else "fc_gguf_run_grouped")

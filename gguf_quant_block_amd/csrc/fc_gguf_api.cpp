@@ -30,6 +30,11 @@ struct fc_gguf {
                                 // dequantised f16 weights of the scratch path, the int8
                                 // path's quantised activations)
   size_t ws_bytes = 0;
+  // the routing whose bucketing the workspace holds (set by a completed
+  // fc_gguf_run_grouped launch; read by fc_gguf_run_grouped_reuse)
+  const int32_t* routed_ids = nullptr;
+  int64_t routed_T = 0;
+  int routed_top_k = 0;
   rocblas_handle blas = nullptr;  // created on the first scratch-path call
   hipError_t last = hipSuccess;
 };
@@ -277,12 +282,13 @@ int check_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, const i
   return FC_GGUF_OK;
 }
 
-// The bucketing and grouped-FC launches with the bucketing workspace `ws`.
+// The bucketing (if `bucket`) and grouped-FC launches with the bucketing
+// workspace `ws`.
 int launch_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, const int32_t* ids,
-                   int top_k, void* Y, void* ws, hipStream_t st) {
+                   int top_k, void* Y, void* ws, bool bucket, hipStream_t st) {
   hipError_t e = fcg::launch_moe(h->qtype, h->w, h->expert_bytes, (int)h->E, (int)h->N, (int)h->K,
                                  (const fcg::f16*)A, (int)T, a_per_slot, ids, top_k, (fcg::f16*)Y,
-                                 ws, h->num_cu, st);
+                                 ws, bucket, st);
   if (e == hipErrorNotSupported) return FC_GGUF_EUNSUPPORTED;
   if (e != hipSuccess) return hip_fail(h, e);
   return FC_GGUF_OK;
@@ -417,10 +423,28 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot, c
                         int top_k, void* Y, void* stream) {
   int rc = check_grouped(h, A, T, a_per_slot, ids, top_k, Y);
   if (rc != FC_GGUF_OK || T == 0) return rc;
+  h->routed_ids = nullptr;                          // the workspace is about to change
   const size_t need = fcg::moe_workspace_bytes((int)h->E, (int)T, top_k);
   rc = ensure_ws(h, need, (hipStream_t)stream);
   if (rc != FC_GGUF_OK) return rc;
-  return launch_grouped(h, A, T, a_per_slot, ids, top_k, Y, h->ws, (hipStream_t)stream);
+  rc = launch_grouped(h, A, T, a_per_slot, ids, top_k, Y, h->ws, true, (hipStream_t)stream);
+  if (rc == FC_GGUF_OK) {
+    h->routed_ids = ids;
+    h->routed_T = T;
+    h->routed_top_k = top_k;
+  }
+  return rc;
+}
+
+int fc_gguf_run_grouped_reuse(fc_gguf_t h, fc_gguf_t routed, const void* A, int64_t T,
+                              int a_per_slot, const int32_t* ids, int top_k, void* Y,
+                              void* stream) {
+  int rc = check_grouped(h, A, T, a_per_slot, ids, top_k, Y);
+  if (rc != FC_GGUF_OK || T == 0) return rc;
+  if (!routed || routed->E != h->E || routed->device != h->device || routed->routed_ids != ids ||
+      routed->routed_T != T || routed->routed_top_k != top_k)
+    return FC_GGUF_EINVAL;
+  return launch_grouped(h, A, T, a_per_slot, ids, top_k, Y, routed->ws, false, (hipStream_t)stream);
 }
 
 int fc_gguf_run_grouped_noalloc(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
@@ -431,7 +455,7 @@ int fc_gguf_run_grouped_noalloc(fc_gguf_t h, const void* A, int64_t T, int a_per
   void* ws = nullptr;
   rc = scratch_ptr(h->device, &ws);
   if (rc != FC_GGUF_OK) return rc;
-  return launch_grouped(h, A, T, a_per_slot, ids, top_k, Y, ws, (hipStream_t)stream);
+  return launch_grouped(h, A, T, a_per_slot, ids, top_k, Y, ws, true, (hipStream_t)stream);
 }
 
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s, int32_t* T,

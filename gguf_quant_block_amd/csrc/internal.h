@@ -81,7 +81,9 @@ hipError_t launch_prefill_i8(int qtype, const uint8_t* W, const f16* A, const f1
 // grouped (MoE) path
 constexpr int MOE_MAX_E = 4096;   // experts per grouped handle (bucketing counts live in LDS)
 size_t moe_workspace_bytes(int E, int T, int top_k);
+// bucket: run the bucketing into ws first; false: ws already holds the
+// bucketing of the same routing (E, T, top_k, ids)
 hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, int N, int K,
                       const f16* A, int T, int a_per_slot, const int32_t* ids, int top_k, f16* Y,
-                      void* ws, int num_cu, hipStream_t st);
+                      void* ws, bool bucket, hipStream_t st);
 }  // namespace fcg

@@ -10,14 +10,18 @@
 //
 // Two launches on the caller's stream:
 //   1. moe_bucket_kernel (one workgroup): counting sort of the (token, slot)
-//      pairs by expert id -> offsets[E+1] and the pair list, then the tile
-//      list: one entry (expert, first row) per BM routed rows of an expert.
-//      Pairs with an id outside [0, E) get zero output rows.
+//      pairs by expert id -> offsets[E+2] and the pair list, then the tile
+//      list: one entry (bucket, first row) per BM routed rows of a bucket.
+//      Buckets 0..E-1 are the experts; bucket E holds the pairs whose id is
+//      outside [0, E).  The bucketing depends on the routing only, so a
+//      second grouped FC with the same routing (the down projection after
+//      gate/up) can run on it without sorting again.
 //   2. moe_grouped_kernel: one workgroup per (tile, weight-row tile); the
 //      grid is sized for the largest possible tile count (known on the host
 //      without reading the routing) and workgroups past the real count exit
 //      at once.  Rows are gathered through the pair list: token t = p / top_k
-//      reads A[t] (shared rows) or A[p] (one row per pair), and writes Y[p].
+//      reads A[t] (shared rows) or A[p] (one row per pair), and writes Y[p];
+//      the tiles of bucket E write zero rows.
 // The order of the pairs inside one expert's range is unspecified (atomic
 // cursors), so the tile and the position within it that a row lands in vary
 // from call to call.  Results do not: every output row depends only on its
@@ -42,13 +46,14 @@ constexpr int MOE_SH = 2;                  // half super-blocks per stage
 // nothing, while a tall expert decodes its weights fewer times.
 static int moe_mt(int E, long long P) { return P < 8LL * E ? 2 : (P >= 64LL * E ? 8 : 4); }
 
+// tiles of E + 1 buckets holding P pairs in all, at most
 static long long moe_max_tiles(int E, long long P, int BM) {
-  return (P + BM - 1) / BM + (E < P ? E : P);
+  return (P + BM - 1) / BM + (E + 1 < P ? E + 1 : P);
 }
 
 struct MoeWs {
   int2* tiles;      // [max_tiles] (expert, first row within the expert)
-  int* offsets;     // [E + 1]
+  int* offsets;     // [E + 2]: bucket b's pairs are pairs[offsets[b] .. offsets[b+1])
   int* pairs;       // [P] pair index p = t * top_k + j, grouped by expert
   int* ntiles;      // [1]
 };
@@ -57,7 +62,7 @@ static MoeWs moe_ws(void* ws, int E, long long P, long long max_tiles) {
   MoeWs w;
   w.tiles = (int2*)ws;
   w.offsets = (int*)(w.tiles + max_tiles);
-  w.pairs = w.offsets + (E + 1);
+  w.pairs = w.offsets + (E + 2);
   w.ntiles = w.pairs + P;
   return w;
 }
@@ -65,7 +70,7 @@ static MoeWs moe_ws(void* ws, int E, long long P, long long max_tiles) {
 size_t moe_workspace_bytes(int E, int T, int top_k) {
   const long long P = (long long)T * top_k;
   const long long mt = moe_max_tiles(E, P, 16 * moe_mt(E, P));
-  return (size_t)mt * sizeof(int2) + (size_t)(E + 1 + P + 1) * sizeof(int);
+  return (size_t)mt * sizeof(int2) + (size_t)(E + 2 + P + 1) * sizeof(int);
 }
 
 // exclusive scan of one int per thread over the workgroup; returns the
@@ -96,28 +101,29 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return before + x - v;
 }
 
+// bucket of routing id e: the expert, or E for an id outside [0, E)
+__device__ __forceinline__ int moe_bucket(int e, int E) { return (unsigned)e < (unsigned)E ? e : E; }
+
 __global__ void __launch_bounds__(MOE_BUCKET_THREADS)
-moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM, int N,
-                  f16* __restrict__ Y, int2* __restrict__ tiles, int* __restrict__ offsets,
+moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM,
+                  int2* __restrict__ tiles, int* __restrict__ offsets,
                   int* __restrict__ pairs, int* __restrict__ ntiles) {
-  __shared__ int cnt[MOE_MAX_E];          // rows per expert, then the scatter cursors
+  __shared__ int cnt[MOE_MAX_E + 1];      // rows per bucket, then the scatter cursors
   __shared__ int wsum[2][MOE_BUCKET_THREADS / 64];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += MOE_BUCKET_THREADS) cnt[e] = 0;
+  const int NB = E + 1;                   // buckets
+  for (int b = tid; b < NB; b += MOE_BUCKET_THREADS) cnt[b] = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += MOE_BUCKET_THREADS) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
-  }
+  for (int p = tid; p < P; p += MOE_BUCKET_THREADS) atomicAdd(&cnt[moe_bucket(ids[p], E)], 1);
   __syncthreads();
 
-  // each thread owns a contiguous run of experts; scan rows and tiles
-  const int per = (E + MOE_BUCKET_THREADS - 1) / MOE_BUCKET_THREADS;
+  // each thread owns a contiguous run of buckets; scan rows and tiles
+  const int per = (NB + MOE_BUCKET_THREADS - 1) / MOE_BUCKET_THREADS;
   const int e0 = tid * per;
   int rows = 0, tl = 0;
   for (int q = 0; q < per; ++q) {
     const int e = e0 + q;
-    if (e < E) {
+    if (e < NB) {
       rows += cnt[e];
       tl += (cnt[e] + BM - 1) / BM;
     }
@@ -127,7 +133,7 @@ moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM, int N,
   int tbase = block_exclusive_scan(tl, wsum[1], &tiles_total);
   for (int q = 0; q < per; ++q) {
     const int e = e0 + q;
-    if (e >= E) break;
+    if (e >= NB) break;
     const int c = cnt[e];
     offsets[e] = rbase;
     for (int r0 = 0; r0 < c; r0 += BM) tiles[tbase++] = make_int2(e, r0);
@@ -135,20 +141,12 @@ moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM, int N,
     rbase += c;
   }
   if (tid == 0) {
-    offsets[E] = rows_total;
+    offsets[NB] = rows_total;
     *ntiles = tiles_total;
   }
   __syncthreads();
 
-  for (int p = tid; p < P; p += MOE_BUCKET_THREADS) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) {
-      pairs[atomicAdd(&cnt[e], 1)] = p;
-    } else {
-      f16* y = Y + (size_t)p * N;
-      for (int n = 0; n < N; ++n) y[n] = (f16)0.f;
-    }
-  }
+  for (int p = tid; p < P; p += MOE_BUCKET_THREADS) pairs[atomicAdd(&cnt[moe_bucket(ids[p], E)], 1)] = p;
 }
 
 template <int QT, int MT, int NT>
@@ -156,7 +154,7 @@ __global__ void __launch_bounds__(256)
 moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
                    f16* __restrict__ Y, const int2* __restrict__ tiles,
                    const int* __restrict__ offsets, const int* __restrict__ pairs,
-                   const int* __restrict__ ntiles, int N, int K, int top_k, int a_per_slot,
+                   const int* __restrict__ ntiles, int E, int N, int K, int top_k, int a_per_slot,
                    int max_tiles, int tiles_n) {
   constexpr int BM = 16 * MT;
   constexpr int BN = 64 * NT;
@@ -184,6 +182,19 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
   const int n0 = nt * BN;
 
   const int tid = threadIdx.x;
+  if (e == E) {
+    // pairs routed to no expert: zero output rows (this workgroup's columns)
+    for (int i = tid; i < cnt * (BN / 4); i += 256) {
+      const int r = i / (BN / 4), n = n0 + 4 * (i % (BN / 4));
+      f16* y = Y + (size_t)pairs[base + r] * N;
+      if (n + 4 <= N && (N & 3) == 0) {
+        *(uint2*)(y + n) = make_uint2(0u, 0u);
+      } else {
+        for (int c = n; c < n + 4 && c < N; ++c) y[c] = (f16)0.f;
+      }
+    }
+    return;
+  }
   const int lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4;
 
@@ -224,34 +235,35 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
 
 template <int QT, int MT>
 static hipError_t launch_grouped_t(const uint8_t* W, size_t expert_bytes, const f16* A, f16* Y,
-                                   const MoeWs& w, int N, int K, int top_k, int a_per_slot,
+                                   const MoeWs& w, int E, int N, int K, int top_k, int a_per_slot,
                                    int max_tiles, hipStream_t st) {
   constexpr int BN = 64 * MOE_NT;
   const int tiles_n = (N + BN - 1) / BN;
   const long long grid = (long long)max_tiles * tiles_n;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((moe_grouped_kernel<QT, MT, MOE_NT>), dim3((unsigned)grid), dim3(256), 0, st,
-                     W, expert_bytes, A, Y, w.tiles, w.offsets, w.pairs, w.ntiles, N, K, top_k,
+                     W, expert_bytes, A, Y, w.tiles, w.offsets, w.pairs, w.ntiles, E, N, K, top_k,
                      a_per_slot, max_tiles, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, int N, int K,
                       const f16* A, int T, int a_per_slot, const int32_t* ids, int top_k, f16* Y,
-                      void* ws, int num_cu, hipStream_t st) {
-  (void)num_cu;
+                      void* ws, bool bucket, hipStream_t st) {
   if (E > MOE_MAX_E) return hipErrorInvalidValue;
   const long long P = (long long)T * top_k;
   const int mt = moe_mt(E, P);
   const int BM = 16 * mt;
   const long long max_tiles = moe_max_tiles(E, P, BM);
   const MoeWs w = moe_ws(ws, E, P, max_tiles);
-  hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(MOE_BUCKET_THREADS), 0, st, ids, (int)P, E,
-                     BM, N, Y, w.tiles, w.offsets, w.pairs, w.ntiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (bucket) {
+    hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(MOE_BUCKET_THREADS), 0, st, ids, (int)P, E,
+                       BM, w.tiles, w.offsets, w.pairs, w.ntiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 #define FCG_MOE(QT_, MT_) \
-  if (mt == MT_) return launch_grouped_t<QT_, MT_>(W, expert_bytes, A, Y, w, N, K, top_k, a_per_slot, (int)max_tiles, st);
+  if (mt == MT_) return launch_grouped_t<QT_, MT_>(W, expert_bytes, A, Y, w, E, N, K, top_k, a_per_slot, (int)max_tiles, st);
   if (qtype == QT_Q4K) {
     FCG_MOE(QT_Q4K, 2) FCG_MOE(QT_Q4K, 4) FCG_MOE(QT_Q4K, 8)
   } else if (qtype == QT_Q5K) {

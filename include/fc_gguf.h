@@ -176,6 +176,23 @@ int fc_gguf_run_grouped(fc_gguf_t h, const void* A, int64_t T, int a_per_slot,
                         const int32_t* ids, int top_k, void* Y, void* stream);
 
 /*
+ * fc_gguf_run_grouped on the expert bucketing that the last
+ * fc_gguf_run_grouped call on `routed` computed, without sorting the routing
+ * again: for a second grouped FC with the same routing, such as the down
+ * projection after gate/up (llama.cpp PR #28301, section Overview: the rows
+ * are grouped by expert once per routing).  `routed` is a grouped handle
+ * with the same expert count on the same device whose last
+ * fc_gguf_run_grouped call had these same `ids` (the same pointer, holding
+ * the same values), T and top_k; otherwise FC_GGUF_EINVAL.  The bucketing is
+ * read from `routed`'s workspace, so this call must be ordered after that
+ * one (the same stream) and before the next grouped call on `routed`.  h may
+ * be `routed` itself.  Other arguments and results as fc_gguf_run_grouped.
+ */
+int fc_gguf_run_grouped_reuse(fc_gguf_t h, fc_gguf_t routed, const void* A, int64_t T,
+                              int a_per_slot, const int32_t* ids, int top_k, void* Y,
+                              void* stream);
+
+/*
  * fc_gguf_run_grouped without any allocation, for callers that cannot
  * allocate device memory (code being captured into a HIP graph, tight serving
  * loops, harnesses that forbid hipMalloc): the same arguments, kernels and

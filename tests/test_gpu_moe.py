@@ -211,3 +211,71 @@ def test_moe_random(gpu_lib, seed):
     assert np.isfinite(y).all()
     check_fro(y, ofc.moe_ref(A, w, qtype, ids, a_per_slot))
     _check_experts(y, w, qtype, A, ids, a_per_slot, np.unique(ids))
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_moe_reuse_routing(gpu_lib, qtype):
+    # gate/up then down with the same routing: the down call on the gate/up
+    # call's bucketing (fc_gguf_run_grouped_reuse) is bit-identical to a
+    # fresh down call, including the zero rows of invalid ids
+    import torch
+    from gguf_quant_block_amd.binding import FcGguf
+    E, T, top_k = 12, 70, 3
+    (N1, K1), (N2, K2) = (192, 512), (96, 768)
+    w1, A1, ids = _moe_case(qtype, E, N1, K1, T, top_k, False, 46, 0)
+    w2 = synth.blocks(qtype, E * N2, K2, synth.rng(46, 1, synth.TAG_BLOCKS)).reshape(E, N2, -1)
+    A2 = synth.normal_f16((T, top_k, K2), synth.rng(46, 1, synth.TAG_A))
+    ids[5, 2] = -3
+    ids[9, 0] = E + 1
+    up = FcGguf(N1, K1, qtype, w1, experts=E)
+    down = FcGguf(N2, K2, qtype, w2, experts=E)
+    idd, A1d, A2d = _dev(ids), _dev(A1), _dev(A2)
+    up.grouped(A1d, idd, False)
+    y_reuse, ok = guarded((T, top_k, N2), torch.float16, seed=9)
+    y_reuse.fill_(float("nan"))
+    down.grouped(A2d, idd, True, out=y_reuse, routed=up)
+    ok()
+    y_fresh = down.grouped(A2d, idd, True)
+    torch.cuda.synchronize()
+    assert torch.equal(y_reuse, y_fresh)
+    y = _host(y_reuse)
+    assert np.all(y[5, 2] == 0) and np.all(y[9, 0] == 0)
+    check_fro(y, ofc.moe_ref(A2, w2, qtype, ids, True))
+    # a handle may reuse its own bucketing
+    y_self = down.grouped(A2d, idd, True, routed=down)
+    torch.cuda.synchronize()
+    assert torch.equal(y_self, y_fresh)
+
+
+def test_moe_reuse_checks(gpu_lib):
+    import ctypes
+    import torch
+    from gguf_quant_block_amd.binding import FcGguf, FcGgufError, lib
+    E, N, K, T, top_k = 8, 64, 256, 20, 2
+    w, A, ids = _moe_case("q4_k", E, N, K, T, top_k, False, 47, 0)
+    a = FcGguf(N, K, "q4_k", w, experts=E)
+    b = FcGguf(N, K, "q4_k", w, experts=E)
+    other = FcGguf(N, K, "q4_k", np.concatenate([w, w]).reshape(2 * E, N, -1), experts=2 * E)
+    Ad, idd = _dev(A), _dev(ids)
+    idd2 = idd.clone()
+    Y = torch.empty((T, top_k, N), dtype=torch.float16, device="cuda")
+    with pytest.raises(FcGgufError):            # a has not run yet
+        b.grouped(Ad, idd, False, out=Y, routed=a)
+    a.grouped(Ad, idd, False)
+    b.grouped(Ad, idd, False, out=Y, routed=a)  # fine
+
+    def reuse(h, routed, T_, ids_, k_):
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return lib().fc_gguf_run_grouped_reuse(h.handle, routed, ctypes.c_void_p(Ad.data_ptr()), T_, 0,
+                                               ctypes.c_void_p(ids_.data_ptr()), k_,
+                                               ctypes.c_void_p(Y.data_ptr()), st)
+    assert reuse(b, a.handle, T, idd, top_k) == 0
+    assert reuse(b, a.handle, T, idd2, top_k) == -1       # another ids buffer
+    assert reuse(b, a.handle, T - 1, idd, top_k) == -1    # another token count
+    assert reuse(b, a.handle, T, idd, 1) == -1            # another top_k
+    assert reuse(b, other.handle, T, idd, top_k) == -1    # another expert count
+    assert reuse(b, None, T, idd, top_k) == -1
+    a.grouped(Ad, idd2, False)                            # a's bucketing now follows idd2
+    assert reuse(b, a.handle, T, idd, top_k) == -1
+    assert reuse(b, a.handle, T, idd2, top_k) == 0
+    torch.cuda.synchronize()
