@@ -32,7 +32,7 @@ int8 matrix-core instructions), the dequantise-once and int8 comparison
 paths, and the CPU oracle timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       python bench.py --pmc-target | --pmc-prefill-target | --pmc-moe-target
+       python bench.py --pmc-target | --pmc-prefill-target | --pmc-moe-target | --pmc-int8-target
        python bench.py --traffic-summary FETCH_CSV WRITE_CSV
 """
 
@@ -445,6 +445,27 @@ def pmc_moe_target(dev):
     print("pmc moe target done", flush=True)
 
 
+def pmc_int8_target(dev):
+    """Counter-collection target for the int8 matrix-core prefill variant:
+    the Q5_K FC on [8192, 2048] at M = 512 on the int8 path, ten eager
+    launches (each: quant_i8_kernel, then prefill_i8_kernel)."""
+    import torch
+    from gguf_quant_block_amd import synth
+    from gguf_quant_block_amd.binding import FcGguf
+    N, K = synth.PREFILL_SHAPES[0]
+    M = 512
+    w = torch.from_numpy(synth.q5k_blocks(N, K, synth.rng(2, 0, synth.TAG_BLOCKS))).to(dev)
+    A = torch.from_numpy(synth.normal_f16((M, K), synth.rng(2, 0, synth.TAG_A))).to(dev)
+    R = torch.from_numpy(synth.normal_f16((M, N), synth.rng(2, 0, synth.TAG_R))).to(dev)
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    fc = FcGguf(N, K, "q5_k", w)
+    fc.set_path("int8")
+    for _ in range(10):
+        fc(A, R, out=Y)
+    torch.cuda.synchronize()
+    print("pmc int8 target done", flush=True)
+
+
 CALIB_BYTES = 256 << 20
 
 
@@ -460,10 +481,11 @@ def traffic_summary(fetch_csv, write_csv):
         gemv, calib = [], []
         with open(path) as f:
             rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id") or 0))
         for r in rows:
             v = float(r["Counter_Value"]) * 1024.0
             if "gemv_kernel" in r["Kernel_Name"]:
-                gemv.append((int(r["Grid_Size"]), v))
+                gemv.append((len(gemv), v))
             elif "copyBuffer" in r["Kernel_Name"]:
                 calib.append(v)
         return gemv, calib
@@ -476,9 +498,11 @@ def traffic_summary(fetch_csv, write_csv):
     fetch = sum(v for _, v in fg) / len(fg) * f_factor
     write = sum(v for _, v in wg) / len(wg) * w_factor
     alg = sum(N * (K // 256) * 176 + 2 * K + 4 * N for N, K in synth.PHI35_LAYERS.values()) / len(synth.PHI35_LAYERS)
-    per_grid = {}
-    for (g, fv), (_, wv) in zip(fg, wg):
-        per_grid.setdefault(g, []).append(fv * f_factor + wv * w_factor)
+    # --pmc-target dispatches, per pass, 4 launches of each shape in layer order
+    names = list(synth.PHI35_LAYERS)
+    per_shape = {}
+    for (i, fv), (_, wv) in zip(fg, wg):
+        per_shape.setdefault(names[(i % (4 * len(names))) // 4], []).append(fv * f_factor + wv * w_factor)
     rec = {
         "kernel": "gemv_kernel<Q5_K, M=1>",
         "workload": "Q5_K decode GEMV at M=1 over the Phi-3.5-mini layer set, equal mix of the four shapes",
@@ -491,7 +515,7 @@ def traffic_summary(fetch_csv, write_csv):
         "hbm_bytes_per_launch": round(fetch + write),
         "algorithmic_bytes_per_launch": round(alg),
         "traffic_over_algorithmic": round((fetch + write) / alg, 4),
-        "hbm_bytes_per_launch_by_grid": {str(g): round(sum(v) / len(v)) for g, v in sorted(per_grid.items())},
+        "hbm_bytes_per_launch_by_shape": {k: round(sum(v) / len(v)) for k, v in per_shape.items()},
     }
     out = os.path.join(ROOT, "profiles", "decode_gemv_q5k_m1_traffic.json")
     with open(out, "w") as f:
@@ -566,6 +590,9 @@ def main():
     ap.add_argument("--pmc-moe-target", action="store_true",
                     help="run the benchmark's Q6_K grouped calls (gate/up, down) three times each "
                          "eagerly, for rocprofv3 --pmc counter passes over the grouped kernel")
+    ap.add_argument("--pmc-int8-target", action="store_true",
+                    help="run the int8 prefill variant (Q5_K [8192, 2048], M = 512) ten times eagerly, "
+                         "for rocprofv3 --pmc counter passes")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from the two counter passes over --pmc-target")
     args = ap.parse_args()
@@ -596,6 +623,9 @@ def main():
         return
     if args.pmc_moe_target:
         pmc_moe_target(dev)
+        return
+    if args.pmc_int8_target:
+        pmc_int8_target(dev)
         return
 
     def log(msg):
