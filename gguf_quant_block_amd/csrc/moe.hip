@@ -73,30 +73,33 @@ size_t moe_workspace_bytes(int E, int T, int top_k) {
   return (size_t)mt * sizeof(int2) + (size_t)(E + 2 + P + 1) * sizeof(int);
 }
 
-// exclusive scan of one int per thread over the workgroup; returns the
-// thread's prefix and writes the total to *total
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+// exclusive scan of one 64-bit value per thread over the workgroup (two
+// 32-bit counts packed, neither of which can carry into the other); returns
+// the thread's prefix and writes the total to *total
+__device__ __forceinline__ unsigned long long block_exclusive_scan(unsigned long long v,
+                                                                  unsigned long long* wsum,
+                                                                  unsigned long long* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  int x = v;
+  unsigned long long x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
+    const unsigned long long y = __shfl_up(x, d, 64);
     if (lane >= d) x += y;
   }
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int s = lane < nw ? wsum[lane] : 0;
+    unsigned long long t = lane < nw ? wsum[lane] : 0ull;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(s, d, 64);
-      if (lane >= d) s += y;
+      const unsigned long long y = __shfl_up(t, d, 64);
+      if (lane >= d) t += y;
     }
-    if (lane < nw) wsum[lane] = s;          // inclusive wave totals
+    if (lane < nw) wsum[lane] = t;          // inclusive wave totals
   }
   __syncthreads();
-  const int before = wave > 0 ? wsum[wave - 1] : 0;
+  const unsigned long long before = wave > 0 ? wsum[wave - 1] : 0ull;
   *total = wsum[nw - 1];
   return before + x - v;
 }
@@ -104,23 +107,36 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
 // bucket of routing id e: the expert, or E for an id outside [0, E)
 __device__ __forceinline__ int moe_bucket(int e, int E) { return (unsigned)e < (unsigned)E ? e : E; }
 
+constexpr int MOE_IDS_PT = 4;   // routing ids a thread keeps in registers between the two passes
+
 __global__ void __launch_bounds__(MOE_BUCKET_THREADS)
 moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM,
                   int2* __restrict__ tiles, int* __restrict__ offsets,
                   int* __restrict__ pairs, int* __restrict__ ntiles) {
   __shared__ int cnt[MOE_MAX_E + 1];      // rows per bucket, then the scatter cursors
-  __shared__ int wsum[2][MOE_BUCKET_THREADS / 64];
+  __shared__ unsigned long long wsum[MOE_BUCKET_THREADS / 64];
   const int tid = threadIdx.x;
   const int NB = E + 1;                   // buckets
+  // the thread's first MOE_IDS_PT pairs' buckets, loaded once
+  int bk[MOE_IDS_PT];
+#pragma unroll
+  for (int i = 0; i < MOE_IDS_PT; ++i) {
+    const int p = tid + i * MOE_BUCKET_THREADS;
+    bk[i] = p < P ? moe_bucket(ids[p], E) : 0;
+  }
   for (int b = tid; b < NB; b += MOE_BUCKET_THREADS) cnt[b] = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += MOE_BUCKET_THREADS) atomicAdd(&cnt[moe_bucket(ids[p], E)], 1);
+#pragma unroll
+  for (int i = 0; i < MOE_IDS_PT; ++i)
+    if (tid + i * MOE_BUCKET_THREADS < P) atomicAdd(&cnt[bk[i]], 1);
+  for (int p = tid + MOE_IDS_PT * MOE_BUCKET_THREADS; p < P; p += MOE_BUCKET_THREADS)
+    atomicAdd(&cnt[moe_bucket(ids[p], E)], 1);
   __syncthreads();
 
-  // each thread owns a contiguous run of buckets; scan rows and tiles
+  // each thread owns a contiguous run of buckets; one scan of (rows, tiles)
   const int per = (NB + MOE_BUCKET_THREADS - 1) / MOE_BUCKET_THREADS;
   const int e0 = tid * per;
-  int rows = 0, tl = 0;
+  unsigned rows = 0, tl = 0;
   for (int q = 0; q < per; ++q) {
     const int e = e0 + q;
     if (e < NB) {
@@ -128,9 +144,10 @@ moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM,
       tl += (cnt[e] + BM - 1) / BM;
     }
   }
-  int rows_total, tiles_total;
-  int rbase = block_exclusive_scan(rows, wsum[0], &rows_total);
-  int tbase = block_exclusive_scan(tl, wsum[1], &tiles_total);
+  unsigned long long tot;
+  const unsigned long long base =
+      block_exclusive_scan(((unsigned long long)tl << 32) | rows, wsum, &tot);
+  int rbase = (int)(base & 0xFFFFFFFFu), tbase = (int)(base >> 32);
   for (int q = 0; q < per; ++q) {
     const int e = e0 + q;
     if (e >= NB) break;
@@ -141,12 +158,18 @@ moe_bucket_kernel(const int32_t* __restrict__ ids, int P, int E, int BM,
     rbase += c;
   }
   if (tid == 0) {
-    offsets[NB] = rows_total;
-    *ntiles = tiles_total;
+    offsets[NB] = (int)(tot & 0xFFFFFFFFu);
+    *ntiles = (int)(tot >> 32);
   }
   __syncthreads();
 
-  for (int p = tid; p < P; p += MOE_BUCKET_THREADS) pairs[atomicAdd(&cnt[moe_bucket(ids[p], E)], 1)] = p;
+#pragma unroll
+  for (int i = 0; i < MOE_IDS_PT; ++i) {
+    const int p = tid + i * MOE_BUCKET_THREADS;
+    if (p < P) pairs[atomicAdd(&cnt[bk[i]], 1)] = p;
+  }
+  for (int p = tid + MOE_IDS_PT * MOE_BUCKET_THREADS; p < P; p += MOE_BUCKET_THREADS)
+    pairs[atomicAdd(&cnt[moe_bucket(ids[p], E)], 1)] = p;
 }
 
 template <int QT, int MT, int NT>
