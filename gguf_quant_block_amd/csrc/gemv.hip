@@ -27,8 +27,9 @@
 //     sums and the f32 scale algebra remain.  The first unit of the next row
 //     tile is loaded before this row tile's last dots.
 //   * Row sums in a fixed order: over a lane's units, then across the four
-//     lanes of a row (butterfly), then across the waves in wave order; R is
-//     added and the result is rounded once to the output type.
+//     lanes of a row ((b0 + b1) + (b2 + b3), from the lanes' sums in LDS),
+//     then across the waves in wave order; R is added and the result is
+//     rounded once to the output type.
 #include <type_traits>
 
 #include "common.h"
@@ -66,15 +67,16 @@ __host__ __device__ inline int gemv_waves(int K) {
 
 // LDS: qa int8 [MR][KBp] records of QA_REC bytes (256 codes + 16 bytes of
 // padding, so that the four blocks a wave reads at once start on different
-// banks) | rec u32 [MR][KBp][REC] | part f32 [2][waves][MR][16] (a wave's
-// sums for the 16 rows of a row tile; two buffers, alternating over the
+// banks) | rec u32 [MR][KBp][REC] | part f32 [2][waves][MR][16][4] (a wave's
+// sums for the 16 rows of a row tile, one per lane: row, then the lane's
+// block within the 4-block tile; two buffers, alternating over the
 // workgroup's row tiles).
 constexpr int QA_REC = QK + 16;
 template <int QT>
 __host__ __device__ constexpr GemvLayout gemv_layout(int MR, int KBp, int waves) {
   const size_t rec = (size_t)MR * KBp * QA_REC;
   const size_t part = rec + (size_t)MR * KBp * GemvFmt<QT>::REC * 4;
-  const size_t total = part + (size_t)2 * waves * MR * TILE_ROWS * 4;
+  const size_t total = part + (size_t)2 * waves * MR * 64 * 4;
   return GemvLayout{rec, part, total};
 }
 
@@ -102,23 +104,31 @@ __device__ __forceinline__ uint4 act_load(const AT* A, int nch, int c, int wbase
 // Quantise chunk c (held in raw) into LDS: its codes at their place in the
 // (m, kb) code record, and, from the group's first lane (and, for Q6_K, the
 // first lane of its second half), the record entries of the group.
-template <int QT, class AT>
-__device__ __forceinline__ void act_quant(uint4 raw, int c, int nch, int K, int KBp, uint8_t* smem,
-                                          uint32_t* rec) {
+// kb_magic = ceil(2^32 / KB) (KB = K / 256 > 1; 0 for KB = 1): the
+// activation row of a block index b < MR * KB is umulhi(b, kb_magic),
+// exactly, since b < 2^32 / KB.
+template <int QT, int MR, class AT>
+__device__ __forceinline__ void act_quant(uint4 raw, int c, int nch, int K, int KBp,
+                                          uint32_t kb_magic, uint8_t* smem, uint32_t* rec) {
   constexpr int CV = chunk_vals<AT>(), GL = group_lanes<AT>(), REC = GemvFmt<QT>::REC;
   uint32_t q[2];
   float s;
   int tsum, thalf;
   quant_chunk<AT>(raw, q, s, tsum, thalf);
   if (c >= nch) return;
-  const int e = c * CV;                               // first value (flat over MR x K)
-  const int m = e / K, pos = e - m * K;
-  const int kb = pos / QK, off = pos % QK, g = off / 32;
-  uint8_t* dst = smem + (m * KBp + kb) * QA_REC + off;
+  const uint32_t e = (uint32_t)c * CV;                // first value (flat over MR x K)
+  uint32_t m = 0, pos = e;
+  if constexpr (MR > 1) {
+    m = kb_magic ? __umulhi(e / QK, kb_magic) : e / QK;
+    pos = e - __umul24(m, (uint32_t)K);
+  }
+  const uint32_t kb = pos / QK, off = pos % QK, g = off / 32;
+  const uint32_t mk = __umul24(m, (uint32_t)KBp) + kb;  // the (m, kb) record
+  uint8_t* dst = smem + __umul24(mk, (uint32_t)QA_REC) + off;
   if constexpr (CV == 8) *(uint2*)dst = make_uint2(q[0], q[1]);
   else *(uint32_t*)dst = q[0];
-  uint32_t* r = rec + ((size_t)m * KBp + kb) * REC;
-  const int lg = c % GL;                              // lane within the group
+  uint32_t* r = rec + __umul24(mk, (uint32_t)REC);
+  const uint32_t lg = (uint32_t)c % GL;               // lane within the group
   if (lg == 0) r[g] = __builtin_bit_cast(uint32_t, s);
   if constexpr (QT != QT_Q6K) {
     if (lg == 0) r[8 + g] = __builtin_bit_cast(uint32_t, s * (float)tsum);
@@ -277,10 +287,11 @@ __device__ __forceinline__ void dot_unit(const QDec<QT>& o, int q, int kb, int K
                                          const uint8_t* smem, const uint32_t* rec, float* part) {
   if (kb >= KB) return;                               // zero padding block
   constexpr int REC = GemvFmt<QT>::REC;
+  const uint32_t qa0 = __umul24((uint32_t)kb, (uint32_t)QA_REC), r0 = __umul24((uint32_t)kb, (uint32_t)REC);
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    const uint8_t* qa = smem + (m * KBp + kb) * QA_REC;
-    const uint32_t* r = rec + ((size_t)m * KBp + kb) * REC;
+    const uint8_t* qa = smem + qa0 + (uint32_t)(m * KBp * QA_REC);
+    const uint32_t* r = rec + r0 + (uint32_t)(m * KBp * REC);
     if constexpr (QT != QT_Q6K) {
       // values 64q + [0, 32) (group 2q) and 64q + 32 + [0, 32) (group 2q+1)
       const uint4* a = (const uint4*)(qa + 64 * q);
@@ -315,6 +326,19 @@ __device__ __forceinline__ void dot_unit(const QDec<QT>& o, int q, int kb, int K
 }
 
 // ---------------------------------------------------------------- kernel --
+
+// Cross-row lane exchanges on the gfx950 permlane-swap instructions (VALU,
+// no LDS round trip).  lane_xor16_even_rows(x) is x of lane l ^ 16 in the
+// even 16-lane rows (lanes 0-15, 32-47); lane_xor32_low_half(x) is x of lane
+// l + 32 in lanes 0-31.  Other lanes receive values that are not used.
+__device__ __forceinline__ float lane_xor16_even_rows(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_permlane16_swap(u, u, false, false)[1]);
+}
+__device__ __forceinline__ float lane_xor32_low_half(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_permlane32_swap(u, u, false, false)[1]);
+}
 
 // Workgroup barrier after the quantisation: every wave's LDS writes complete
 // (lgkmcnt(0)) before it arrives, while its weight loads stay in flight.
@@ -351,6 +375,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
   float* part_lds = (float*)(smem + Ly.part);
 
   const int nch = act_chunks<AT>(MR, K);
+  const uint32_t kb_magic = KB > 1 ? 0xFFFFFFFFu / (uint32_t)KB + 1u : 0u;
   uint4 araw[QPRE];
 #pragma unroll
   for (int r = 0; r < QPRE; ++r) araw[r] = act_load<AT>(A, nch, r * nt + tid, r * nt + wave * 64);
@@ -374,9 +399,11 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
 
 #pragma unroll
   for (int r = 0; r < QPRE; ++r)
-    if (r * nt + wave * 64 < nch) act_quant<QT, AT>(araw[r], r * nt + tid, nch, K, KBp, smem, rec);
+    if (r * nt + wave * 64 < nch)
+      act_quant<QT, MR, AT>(araw[r], r * nt + tid, nch, K, KBp, kb_magic, smem, rec);
   for (int c0 = QPRE * nt; c0 + wave * 64 < nch; c0 += nt)
-    act_quant<QT, AT>(act_load<AT>(A, nch, c0 + tid, c0 + wave * 64), c0 + tid, nch, K, KBp, smem, rec);
+    act_quant<QT, MR, AT>(act_load<AT>(A, nch, c0 + tid, c0 + wave * 64), c0 + tid, nch, K, KBp,
+                          kb_magic, smem, rec);
   // the first unit's weight side, while the other waves finish quantising
   QDec<QT> dec;
   decode_unit<QT>(cur, q, dec);
@@ -409,17 +436,15 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
     // row sums: the four lanes of a row (kbq = 0..3), then the waves in order
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      part[m] += __shfl_xor(part[m], 16, 64);
-      part[m] += __shfl_xor(part[m], 32, 64);
+      part[m] += lane_xor16_even_rows(part[m]);
+      part[m] += lane_xor32_low_half(part[m]);
     }
-    float* pb = part_lds + (size_t)(i & 1) * nw * MR * TILE_ROWS;
+    float* pb = part_lds + (size_t)(i & 1) * nw * MR * 64;
     if (lane < TILE_ROWS) {
 #pragma unroll
       for (int m = 0; m < MR; ++m) pb[(wave * MR + m) * TILE_ROWS + lane] = part[m];
     }
     __syncthreads();
-    // the final sums: thread t < 16 * MR adds the waves' partial sums of its
-    // (row, column) in wave order
     if (fin) {
       float v[GEMV_MAX_WAVES];
 #pragma unroll

@@ -24,7 +24,7 @@ constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23: x + magic rounds x to 
 // The lanes of a group share it: each lane holds one 16-byte chunk of the
 // group's values (8 f16 values, the group on 4 consecutive lanes; or 4 f32
 // values, on 8 lanes), so that a wave's loads of consecutive chunks are
-// contiguous.  round-half-even(fl32(a * inv)) lands in the low byte of the
+// contiguous; the group's lanes exchange their maxima and sums over DPP.  round-half-even(fl32(a * inv)) lands in the low byte of the
 // result.  The product is rounded to f32 first and only then rounded to an
 // integer (adding 1.5*2^23 rounds to the nearest integer, ties to even, for
 // |x| < 2^22); the empty asm keeps the compiler from fusing the two into one
@@ -33,6 +33,21 @@ __device__ __forceinline__ uint32_t rne_code(float a, float inv) {
   float p = a * inv;
   asm volatile("" : "+v"(p));
   return __builtin_bit_cast(uint32_t, p + RNE_MAGIC);
+}
+
+// Lane exchanges inside the 4 or 8 lanes of a group, on the DPP crossbar
+// (an operand modifier of the consuming instruction; no LDS round trip):
+// xor 1 and xor 2 within an aligned quad, and the mirror of an aligned
+// 8-lane half row (lane i <-> 7 - i), which pairs each lane of one quad with
+// one of the other.  Every lane of the group must be active.
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // row_half_mirror
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
 }
 
 template <class AT>
@@ -68,8 +83,9 @@ __device__ __forceinline__ void quant_chunk(uint4 raw, uint32_t* q, float& s, in
 #pragma unroll
     for (int j = 0; j < 4; ++j) amax = fmaxf(amax, __builtin_bit_cast(float, w[j] & 0x7FFFFFFFu));
   }
-#pragma unroll
-  for (int off = 1; off < GL; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  amax = fmaxf(amax, dpp_f<DPP_XOR1>(amax));
+  amax = fmaxf(amax, dpp_f<DPP_XOR2>(amax));
+  if constexpr (GL == 8) amax = fmaxf(amax, dpp_f<DPP_HALF_MIRROR>(amax));
   float inv = 0.f;
   s = 0.f;
   if (amax > 0.f) {
@@ -90,11 +106,12 @@ __device__ __forceinline__ void quant_chunk(uint4 raw, uint32_t* q, float& s, in
     q[c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     p = dot4((int)q[c], 0x01010101, p);
   }
-  // code sums: over the lanes of the half, then of the group
-#pragma unroll
-  for (int off = 1; off < GL / 2; off <<= 1) p += __shfl_xor(p, off, 64);
+  // code sums: over the lanes of the half (2 or 4 lanes), then of the group
+  p += dpp_i<DPP_XOR1>(p);
+  if constexpr (GL == 8) p += dpp_i<DPP_XOR2>(p);
   thalf = p;
-  tsum = p + __shfl_xor(p, GL / 2, 64);
+  if constexpr (GL == 8) tsum = p + dpp_i<DPP_HALF_MIRROR>(p);
+  else tsum = p + dpp_i<DPP_XOR2>(p);
 }
 
 }  // namespace fcg
