@@ -384,12 +384,21 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
   // tile ahead so that its latency hides under the weight stream
   const int fm = tid / TILE_ROWS, fr = tid % TILE_ROWS;
   const bool fin = tid < TILE_ROWS * MR;
-  auto load_r = [&](int rt) -> float {
+  // (as raw bits, converted where they are added: a conversion right after
+  // the load would make the wave wait for it there)
+  auto load_r = [&](int rt) -> uint32_t {
     const int c = rt * TILE_ROWS + fr;
-    return R && fin ? (float)R[(size_t)fm * N + (c < N ? c : N - 1)] : 0.f;
+    if (!R || !fin) return 0u;
+    const AT* p = R + (size_t)fm * N + (c < N ? c : N - 1);
+    if constexpr (sizeof(AT) == 2) return *(const uint16_t*)p;
+    else return *(const uint32_t*)p;
+  };
+  auto r_value = [](uint32_t bits) -> float {
+    if constexpr (sizeof(AT) == 2) return h2f(bits);
+    else return __builtin_bit_cast(float, bits);
   };
   int rt = blockIdx.x;
-  float rres = load_r(rt);
+  uint32_t rres = load_r(rt);
   asm volatile("" ::: "memory");                    // activation and residual loads first
 
   const UnitAddr ua{W, L.qh_base(), L.sc_base(), L.d_base(), lane};
@@ -427,7 +436,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
     }
     const int rtn = rt + gridDim.x;
     const bool more = rtn < nrt;
-    float rnext = 0.f;
+    uint32_t rnext = 0u;
     if (more) {
       load_unit<QT>(ua, (size_t)rtn * G + g0, q, cur);
       rnext = load_r(rtn);
@@ -454,7 +463,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
 #pragma unroll
       for (int w = 0; w < GEMV_MAX_WAVES; ++w) y += v[w];
       const int c = rt * TILE_ROWS + fr;
-      if (c < N) Y[(size_t)fm * N + c] = (AT)(y + rres);
+      if (c < N) Y[(size_t)fm * N + c] = (AT)(y + r_value(rres));
     }
     if (!more) break;
     rt = rtn;
