@@ -24,6 +24,7 @@ struct fc_gguf {
   int path = FC_GGUF_PATH_AUTO;
   int decode_rows = 8;                // AUTO: M < decode_rows -> decode path
   int prefill_kernel = 0;             // fcg::PREFILL_KERNEL_*: which prefill kernel
+  int tile_mt = 0, tile_splits = 0;   // FC_GGUF_TILE: forced loader-wave tile (0: by M)
   int device = 0;
   int num_cu = 256;
   void* ws = nullptr;           // device workspace (split-K partials, MoE bucketing, the
@@ -89,6 +90,25 @@ int default_prefill_kernel() {
   return fcg::PREFILL_KERNEL_AUTO;
 }
 
+// FC_GGUF_TILE=<mt>,<splits> forces the loader-wave prefill tile (tuning):
+// 16*mt activation rows (mt = 1, 2, 4 or 8) and K in `splits` parts (a power
+// of two from 1 to 64).  Read when a handle is created; anything else, and a
+// split count that would leave a part of K empty for the call's K, leaves
+// the choice to the row count.
+void default_tile(int* mt, int* splits) {
+  *mt = *splits = 0;
+  const char* p = getenv("FC_GGUF_TILE");
+  if (!p || !*p) return;
+  char* end = nullptr;
+  const long m = strtol(p, &end, 10);
+  if (*end != ',') return;
+  const long s = strtol(end + 1, &end, 10);
+  if (*end != '\0') return;
+  if ((m != 1 && m != 2 && m != 4 && m != 8) || s < 1 || s > 64 || (s & (s - 1))) return;
+  *mt = (int)m;
+  *splits = (int)s;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // FC_GGUF_TEST_FAIL_ALLOC names allocations that fail on purpose, so that
@@ -149,6 +169,7 @@ int create_impl(int64_t E, int64_t N, int64_t K, int qtype, const void* blocks, 
   h->path = default_path();
   h->decode_rows = default_decode_rows();
   h->prefill_kernel = default_prefill_kernel();
+  default_tile(&h->tile_mt, &h->tile_splits);
   hipError_t e = hipGetDevice(&h->device);
   if (e == hipSuccess)
     e = hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device);
@@ -396,8 +417,17 @@ int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, v
     if (rc != FC_GGUF_OK) return rc;
     e = fcg::launch_prefill_i8(h->qtype, h->w, a, r, y, h->ws, (int)M, N, K, mt, splits, st);
   } else {
-    const fcg::PrefillPlan plan = fcg::prefill_plan(h->qtype, (int)M, N, K, h->num_cu,
-                                                    h->prefill_kernel);
+    fcg::PrefillPlan plan = fcg::prefill_plan(h->qtype, (int)M, N, K, h->num_cu,
+                                              h->prefill_kernel);
+    if (plan.kind == fcg::PREFILL_KERNEL_DMA && h->tile_mt) {
+      // the forced tile, when every part of K keeps at least one stage
+      const int S_total = K / fcg::PREFILL_KSTAGE;
+      const int per = (S_total + h->tile_splits - 1) / h->tile_splits;
+      if ((h->tile_splits - 1) * per < S_total) {
+        plan.mt = h->tile_mt;
+        plan.splits = h->tile_splits;
+      }
+    }
     const size_t need = fcg::prefill_workspace_bytes((int)M, N, plan.splits);
     if (need) {
       rc = ensure_ws(h, need, st);

@@ -54,6 +54,7 @@ hipError_t launch_dequant_f16(int qtype, const uint8_t* W, f16* out, int N, int 
 // AUTO takes the loader-wave tile at every row count (the faster one on the
 // benchmark shapes), the decode-once tile is forced with
 // FC_GGUF_PREFILL_KERNEL=lds
+constexpr int PREFILL_KSTAGE = 128;   // values of K per loader-wave stage (half a super-block)
 constexpr int PREFILL_KERNEL_AUTO = 0;
 constexpr int PREFILL_KERNEL_DMA = 1;
 constexpr int PREFILL_KERNEL_LDS = 2;

@@ -21,6 +21,8 @@
 
 namespace fcg {
 
+static_assert(PREFILL_KSTAGE == KSTAGE, "the host and the tile agree on the stage size");
+
 // Epilogue of a wave's sub-tiles: lane holds C[n = 4*(lane>>4) + r][m = lane & 15]
 // of each 16x16 sub-tile (i, j), whose first row is m0 + 16 i and first
 // column n0 + 16 j; + R and one f16 rounding, or f32 split-K partials.
@@ -315,21 +317,41 @@ static hipError_t launch_lds_t(const uint8_t* W, const f16* A, const f16* R, f16
 }
 
 // The loader-wave tile's row count and K splits for M rows (also the int8
-// variant's tile): tile rows grow with M (16, 32, 64, 128); K is split only
-// while the grid is under one workgroup per CU and every split keeps at
-// least 4 stages.
+// variant's tile).  Candidates: 16, 32, 64 or 128 activation rows (up to the
+// first tile that covers M) and K in 1, 2, 4, ... parts of at least 4 stages
+// each.  The choice minimises an estimate of the launch time fitted to
+// measurements of this kernel on MI355X: one workgroup per CU at a time, so
+// ceil(tiles * splits / CUs) rounds of S / splits stages, a stage costing
+// about 0.8 us + 0.0075 us per activation row of the tile; a split adds the
+// f32 partials' round trip (8 bytes per partial element at about 4 TB/s) and
+// about 2 us for the reduction launch.  Splitting only fills CUs that the
+// tile grid leaves idle; a smaller tile fills them too, at the price of
+// decoding each weight block once per tile row.
 void prefill_choose(int qtype, int M, int N, int K, int num_cu, int* mt, int* nt, int* splits) {
   (void)qtype;
-  int t = 1;
-  while (t < 8 && 16 * t < M) t *= 2;
-  *mt = t;
-  *nt = 2;
-  const int BM = 16 * t, BN = 128;
-  const long long tiles = (long long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  int tmax = 1;
+  while (tmax < 8 && 16 * tmax < M) tmax *= 2;
   const int S_total = K / KSTAGE;
-  int s = 1;
-  while (tiles * s < num_cu && S_total / (s * 2) >= 4) s *= 2;
-  *splits = s;
+  const long long tiles_n = (N + 127) / 128;
+  const int cus = num_cu > 0 ? num_cu : 1;
+  double best = 0.0;
+  int bt = tmax, bs = 1;
+  for (int t = 1; t <= tmax; t *= 2) {
+    const long long tiles = (long long)((M + 16 * t - 1) / (16 * t)) * tiles_n;
+    for (int s = 1; s == 1 || S_total / s >= 4; s *= 2) {
+      const long long rounds = (tiles * s + cus - 1) / cus;
+      double cost = (double)rounds * ((double)S_total / s) * (0.8 + 0.0075 * 16 * t);
+      if (s > 1) cost += 2.0 + (double)s * M * N * 8.0 / 4.0e6;
+      if ((t == 1 && s == 1) || cost < best) {
+        best = cost;
+        bt = t;
+        bs = s;
+      }
+    }
+  }
+  *mt = bt;
+  *nt = 2;
+  *splits = bs;
 }
 
 PrefillPlan prefill_plan(int qtype, int M, int N, int K, int num_cu, int kernel) {

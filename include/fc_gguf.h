@@ -54,7 +54,11 @@
  *     default at every M), and a 128 x 128 tile whose producer waves decode
  *     each block once into an f16 tile in LDS that consumer waves multiply.
  *     The environment variable FC_GGUF_PREFILL_KERNEL = dma | lds, read when
- *     a handle is created, forces the first or the second (testing).
+ *     a handle is created, forces the first or the second (testing).  The
+ *     first tile's height and its split of K come from an estimate of the
+ *     launch time; FC_GGUF_TILE = <mt>,<splits> (mt in 1, 2, 4, 8: 16*mt rows;
+ *     splits a power of two up to 64), read when a handle is created, forces
+ *     them (tuning; ignored for a call whose K it would leave a part of).
  */
 #ifndef FC_GGUF_H
 #define FC_GGUF_H

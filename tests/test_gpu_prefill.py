@@ -223,3 +223,21 @@ def test_decode_once_tile_full_size_sampled(gpu_lib, monkeypatch, qtype, shape):
     cols = stratified_cols(N, N + 7)
     ref = ofc.fc_ref(A, okq.dequantize(w[cols], qtype), R[:, cols])
     check_fro(y[:, cols], ref)
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("tile", ["1,1", "2,1", "2,2", "4,2", "4,4", "8,1", "8,8", "1,8",
+                                  "3,2", "4,3", "8,64"])
+def test_loader_wave_tile_forced_shapes(gpu_lib, monkeypatch, qtype, tile):
+    # FC_GGUF_TILE=<mt>,<splits> (read when the handle is created) forces the
+    # loader-wave tile's row count and K split, whatever the row-count rule
+    # picks: every tile height, split-K from none to one stage per split, on
+    # ragged M and N; malformed values ("3,2", "4,3") and a split count that
+    # would leave parts of K empty ("8,64" over 8 stages) fall back to the rule
+    M, N, K = 70, 200, 1024
+    w, A, R = case(qtype, M, N, K, 71, len(tile))
+    monkeypatch.setenv("FC_GGUF_TILE", tile)
+    f = _fc(w, qtype, N, K)
+    monkeypatch.delenv("FC_GGUF_TILE", raising=False)
+    y = _host(f(_dev(A), _dev(R)))
+    check_fro(y, ofc.fc_gguf_ref(A, w, qtype, R))
