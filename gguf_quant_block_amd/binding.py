@@ -41,8 +41,8 @@ _SIGS = {
     "fc_gguf_destroy": (ctypes.c_int, [_vp]),
     "fc_gguf_info": (ctypes.c_int, [_vp, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64),
                                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_c_i64)]),
-    "fc_gguf_debug_quantize": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
-    "fc_gguf_debug_quantize_f32": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "fc_gguf_debug_quantize": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "fc_gguf_debug_quantize_f32": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "fc_gguf_debug_int_dots": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp]),
     "fc_gguf_debug_weights": (ctypes.c_int, [_vp, _vp, _vp]),
     "fc_gguf_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -219,13 +219,16 @@ class FcGguf:
 
 def debug_quantize(A):
     """The decode path's per-32 int8 quantisation of f16 or f32 A[M, K]:
-    (qa i8[M,K], s f32[M,K/32], T i32[M,K/32])."""
+    (qa i8[M,K], s f32[M,K/32], T i32[M,K/32], H i32[M,K/16]); H holds the
+    code sums of the groups' 16-value halves."""
     torch = _torch()
     M, K = A.shape
     assert A.dtype in (torch.float16, torch.float32)
     qa = torch.empty((M, K), dtype=torch.int8, device=A.device)
     s = torch.empty((M, K // 32), dtype=torch.float32, device=A.device)
     T = torch.empty((M, K // 32), dtype=torch.int32, device=A.device)
+    H = torch.empty((M, K // 16), dtype=torch.int32, device=A.device)
     f = lib().fc_gguf_debug_quantize if A.dtype == torch.float16 else lib().fc_gguf_debug_quantize_f32
-    _check(f(_ptr(A.contiguous()), M, K, _ptr(qa), _ptr(s), _ptr(T), _stream()), "fc_gguf_debug_quantize")
-    return qa, s, T
+    _check(f(_ptr(A.contiguous()), M, K, _ptr(qa), _ptr(s), _ptr(T), _ptr(H), _stream()),
+           "fc_gguf_debug_quantize")
+    return qa, s, T, H

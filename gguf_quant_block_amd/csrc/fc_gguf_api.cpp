@@ -489,22 +489,22 @@ int fc_gguf_run_grouped_noalloc(fc_gguf_t h, const void* A, int64_t T, int a_per
 }
 
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s, int32_t* T,
-                           void* stream) {
+                           int32_t* H, void* stream) {
   if (M < 0 || K <= 0 || (K % 32) != 0) return FC_GGUF_EINVAL;
   if (M == 0) return FC_GGUF_OK;
   if (!A || !qa || !s || !T || !aligned(A, 16) || !aligned(qa, 16)) return FC_GGUF_EINVAL;
   if (M * K > ((int64_t)1 << 31)) return FC_GGUF_ERANGE;
-  hipError_t e = fcg::launch_debug_quantize(A, false, (int)M, (int)K, qa, s, T, (hipStream_t)stream);
+  hipError_t e = fcg::launch_debug_quantize(A, false, (int)M, (int)K, qa, s, T, H, (hipStream_t)stream);
   return e == hipSuccess ? FC_GGUF_OK : FC_GGUF_EHIP;
 }
 
 int fc_gguf_debug_quantize_f32(const float* A, int64_t M, int64_t K, int8_t* qa, float* s,
-                               int32_t* T, void* stream) {
+                               int32_t* T, int32_t* H, void* stream) {
   if (M < 0 || K <= 0 || (K % 32) != 0) return FC_GGUF_EINVAL;
   if (M == 0) return FC_GGUF_OK;
   if (!A || !qa || !s || !T || !aligned(A, 16) || !aligned(qa, 16)) return FC_GGUF_EINVAL;
   if (M * K > ((int64_t)1 << 31)) return FC_GGUF_ERANGE;
-  hipError_t e = fcg::launch_debug_quantize(A, true, (int)M, (int)K, qa, s, T, (hipStream_t)stream);
+  hipError_t e = fcg::launch_debug_quantize(A, true, (int)M, (int)K, qa, s, T, H, (hipStream_t)stream);
   return e == hipSuccess ? FC_GGUF_OK : FC_GGUF_EHIP;
 }
 

@@ -541,10 +541,11 @@ hipError_t launch_gemv_f32(int qtype, const uint8_t* W, const float* A, const fl
 
 // The decode path's quantisation routine (the quant_chunk<AT> that the GEMV
 // runs), one thread per 16-byte chunk, written out unswizzled to global
-// memory: codes, and per group its scale and code sum.
+// memory: codes, per group its scale and code sum, and (H not null) the
+// code sum of each 16-value half of a group.
 template <class AT>
 __global__ void debug_quantize_kernel(const AT* __restrict__ A, int M, int K, int8_t* qa, float* s,
-                                      int* T) {
+                                      int* T, int* H) {
   constexpr int CV = chunk_vals<AT>(), GL = group_lanes<AT>();
   const int nch = M * K / CV;
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
@@ -560,18 +561,19 @@ __global__ void debug_quantize_kernel(const AT* __restrict__ A, int M, int K, in
     s[c / GL] = sc;
     T[c / GL] = tsum;
   }
+  if (H && c % (GL / 2) == 0) H[c / (GL / 2)] = thalf;
 }
 
 hipError_t launch_debug_quantize(const void* A, bool f32, int M, int K, int8_t* qa, float* s, int* T,
-                                 hipStream_t st) {
+                                 int* H, hipStream_t st) {
   const long long chunks = (long long)M * K / (f32 ? chunk_vals<float>() : chunk_vals<f16>());
   const unsigned grid = (unsigned)((chunks + 255) / 256);
   if (f32)
     hipLaunchKernelGGL(debug_quantize_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)A, M,
-                       K, qa, s, T);
+                       K, qa, s, T, H);
   else
     hipLaunchKernelGGL(debug_quantize_kernel<f16>, dim3(grid), dim3(256), 0, st, (const f16*)A, M, K,
-                       qa, s, T);
+                       qa, s, T, H);
   return hipGetLastError();
 }
 

@@ -39,9 +39,9 @@ hipError_t launch_gemv(int qtype, const uint8_t* W, const f16* A, const f16* R, 
                        int N, int K, int max_wgs, hipStream_t st);
 hipError_t launch_gemv_f32(int qtype, const uint8_t* W, const float* A, const float* R, float* Y,
                            int M, int N, int K, int max_wgs, hipStream_t st);
-// A is f32 if f32, else f16
+// A is f32 if f32, else f16; H (16-value half sums) may be null
 hipError_t launch_debug_quantize(const void* A, bool f32, int M, int K, int8_t* qa, float* s, int* T,
-                                 hipStream_t st);
+                                 int* H, hipStream_t st);
 hipError_t launch_debug_int_dots(int qtype, const uint8_t* W, const int8_t* qa, int M, int N, int K,
                                  int* S, hipStream_t st);
 

@@ -217,7 +217,10 @@ int fc_gguf_run_grouped_noalloc(fc_gguf_t h, const void* A, int64_t T, int a_per
  *
  * fc_gguf_debug_quantize: the per-32 int8 activation quantisation of the
  *   decode path.  A device f16[M,K] (K % 32 == 0); qa device i8[M,K];
- *   s device f32[M,K/32]; T device i32[M,K/32] (sum of qa per group).
+ *   s device f32[M,K/32]; T device i32[M,K/32] (sum of qa per group);
+ *   H device i32[M,K/16] or NULL: the sum of qa over each 16-value half of
+ *   a group, as the quantisation hands it to the Q6_K GEMV (whose sub-blocks
+ *   are 16 values: the -32 offset enters as -32 times this sum).
  * fc_gguf_debug_quantize_f32: the same for f32 activations, A device
  *   f32[M,K] (the quantisation fc_gguf_run_f32 runs).
  *
@@ -241,9 +244,9 @@ int fc_gguf_run_grouped_noalloc(fc_gguf_t h, const void* A, int64_t T, int a_per
  *   another.
  */
 int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, float* s,
-                           int32_t* T, void* stream);
+                           int32_t* T, int32_t* H, void* stream);
 int fc_gguf_debug_quantize_f32(const float* A, int64_t M, int64_t K, int8_t* qa, float* s,
-                               int32_t* T, void* stream);
+                               int32_t* T, int32_t* H, void* stream);
 int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S, void* stream);
 int fc_gguf_debug_weights(fc_gguf_t h, void* dst, void* stream);
 

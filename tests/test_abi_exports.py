@@ -80,7 +80,7 @@ def test_host_validation_without_gpu(L):
     assert L.fc_gguf_destroy(None) == 0
     assert L.fc_gguf_info(None, None, None, None, None) == -1
     assert L.fc_gguf_run_grouped(None, None, 1, 0, None, 1, None, None) == -1
-    assert L.fc_gguf_debug_quantize(None, 1, 33, None, None, None, None) == -1
+    assert L.fc_gguf_debug_quantize(None, 1, 33, None, None, None, None, None) == -1
 
 
 def test_size_limits_without_gpu(L):
@@ -94,5 +94,5 @@ def test_size_limits_without_gpu(L):
     assert L.fc_gguf_create_grouped(0, 16, 256, 6, buf, 0, ctypes.byref(h)) == -1
     assert not h.value
     assert L.fc_gguf_run_grouped_noalloc(None, None, 1, 0, None, 1, None, None) == -1
-    assert L.fc_gguf_debug_quantize(buf, 1, 33, buf, buf, buf, None) == -1
-    assert L.fc_gguf_debug_quantize_f32(buf, -1, 32, buf, buf, buf, None) == -1
+    assert L.fc_gguf_debug_quantize(buf, 1, 33, buf, buf, buf, None, None) == -1
+    assert L.fc_gguf_debug_quantize_f32(buf, -1, 32, buf, buf, buf, None, None) == -1

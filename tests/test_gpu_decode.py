@@ -57,11 +57,14 @@ def test_quantize_bit_exact(gpu_lib, M, K):
     A = synth.normal_f16((M, K), synth.rng(50, K, 1))
     if M == 6:
         A = _special_rows(K)
-    qa, s, T = (_host(x) for x in debug_quantize(_dev(A)))
+    qa, s, T, H = (_host(x) for x in debug_quantize(_dev(A)))
     qa0, s0, T0 = ofc.quantize_act(A)
     assert np.array_equal(qa, qa0)
     assert np.array_equal(s.view(np.uint32), s0.view(np.uint32))
     assert np.array_equal(T, T0)
+    # the 16-value half sums the Q6_K GEMV takes its -32 offset from: the
+    # oracle's codes summed per half group
+    assert np.array_equal(H, qa0.reshape(A.shape[0], -1, 16).astype(np.int64).sum(axis=2))
 
 
 # ---------------------------------------------------------------- regroup --
@@ -219,11 +222,14 @@ def test_quantize_f32_bit_exact(gpu_lib, M, K):
     A = synth.normal_f32((M, K), synth.rng(57, K, 1))
     if M == 6:
         A = _special_rows_f32(K)
-    qa, s, T = (_host(x) for x in debug_quantize(_dev(A)))
+    qa, s, T, H = (_host(x) for x in debug_quantize(_dev(A)))
     qa0, s0, T0 = ofc.quantize_act(A)
     assert np.array_equal(qa, qa0)
     assert np.array_equal(s.view(np.uint32), s0.view(np.uint32))
     assert np.array_equal(T, T0)
+    # the 16-value half sums the Q6_K GEMV takes its -32 offset from: the
+    # oracle's codes summed per half group
+    assert np.array_equal(H, qa0.reshape(A.shape[0], -1, 16).astype(np.int64).sum(axis=2))
 
 
 def _case_f32(qtype, M, N, K, idx, with_r):
