@@ -32,8 +32,8 @@ CFLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["fc_gguf_api.cpp", "layout.hip", "gemv.hip", "prefill.hip", "prefill_i8.hip", "moe.hip",
-           "dequant.hip"]
+SOURCES = ["fc_gguf_api.cpp", "layout.hip", "gemv.hip", "prefill.hip", "skinny.hip", "prefill_i8.hip",
+           "moe.hip", "dequant.hip"]
 CEIL_SOURCES = ["ceilings.hip"]
 
 

@@ -81,12 +81,14 @@ int default_decode_rows() {
   return (int)v;
 }
 
-// FC_GGUF_PREFILL_KERNEL=dma|lds forces one of the two prefill kernels at
-// every row count (testing); anything else leaves the choice to the row count.
+// FC_GGUF_PREFILL_KERNEL=dma|lds|skinny forces one of the prefill kernels
+// (testing; skinny only where its rows fit, else the row count decides);
+// anything else leaves the choice to the row count.
 int default_prefill_kernel() {
   const char* p = getenv("FC_GGUF_PREFILL_KERNEL");
   if (p && !strcmp(p, "dma")) return fcg::PREFILL_KERNEL_DMA;
   if (p && !strcmp(p, "lds")) return fcg::PREFILL_KERNEL_LDS;
+  if (p && !strcmp(p, "skinny")) return fcg::PREFILL_KERNEL_SKINNY;
   return fcg::PREFILL_KERNEL_AUTO;
 }
 
@@ -417,8 +419,11 @@ int fc_gguf_run(fc_gguf_t h, const void* A, int64_t M, const void* R, void* Y, v
     if (rc != FC_GGUF_OK) return rc;
     e = fcg::launch_prefill_i8(h->qtype, h->w, a, r, y, h->ws, (int)M, N, K, mt, splits, st);
   } else {
-    fcg::PrefillPlan plan = fcg::prefill_plan(h->qtype, (int)M, N, K, h->num_cu,
-                                              h->prefill_kernel);
+    // a forced loader-wave tile (FC_GGUF_TILE) also forces that kernel
+    const int kernel = h->tile_mt && h->prefill_kernel == fcg::PREFILL_KERNEL_AUTO
+                           ? fcg::PREFILL_KERNEL_DMA
+                           : h->prefill_kernel;
+    fcg::PrefillPlan plan = fcg::prefill_plan(h->qtype, (int)M, N, K, h->num_cu, kernel);
     if (plan.kind == fcg::PREFILL_KERNEL_DMA && h->tile_mt) {
       // the forced tile, when every part of K keeps at least one stage
       const int S_total = K / fcg::PREFILL_KSTAGE;

@@ -48,27 +48,36 @@ hipError_t launch_debug_int_dots(int qtype, const uint8_t* W, const int8_t* qa, 
 // dequantise-once comparison path: tiled weights -> row-major f16 W16[N, K]
 hipError_t launch_dequant_f16(int qtype, const uint8_t* W, f16* out, int N, int K, hipStream_t st);
 
-// prefill path: two kernels, the loader-wave tile (16 .. 128 activation rows,
-// weights decoded in the compute waves' registers) and the decode-once tile
-// (128 x 128, weights decoded once into an f16 LDS tile by producer waves);
-// AUTO takes the loader-wave tile at every row count (the faster one on the
-// benchmark shapes), the decode-once tile is forced with
-// FC_GGUF_PREFILL_KERNEL=lds
+// prefill path: three kernels, the loader-wave tile (16 .. 128 activation
+// rows, weights decoded in the compute waves' registers), the decode-once
+// tile (128 x 128, weights decoded once into an f16 LDS tile by producer
+// waves) and the few-row kernel (skinny.hip: the GEMV's work layout on the
+// matrix cores, no K split); prefill_plan takes the few-row kernel where
+// M <= 32 rows fit its LDS, else the loader-wave tile, and
+// FC_GGUF_PREFILL_KERNEL=dma|lds|skinny forces one
 constexpr int PREFILL_KSTAGE = 128;   // values of K per loader-wave stage (half a super-block)
 constexpr int PREFILL_KERNEL_AUTO = 0;
 constexpr int PREFILL_KERNEL_DMA = 1;
 constexpr int PREFILL_KERNEL_LDS = 2;
+constexpr int PREFILL_KERNEL_SKINNY = 3;
 struct PrefillPlan {
-  int kind;       // PREFILL_KERNEL_DMA or PREFILL_KERNEL_LDS
+  int kind;       // PREFILL_KERNEL_DMA, _LDS or _SKINNY
   int mt;         // activation rows per tile / 16
   int splits;     // K splits (f32 partials + reduction when > 1)
   int sb_per;     // super-blocks per split (decode-once tile)
+  int wgs;        // most workgroups of the launch (skinny kernel)
 };
 void prefill_choose(int qtype, int M, int N, int K, int num_cu, int* mt, int* nt, int* splits);
 PrefillPlan prefill_plan(int qtype, int M, int N, int K, int num_cu, int kernel);
 size_t prefill_workspace_bytes(int M, int N, int splits);
 hipError_t launch_prefill(const PrefillPlan& p, int qtype, const uint8_t* W, const f16* A,
                           const f16* R, f16* Y, float* P, int M, int N, int K, hipStream_t st);
+// the few-row prefill kernel (skinny.hip): M <= 32 rows whose f16 copy fits
+// the LDS next to the partial sums; max_wgs as for the GEMV
+bool skinny_fits(int M, int K);
+int skinny_max_wgs(int M, int K, int num_cu);
+hipError_t launch_skinny(int qtype, const uint8_t* W, const f16* A, const f16* R, f16* Y, int M,
+                         int N, int K, int max_wgs, hipStream_t st);
 // Y = sum over splits of P[split][M*N] + R, one f16 rounding
 hipError_t launch_splitk_reduce(const float* P, const f16* R, f16* Y, long long MN, int splits,
                                 hipStream_t st);

@@ -356,6 +356,16 @@ void prefill_choose(int qtype, int M, int N, int K, int num_cu, int* mt, int* nt
 
 PrefillPlan prefill_plan(int qtype, int M, int N, int K, int num_cu, int kernel) {
   PrefillPlan p{};
+  // the few-row kernel wherever its rows fit (faster than the loader-wave
+  // tile at every such row count on the benchmark shapes), unless a tile is
+  // forced
+  if ((kernel == PREFILL_KERNEL_SKINNY || kernel == PREFILL_KERNEL_AUTO) && skinny_fits(M, K)) {
+    p.kind = PREFILL_KERNEL_SKINNY;
+    p.mt = M > 16 ? 2 : 1;
+    p.splits = 1;
+    p.wgs = skinny_max_wgs(M, K, num_cu);
+    return p;
+  }
   const bool lds = kernel == PREFILL_KERNEL_LDS;
   if (!lds) {
     int nt;
@@ -382,6 +392,7 @@ size_t prefill_workspace_bytes(int M, int N, int splits) {
 hipError_t launch_prefill(const PrefillPlan& p, int qtype, const uint8_t* W, const f16* A,
                           const f16* R, f16* Y, float* P, int M, int N, int K, hipStream_t st) {
   hipError_t e = hipErrorInvalidValue;
+  if (p.kind == PREFILL_KERNEL_SKINNY) return launch_skinny(qtype, W, A, R, Y, M, N, K, p.wgs, st);
   if (p.kind == PREFILL_KERNEL_LDS) {
     if (qtype == QT_Q4K) e = launch_lds_t<QT_Q4K>(W, A, R, Y, P, M, N, K, p.splits, p.sb_per, st);
     else if (qtype == QT_Q5K) e = launch_lds_t<QT_Q5K>(W, A, R, Y, P, M, N, K, p.splits, p.sb_per, st);

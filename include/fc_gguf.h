@@ -48,17 +48,23 @@
  *   - Testing switch: the environment variable FC_GGUF_TEST_FAIL_ALLOC =
  *     create | workspace | all makes the named device allocations fail
  *     (FC_GGUF_ENOMEM), read at every allocation.
- *   - Prefill kernel: two f16 matrix-core kernels serve the prefill path: a
- *     tile whose compute waves decode the weights into their matrix-core
- *     operand registers (16 .. 128 activation rows, growing with M; the
- *     default at every M), and a 128 x 128 tile whose producer waves decode
- *     each block once into an f16 tile in LDS that consumer waves multiply.
- *     The environment variable FC_GGUF_PREFILL_KERNEL = dma | lds, read when
- *     a handle is created, forces the first or the second (testing).  The
- *     first tile's height and its split of K come from an estimate of the
- *     launch time; FC_GGUF_TILE = <mt>,<splits> (mt in 1, 2, 4, 8: 16*mt rows;
+ *   - Prefill kernel: three f16 matrix-core kernels serve the prefill path:
+ *     a tile whose compute waves decode the weights into their matrix-core
+ *     operand registers (16 .. 128 activation rows, growing with M; "dma"),
+ *     a 128 x 128 tile whose producer waves decode each block once into an
+ *     f16 tile in LDS that consumer waves multiply ("lds"), and a few-row
+ *     kernel that streams the weights like the decode GEMV, one workgroup
+ *     per 16 weight rows over all of K, with the activation rows in LDS
+ *     ("skinny": M <= 32 when M * (K + 8) * 2 bytes plus the partial sums
+ *     fit the 160 KB of LDS).  The default takes the few-row kernel where it
+ *     fits, else the first tile.  The environment variable
+ *     FC_GGUF_PREFILL_KERNEL = dma | lds | skinny, read when a handle is
+ *     created, forces one (testing; skinny only where it fits).  The first
+ *     tile's height and its split of K come from an estimate of the launch
+ *     time; FC_GGUF_TILE = <mt>,<splits> (mt in 1, 2, 4, 8: 16*mt rows;
  *     splits a power of two up to 64), read when a handle is created, forces
- *     them (tuning; ignored for a call whose K it would leave a part of).
+ *     that tile and them (tuning; ignored for a call whose K it would leave
+ *     a part of).
  */
 #ifndef FC_GGUF_H
 #define FC_GGUF_H
