@@ -60,16 +60,9 @@ template <int QT> struct SkUnit {
   uint4 v[NV];
 };
 
-// live: the lane's block is one of the row's K / 256 (a padding block of the
-// last tile is not read; its unit is zero, so it decodes to zero weights)
 template <int QT>
 __device__ __forceinline__ void sk_load(const uint8_t* W, const WMap& L, size_t t, int q, int lane,
-                                        bool live, SkUnit<QT>& u) {
-  if (!live) {
-#pragma unroll
-    for (int i = 0; i < SkUnit<QT>::NV; ++i) u.v[i] = make_uint4(0u, 0u, 0u, 0u);
-    return;
-  }
+                                        SkUnit<QT>& u) {
   const size_t l16 = (size_t)lane << 4;
   if constexpr (QT != QT_Q6K) {
     constexpr int P = block_bytes_of(QT) / 16, QS = QT == QT_Q5K ? 3 : 1;
@@ -280,7 +273,7 @@ skinny_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* R, f16* Y,
   uint32_t rres = load_r(rt);
   asm volatile("" ::: "memory");
   SkUnit<QT> cur;
-  sk_load<QT>(W, L, (size_t)rt * G + g0, q, lane, 4 * g0 + (lane >> 4) < KB, cur);
+  sk_load<QT>(W, L, (size_t)rt * G + g0, q, lane, cur);
   // the activation copies and the residual have landed (the weight loads,
   // issued after them, may still be in flight)
   sk_wait_vmcnt<NV>();
@@ -309,7 +302,7 @@ skinny_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* R, f16* Y,
     if constexpr (MULTI) {
       // the next unit's loads are issued before this unit's matrix-core work
       for (; g + nwq < G; g += nwq) {
-        sk_load<QT>(W, L, t0 + g + nwq, q, lane, 4 * (g + nwq) + (lane >> 4) < KB, cur);
+        sk_load<QT>(W, L, t0 + g + nwq, q, lane, cur);
         unit(g);
         dec.init(cur.v, q);
       }
@@ -318,7 +311,7 @@ skinny_kernel(const uint8_t* __restrict__ W, const f16* A, const f16* R, f16* Y,
     const bool more = rtn < nrt;
     uint32_t rnext = 0u;
     if (more) {
-      sk_load<QT>(W, L, (size_t)rtn * G + g0, q, lane, 4 * g0 + (lane >> 4) < KB, cur);
+      sk_load<QT>(W, L, (size_t)rtn * G + g0, q, lane, cur);
       rnext = load_r(rtn);
     }
     unit(g);
