@@ -68,9 +68,11 @@ def _fc(w, qtype, N, K, path=None):
     return f
 
 
-# (path, M): decode at one row and at a chunked row count, prefill with and
-# without split-K partials in the workspace, the int8 variant
-CASES = [("decode", 1), ("decode", 9), ("prefill", 16), ("prefill", 256), ("int8", 64)]
+# (path, M): decode at one row and at a chunked row count, prefill on the
+# few-row kernel (16), the loader-wave tile with split-K partials in the
+# workspace (64) and without (256), the int8 variant
+CASES = [("decode", 1), ("decode", 9), ("prefill", 16), ("prefill", 64), ("prefill", 256),
+         ("int8", 64)]
 
 
 @pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
