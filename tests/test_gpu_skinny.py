@@ -9,7 +9,9 @@ one and two 16-row halves (M up to 32), ragged M and N, K with padding blocks
 (K / 256 not a multiple of 4), one super-block, waves looping over several
 tiles (K / 256 > 16), in place, no residual, extreme scales, guard bytes
 around Y, the persistent loop over row tiles, the fallback where the rows
-do not fit the LDS, and the full-size shapes on sampled columns.
+do not fit the LDS, and the full-size shapes on sampled columns; also that
+the default picks this kernel exactly where it fits, and the loader-wave
+tile forced at those row counts.
 """
 
 import numpy as np
@@ -126,12 +128,17 @@ def test_skinny_falls_back_where_rows_do_not_fit(gpu_lib, monkeypatch, qtype):
 
 @pytest.mark.parametrize("qtype", ["q5_k", "q6_k"])
 @pytest.mark.parametrize("M", [8, 16, 32])
-@pytest.mark.parametrize("shape", ["qkv", "down", "p0", "p1"])
+@pytest.mark.parametrize("shape", ["qkv", "down", "p0", "p1", "output"])
 def test_skinny_full_size_sampled(gpu_lib, monkeypatch, qtype, M, shape):
-    # the Phi-3.5 projections and the prefill shapes at full size (more row
-    # tiles than workgroups: the persistent loop), sampled output columns
-    N, K = synth.PHI35_LAYERS[shape] if shape in synth.PHI35_LAYERS else \
-        synth.PREFILL_SHAPES[int(shape[1])]
+    # the Phi-3.5 projections, the output projection [32064, 3072] and the
+    # prefill shapes at full size (more row tiles than workgroups: the
+    # persistent loop), sampled output columns
+    if shape == "output":
+        N, K = synth.PHI35_OUTPUT
+    elif shape in synth.PHI35_LAYERS:
+        N, K = synth.PHI35_LAYERS[shape]
+    else:
+        N, K = synth.PREFILL_SHAPES[int(shape[1])]
     w, A, R = case(qtype, M, N, K, 85, M + len(shape))
     y = _host(_fc(w, qtype, N, K, "skinny", monkeypatch)(_dev(A), _dev(R)))
     cols = stratified_cols(N, N + M)
