@@ -5,11 +5,14 @@
 // loads and decode are double-buffered, and the tile grows with the number of
 // rows; the residual Add is fused into the output store.
 //
-// gfx950 design: the tile machinery (mfma_tile.h) over a dense range of BM
+// gfx950 design: the loader-wave tile (mfma_dma.h) over a dense range of BM
 // activation rows; the epilogue adds R once and rounds to f16, or writes f32
 // partials for a split-K reduction when the tile grid is too small to fill
 // the 256 compute units.  Tile ids are remapped so that the workgroups
-// sharing weight columns land on the same XCD (one L2 per XCD).
+// sharing weight columns land on the same XCD (one L2 per XCD).  This file
+// also holds the decode-once LDS tile (mfma_lds.h, forced only) and the
+// plan that picks between them and the few-row kernel of skinny.hip, which
+// takes M <= 32 rows whenever they fit its LDS.
 #include "common.h"
 #include "internal.h"
 
