@@ -365,6 +365,9 @@ bool skinny_fits(int M, int K) {
   return sk_lds(M, K, MT) <= 160 * 1024 && 16 * M <= 64 * sk_waves(K);
 }
 
+// Two workgroups per CU where two fit the LDS, else one (one per CU
+// everywhere measured within a few per cent either way on the benchmark
+// shapes).
 int skinny_max_wgs(int M, int K, int num_cu) {
   const size_t lds = sk_lds(M, K, M > 16 ? 2 : 1);
   const int per_cu = lds <= 80 * 1024 ? 2 : 1;
