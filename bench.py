@@ -32,8 +32,10 @@ int8 matrix-core instructions), the dequantise-once and int8 comparison
 paths, and the CPU oracle timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       python bench.py --pmc-target | --pmc-prefill-target | --pmc-moe-target | --pmc-int8-target
+       python bench.py --pmc-target | --pmc-prefill-target | --pmc-prefill4-target |
+                       --pmc-moe-target | --pmc-int8-target
        python bench.py --traffic-summary FETCH_CSV WRITE_CSV
+       python bench.py --prefill-traffic-summary FETCH_CSV WRITE_CSV
 """
 
 from __future__ import annotations
@@ -80,6 +82,29 @@ def traffic_from_profile():
     if rec.get("gemv_source_hash") != gemv_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def prefill_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "mfma_dma.h", "mfma_tile.h", "common.h", "layout.h"):
+        with open(os.path.join(ROOT, "gguf_quant_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_traffic_from_profile():
+    """HBM bytes per M = 512 prefill FC call from the committed counter
+    summary, or None when the kernel source changed since the counters were
+    taken."""
+    p = os.path.join(ROOT, "profiles", "prefill_m512_traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("prefill_source_hash") != prefill_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
 
 
 def cpu_model() -> str:
@@ -415,6 +440,44 @@ def pmc_prefill_target(dev):
     print("pmc prefill target done", flush=True)
 
 
+PREFILL4_CALLS = 3      # eager calls of each of the four M = 512 FCs in --pmc-prefill4-target
+
+
+def prefill4_fcs():
+    """The four M = 512 prefill FCs of the benchmark, in target order."""
+    from gguf_quant_block_amd import synth
+    return [(q, N, K) for q in ("q5_k", "q6_k") for (N, K) in synth.PREFILL_SHAPES]
+
+
+def pmc_prefill4_target(dev):
+    """Counter-collection target for the prefill FC traffic: the four M = 512
+    FCs (Q5_K, Q6_K x [8192, 2048], [2048, 8192]) with the residual,
+    PREFILL4_CALLS eager calls each, then three 256 MiB device copies."""
+    import torch
+    from gguf_quant_block_amd import synth
+    from gguf_quant_block_amd.binding import FcGguf
+    M = 512
+    for i, (q, N, K) in enumerate(prefill4_fcs()):
+        w = torch.from_numpy(synth.blocks(q, N, K, synth.rng(2, i, synth.TAG_BLOCKS))).to(dev)
+        A = torch.from_numpy(synth.normal_f16((M, K), synth.rng(2, i, synth.TAG_A))).to(dev)
+        R = torch.from_numpy(synth.normal_f16((M, N), synth.rng(2, i, synth.TAG_R))).to(dev)
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        fc = FcGguf(N, K, q, w)
+        fc(A, R, out=Y)                       # the workspace grows here, before the counted calls
+        torch.cuda.synchronize()
+        for _ in range(PREFILL4_CALLS):
+            fc(A, R, out=Y)
+        torch.cuda.synchronize()
+        del fc, w
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("pmc prefill4 target done", flush=True)
+
+
 def pmc_moe_target(dev):
     """Counter-collection target for the grouped path: the benchmark's first
     routing and weight copy, gate/up then down (on gate/up's bucketing),
@@ -524,6 +587,69 @@ def traffic_summary(fetch_csv, write_csv):
     print(json.dumps(rec))
 
 
+def prefill_traffic_summary(fetch_csv, write_csv):
+    """Turn the two counter passes over --pmc-prefill4-target into HBM bytes
+    per prefill FC call (the loader-wave tile plus, for a split-K grid, its
+    reduction): each counter scaled by what it reads for the 256 MiB device
+    copy; per FC, the dispatches of its counted calls (the first call of each
+    FC, which grows the workspace, is left out) over the call count."""
+    import csv
+
+    def read(path, counter):
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id") or 0))
+        fcs, calib, cur = [], [], None
+        for r in rows:
+            name = r["Kernel_Name"]
+            v = float(r["Counter_Value"]) * 1024.0
+            if "copyBuffer" in name:
+                calib.append(v)
+            elif "prefill_dma_kernel" in name:
+                cur = [v]
+                fcs.append(cur)
+            elif "splitk_reduce_kernel" in name and cur is not None:
+                cur.append(v)
+        return [sum(c) for c in fcs], calib
+
+    fcalls, fc = read(fetch_csv, "FETCH_SIZE")
+    wcalls, wc = read(write_csv, "WRITE_SIZE")
+    per = PREFILL4_CALLS + 1
+    assert len(fcalls) == len(wcalls) == 4 * per, (len(fcalls), len(wcalls))
+    f_factor = CALIB_BYTES / (sum(fc[-3:]) / 3)
+    w_factor = CALIB_BYTES / (sum(wc[-3:]) / 3)
+    M = 512
+    bb = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
+    by_fc, alg_by_fc = {}, {}
+    for i, (q, N, K) in enumerate(prefill4_fcs()):
+        calls = range(i * per + 1, (i + 1) * per)
+        b = sum(fcalls[j] * f_factor + wcalls[j] * w_factor for j in calls) / PREFILL4_CALLS
+        key = f"{q}_{N}x{K}"
+        by_fc[key] = round(b)
+        alg_by_fc[key] = N * (K // 256) * bb[q] + 2 * M * K + 4 * M * N
+    hbm = sum(by_fc.values()) / 4
+    alg = sum(alg_by_fc.values()) / 4
+    rec = {
+        "kernel": "prefill_dma_kernel (+ splitk_reduce_kernel where K is split)",
+        "workload": "the four M = 512 prefill FCs (Q5_K, Q6_K x [8192, 2048], [2048, 8192]) "
+                    "with the residual, equal mix",
+        "prefill_source_hash": prefill_source_hash(),
+        "fc_calls_counted": 4 * PREFILL4_CALLS,
+        "fetch_factor": round(f_factor, 4),
+        "write_factor": round(w_factor, 4),
+        "hbm_bytes_per_call": round(hbm),
+        "algorithmic_bytes_per_call": round(alg),
+        "traffic_over_algorithmic": round(hbm / alg, 4),
+        "hbm_bytes_per_call_by_fc": by_fc,
+        "algorithmic_bytes_per_call_by_fc": alg_by_fc,
+    }
+    out = os.path.join(ROOT, "profiles", "prefill_m512_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 # ----------------------------------------------------------------- main ----
 
 class Case:
@@ -593,11 +719,20 @@ def main():
     ap.add_argument("--pmc-int8-target", action="store_true",
                     help="run the int8 prefill variant (Q5_K [8192, 2048], M = 512) ten times eagerly, "
                          "for rocprofv3 --pmc counter passes")
+    ap.add_argument("--pmc-prefill4-target", action="store_true",
+                    help="run the four M = 512 prefill FCs eagerly and a 256 MiB device copy of "
+                         "known size, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from the two counter passes over --pmc-target")
+    ap.add_argument("--prefill-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the prefill HBM traffic record from the two counter passes over "
+                         "--pmc-prefill4-target")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.prefill_traffic_summary:
+        prefill_traffic_summary(*args.prefill_traffic_summary)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU (across GPUs the FC would shard along N, each GPU "
@@ -620,6 +755,9 @@ def main():
         return
     if args.pmc_prefill_target:
         pmc_prefill_target(dev)
+        return
+    if args.pmc_prefill4_target:
+        pmc_prefill4_target(dev)
         return
     if args.pmc_moe_target:
         pmc_moe_target(dev)
@@ -858,7 +996,7 @@ def main():
             "peak": F16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(prefill_tflops / F16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": prefill_traffic_from_profile(),
         },
         "roofline_moe": {
             "bound": "hbm",

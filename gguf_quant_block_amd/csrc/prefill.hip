@@ -76,8 +76,11 @@ __device__ __forceinline__ void prefill_epilogue(const floatx4 (&acc)[MT][NT],
 
 // Tile index of this workgroup.  XCD-aware remap: the hardware deals
 // workgroups round-robin over 8 XCDs; give each XCD a contiguous run of
-// logical tiles (m fastest, then split, then n) so tiles sharing weight
-// columns share an L2.
+// logical tiles (m fastest, then n, then split), so that the tiles sharing
+// weight rows share an L2 and, in a split-K grid, an XCD reads the
+// activations of one part of K only.  (Split before n made every XCD read
+// all of A: [2048, 8192] at M = 512 then filled its L2s with 5x the
+// algorithmic bytes.)
 __device__ __forceinline__ void prefill_tile_id(int tiles_m, int tiles_n, int splits, int& mt,
                                                 int& sp, int& nt) {
   const int Gt = tiles_m * tiles_n * splits;
@@ -86,8 +89,8 @@ __device__ __forceinline__ void prefill_tile_id(int tiles_m, int tiles_n, int sp
   bid = x * per + (x < rem ? x : rem) + j;
   mt = bid % tiles_m;
   const int rest = bid / tiles_m;
-  sp = rest % splits;
-  nt = rest / splits;
+  nt = rest % tiles_n;
+  sp = rest / tiles_n;
 }
 
 // The matrix-core tile with loader waves and an LDS ring (mfma_dma.h).
