@@ -178,23 +178,26 @@ moe_grouped_kernel(const uint8_t* W, size_t expert_bytes, const f16* A,
                    f16* __restrict__ Y, const int2* __restrict__ tiles,
                    const int* __restrict__ offsets, const int* __restrict__ pairs,
                    const int* __restrict__ ntiles, int E, int N, int K, int top_k, int a_per_slot,
-                   int max_tiles, int tiles_n) {
+                   int tiles_n) {
   constexpr int BM = 16 * MT;
   constexpr int BN = 64 * NT;
   __shared__ __align__(16) f16 As[2][BM * astr(MOE_SH)];
 
-  // XCD-aware remap (round-robin dispatch over 8 XCDs): each XCD takes a
-  // contiguous run of logical items, row tiles fastest, so the row tiles of
-  // one expert against one weight-row tile share an L2.
-  const int Gt = max_tiles * tiles_n;
-  int bid = blockIdx.x;
-  {
-    const int per = Gt / 8, rem = Gt % 8, x = bid % 8, j = bid / 8;
-    bid = x * per + (x < rem ? x : rem) + j;
-  }
-  const int ti = bid % max_tiles;
-  const int nt = bid / max_tiles;
-  if (ti >= *ntiles) return;               // whole workgroup: past the real tile count
+  // XCD-aware remap (round-robin dispatch over 8 XCDs) over the real items
+  // (the tile count the bucketing found, times the weight-row tiles): each
+  // XCD takes an equal, contiguous run of them, row tiles fastest, so the
+  // row tiles of one expert against one weight-row tile share an L2, and the
+  // workgroups past its run exit at once.  (Over the grid's upper bound
+  // instead, the exiting items fell unevenly: on the benchmark routing two
+  // XCDs of gate/up held 121 real items and six held 94-95.)
+  const int nreal = *ntiles;
+  const int Gr = nreal * tiles_n;
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int per = Gr / 8, rem = Gr % 8;
+  if (j >= per + (xcd < rem ? 1 : 0)) return;       // whole workgroup
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + j;
+  const int ti = item % nreal;
+  const int nt = item / nreal;
 
   const int2 t = tiles[ti];
   const int e = t.x;
@@ -266,7 +269,7 @@ static hipError_t launch_grouped_t(const uint8_t* W, size_t expert_bytes, const 
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((moe_grouped_kernel<QT, MT, MOE_NT>), dim3((unsigned)grid), dim3(256), 0, st,
                      W, expert_bytes, A, Y, w.tiles, w.offsets, w.pairs, w.ntiles, E, N, K, top_k,
-                     a_per_slot, max_tiles, tiles_n);
+                     a_per_slot, tiles_n);
   return hipGetLastError();
 }
 
