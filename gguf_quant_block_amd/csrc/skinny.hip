@@ -1,5 +1,6 @@
-// Prefill path for few activation rows (8 .. 32): the f16 matrix-core FC with
-// the decode path's work layout, in one launch and without a K split.
+// Prefill path for few activation rows (up to 32; 8 .. 32 by default, fewer
+// when the prefill path is forced): the f16 matrix-core FC with the decode
+// path's work layout, in one launch and without a K split.
 //
 // OpenVINO PR #39119, section Implementation: at M >= 8 the weights are
 // decoded exactly to f16 and multiplied on the matrix cores with f32
