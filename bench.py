@@ -33,7 +33,7 @@ paths, and the CPU oracle timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --pmc-target | --pmc-prefill-target | --pmc-prefill4-target |
-                       --pmc-moe-target | --pmc-int8-target
+                       --pmc-skinny-target | --pmc-moe-target | --pmc-int8-target
        python bench.py --traffic-summary FETCH_CSV WRITE_CSV
        python bench.py --prefill-traffic-summary FETCH_CSV WRITE_CSV
 """
@@ -440,6 +440,32 @@ def pmc_prefill_target(dev):
     print("pmc prefill target done", flush=True)
 
 
+def pmc_skinny_target(dev):
+    """Counter-collection target for the few-row prefill kernel: the Q5_K
+    FC on [8192, 2048] at M = 8 (one row tile per workgroup, two
+    workgroups per CU), ten eager launches, then three 256 MiB device
+    copies."""
+    import torch
+    from gguf_quant_block_amd import synth
+    from gguf_quant_block_amd.binding import FcGguf
+    N, K = synth.PREFILL_SHAPES[0]
+    M = 8
+    w = torch.from_numpy(synth.q5k_blocks(N, K, synth.rng(2, 7, synth.TAG_BLOCKS))).to(dev)
+    A = torch.from_numpy(synth.normal_f16((M, K), synth.rng(2, 7, synth.TAG_A))).to(dev)
+    R = torch.from_numpy(synth.normal_f16((M, N), synth.rng(2, 7, synth.TAG_R))).to(dev)
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    fc = FcGguf(N, K, "q5_k", w)
+    for _ in range(10):
+        fc(A, R, out=Y)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("pmc skinny target done", flush=True)
+
+
 PREFILL4_CALLS = 3      # eager calls of each of the four M = 512 FCs in --pmc-prefill4-target
 
 
@@ -722,6 +748,9 @@ def main():
     ap.add_argument("--pmc-prefill4-target", action="store_true",
                     help="run the four M = 512 prefill FCs eagerly and a 256 MiB device copy of "
                          "known size, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--pmc-skinny-target", action="store_true",
+                    help="run the few-row prefill kernel (Q5_K [8192, 2048], M = 8) ten times "
+                         "eagerly and a 256 MiB device copy, for rocprofv3 --pmc counter passes")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from the two counter passes over --pmc-target")
     ap.add_argument("--prefill-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -758,6 +787,9 @@ def main():
         return
     if args.pmc_prefill4_target:
         pmc_prefill4_target(dev)
+        return
+    if args.pmc_skinny_target:
+        pmc_skinny_target(dev)
         return
     if args.pmc_moe_target:
         pmc_moe_target(dev)
