@@ -23,9 +23,10 @@
 //     (Q4_K, Q5_K: s*T per 32-group for the min term; Q6_K: 16-value sums for
 //     the -32 offset).  The activations are quantised once per workgroup.
 //   * The weight side of a unit (codes, scale factors) is decoded as soon as
-//     its pieces arrive; after the barrier only the v_dot4_i32_i8 integer
-//     sums and the f32 scale algebra remain.  The first unit of the next row
-//     tile is loaded before this row tile's last dots.
+//     its pieces arrive; after the barrier only the integer sums (on the
+//     int8 matrix core, four activation rows per instruction) and the f32
+//     scale algebra remain.  The first unit of the next row tile is loaded
+//     before this row tile's last dots.
 //   * Row sums in a fixed order: over a lane's units, then across the four
 //     lanes of a row ((b0 + b1) + (b2 + b3), from the lanes' sums in LDS),
 //     then across the waves in wave order; R is added and the result is
@@ -54,7 +55,7 @@ template <> struct GemvFmt<QT_Q6K> {
 };
 
 struct GemvLayout {
-  size_t rec, part, total;
+  size_t rec, part, zero, total;
 };
 
 // Waves per workgroup (one row tile) for K: one wave per quarter of each
@@ -70,14 +71,15 @@ __host__ __device__ inline int gemv_waves(int K) {
 // banks) | rec u32 [MR][KBp][REC] | part f32 [2][waves][MR][16][4] (a wave's
 // sums for the 16 rows of a row tile, one per lane: row, then the lane's
 // block within the 4-block tile; two buffers, alternating over the
-// workgroup's row tiles).
+// workgroup's row tiles) | 256 zero bytes (the activation operand of the
+// lanes whose matrix-core rows are off the block diagonal, see dot_unit).
 constexpr int QA_REC = QK + 16;
 template <int QT>
 __host__ __device__ constexpr GemvLayout gemv_layout(int MR, int KBp, int waves) {
   const size_t rec = (size_t)MR * KBp * QA_REC;
   const size_t part = rec + (size_t)MR * KBp * GemvFmt<QT>::REC * 4;
-  const size_t total = part + (size_t)2 * waves * MR * 64 * 4;
-  return GemvLayout{rec, part, total};
+  const size_t zero = part + (size_t)2 * waves * MR * 64 * 4;
+  return GemvLayout{rec, part, zero, zero + QK};
 }
 
 // ------------------------------------------------ activation quantisation --
@@ -148,6 +150,8 @@ __device__ __forceinline__ void act_quant(uint4 raw, int c, int nch, int K, int 
 // qh[32h + l]), high nibble -> value 128h + 32(a+2) + l (bit pair 2a+4).
 // Codes are packed four to a word, value order.
 
+// sum of four code words times 16 activation codes (the debug kernel's
+// activation sums)
 __device__ __forceinline__ int dot16u(const uint32_t* c, uint4 a) {
   int s = dot4((int)c[0], (int)a.x, 0);
   s = dot4((int)c[1], (int)a.y, s);
@@ -279,24 +283,91 @@ __device__ __forceinline__ void decode_unit(const GemvUnit<QT>& u, int q, QDec<Q
   else q45k_decode<QT>(u, q, o);
 }
 
+// ------------------------------------------ integer sums on the matrix core --
+// The integer sums come from v_mfma_i32_16x16x64_i8 with a block-diagonal
+// activation operand, which gives every lane the sums of its own block for
+// four activation rows at once.
+// Lane l (block (row l % 16, kb = 4g + l / 16) of the tile) supplies the B
+// operand: 16 codes of its block.  Row i = 4 gi + mi of the A operand holds
+// activation row 4 s + mi of block 4g + gi in the K slice of lane group gi and
+// zeros in the other three slices.  Lane l supplies row l % 16 in slice
+// l / 16, so only the lanes with (l / 4) % 4 == l / 16 load activation codes;
+// the others read zero bytes.  The instruction sums over each lane group's
+// slice separately for a given (row, column), so D row 4 gi + r, column w is
+// the dot product of block (w, 4g + gi)'s 16 codes with activation row
+// 4 s + r's codes of that block; in D's layout (lane l holds rows
+// 4 (l / 16) + r of column l % 16) that is lane l's own block, rows 4 s + r.
+// The sums are exact integers.  Against v_dot4_i32_i8 sums (one instruction
+// per four codes and activation row) this takes the GEMV at four and seven
+// rows 9-20 % faster; at one row the two are even.
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int4v mx_dot(uint4 a, const uint32_t* c, int4v acc) {
+  const int4v av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+  const int4v cv = {(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, cv, acc, 0, 0, 0);
+}
+
+// The lanes whose A-operand row lies on the block diagonal.
+__device__ __forceinline__ bool mx_diag(int lane) { return ((lane >> 2) & 3) == (lane >> 4); }
+
+// Byte offset, within a block's 256 codes, of the quarter's activation
+// operand j: Q4_K / Q5_K values 64q + 16j + [0, 16); Q6_K the sub-blocks
+// s0, s0 + 1, s0 + 4, s0 + 5 of 16 values.
+template <int QT>
+__device__ __forceinline__ int mx_off(int q, int j) {
+  if constexpr (QT != QT_Q6K) return 64 * q + 16 * j;
+  else return 16 * (4 * (q & 2) + 2 * (q & 1)) + 16 * (j & 1) + 64 * (j >> 1);
+}
+
+// The quarter's integer sums for four activation rows from its four
+// activation operands: Q4_K / Q5_K S[0] group 2q, S[1] group 2q + 1; Q6_K
+// S[0..3] the sub-blocks s0, s0 + 1, s0 + 4, s0 + 5 (codes 0..63, without
+// the -32 offset).
+template <int QT>
+__device__ __forceinline__ void mx_sums(const QDec<QT>& o, const uint4* a, int4v* S) {
+  const int4v z = {0, 0, 0, 0};
+  if constexpr (QT != QT_Q6K) {
+    S[0] = mx_dot(a[1], o.lo + 4, mx_dot(a[0], o.lo, z));
+    S[1] = mx_dot(a[3], o.hi + 4, mx_dot(a[2], o.hi, z));
+  } else {
+    S[0] = mx_dot(a[0], o.lo, z);
+    S[1] = mx_dot(a[1], o.lo + 4, z);
+    S[2] = mx_dot(a[2], o.hi, z);
+    S[3] = mx_dot(a[3], o.hi + 4, z);
+  }
+}
+
 // The activation side of quarter q of block kb -> part[m] (the lane's
-// contribution to row m).  The lanes of a wave read the codes of four blocks
-// (one per kb % 4), so the LDS reads are broadcasts.
+// contribution to row m).  Every lane takes part in the matrix-core
+// instructions (the lanes of zero padding blocks too, whose sums are then
+// dropped).  zero: the LDS offset of 256 zero bytes.
 template <int QT, int MR>
 __device__ __forceinline__ void dot_unit(const QDec<QT>& o, int q, int kb, int KB, int KBp,
-                                         const uint8_t* smem, const uint32_t* rec, float* part) {
+                                            const uint8_t* smem, uint32_t zero, const uint32_t* rec,
+                                            float* part) {
+  constexpr int REC = GemvFmt<QT>::REC, SETS = (MR + 3) / 4;
+  const int lane = threadIdx.x & 63;
+  int4v S[SETS][4];
+#pragma unroll
+  for (int s = 0; s < SETS; ++s) {
+    const int m = 4 * s + (lane & 3);
+    const uint32_t base = mx_diag(lane) && m < MR && kb < KB
+                              ? __umul24((uint32_t)(m * KBp + kb), (uint32_t)QA_REC)
+                              : zero;
+    uint4 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *(const uint4*)(smem + base + mx_off<QT>(q, j));
+    mx_sums<QT>(o, a, S[s]);
+  }
   if (kb >= KB) return;                               // zero padding block
-  constexpr int REC = GemvFmt<QT>::REC;
-  const uint32_t qa0 = __umul24((uint32_t)kb, (uint32_t)QA_REC), r0 = __umul24((uint32_t)kb, (uint32_t)REC);
+  const uint32_t r0 = __umul24((uint32_t)kb, (uint32_t)REC);
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    const uint8_t* qa = smem + qa0 + (uint32_t)(m * KBp * QA_REC);
     const uint32_t* r = rec + r0 + (uint32_t)(m * KBp * REC);
+    const int4v* Sm = S[m / 4];
     if constexpr (QT != QT_Q6K) {
-      // values 64q + [0, 32) (group 2q) and 64q + 32 + [0, 32) (group 2q+1)
-      const uint4* a = (const uint4*)(qa + 64 * q);
-      const int S0 = dot16u(o.lo, a[0]) + dot16u(o.lo + 4, a[1]);
-      const int S1 = dot16u(o.hi, a[2]) + dot16u(o.hi + 4, a[3]);
+      const int S0 = Sm[0][m % 4], S1 = Sm[1][m % 4];
       const float2 s2 = *(const float2*)(r + 2 * q);
       const float2 t2 = *(const float2*)(r + 8 + 2 * q);
       float X = o.f[0] * (s2.x * (float)S0);
@@ -305,15 +376,13 @@ __device__ __forceinline__ void dot_unit(const QDec<QT>& o, int q, int kb, int K
       Z = fmaf(o.f[3], t2.y, Z);
       part[m] += X - Z;
     } else {
-      // sub-blocks s0, s0+1 (values 16 s0 + [0, 32)) and s0+4, s0+5
       const int s0 = 4 * (q & 2) + 2 * (q & 1);
-      const uint4* a = (const uint4*)(qa + 16 * s0);
       const int2 tl = *(const int2*)(r + 8 + s0);
       const int2 th = *(const int2*)(r + 8 + s0 + 4);
-      const int S0 = dot16u(o.lo, a[0]) - 32 * tl.x;
-      const int S1 = dot16u(o.lo + 4, a[1]) - 32 * tl.y;
-      const int S4 = dot16u(o.hi, a[4]) - 32 * th.x;
-      const int S5 = dot16u(o.hi + 4, a[5]) - 32 * th.y;
+      const int S0 = Sm[0][m % 4] - 32 * tl.x;
+      const int S1 = Sm[1][m % 4] - 32 * tl.y;
+      const int S4 = Sm[2][m % 4] - 32 * th.x;
+      const int S5 = Sm[3][m % 4] - 32 * th.y;
       const int I = __mul24(o.c[0], S0) + __mul24(o.c[1], S1);
       const int J = __mul24(o.c[2], S4) + __mul24(o.c[3], S5);
       const float sI = __builtin_bit_cast(float, r[s0 >> 1]);
@@ -414,6 +483,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
     act_quant<QT, MR, AT>(act_load<AT>(A, nch, c0 + tid, c0 + wave * 64), c0 + tid, nch, K, KBp,
                           kb_magic, smem, rec);
   // the first unit's weight side, while the other waves finish quantising
+  if (tid < QK / 16) *(uint4*)(smem + Ly.zero + 16 * tid) = make_uint4(0, 0, 0, 0);
   QDec<QT> dec;
   decode_unit<QT>(cur, q, dec);
   barrier_after_lds_writes();                         // quantised activations ready
@@ -430,7 +500,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
       // later units: the next unit's loads are issued before this unit's dots
       for (; g + nwq < G; g += nwq) {
         load_unit<QT>(ua, t0 + g + nwq, q, cur);
-        dot_unit<QT, MR>(dec, q, g * TILE_KB + kbq, KB, KBp, smem, rec, part);
+        dot_unit<QT, MR>(dec, q, g * TILE_KB + kbq, KB, KBp, smem, (uint32_t)Ly.zero, rec, part);
         decode_unit<QT>(cur, q, dec);
       }
     }
@@ -441,7 +511,7 @@ gemv_kernel(const uint8_t* __restrict__ W, const AT* A, const AT* R,
       load_unit<QT>(ua, (size_t)rtn * G + g0, q, cur);
       rnext = load_r(rtn);
     }
-    dot_unit<QT, MR>(dec, q, g * TILE_KB + kbq, KB, KBp, smem, rec, part);
+    dot_unit<QT, MR>(dec, q, g * TILE_KB + kbq, KB, KBp, smem, (uint32_t)Ly.zero, rec, part);
     // row sums: the four lanes of a row (kbq = 0..3), then the waves in order
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
@@ -577,39 +647,53 @@ hipError_t launch_debug_quantize(const void* A, bool f32, int M, int K, int8_t* 
   return hipGetLastError();
 }
 
-// Integer sub-block sums with the GEMV's own unit loads and decoder: one
-// thread per block (n, kb), its four quarters read from the device layout
-// (load_unit at the block's tile and slot) and decoded (decode_unit) as the
-// GEMV does; Q6_K sums include the -32 offset.
+// Integer sub-block sums with the GEMV's own unit loads, decoder and
+// matrix-core sums, in the GEMV's lane mapping: workgroup = one 16 x 4-block
+// tile t of the device layout, wave = quarter; Q6_K sums include the -32
+// offset.
 template <int QT>
-__global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ qa,
-                                      int M, int N, int K, int* __restrict__ S) {
-  const int KB = K / QK;
-  const long long gb = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gb >= (long long)N * KB) return;
-  const int n = (int)(gb / KB), kb = (int)(gb % KB);
+__global__ void __launch_bounds__(256)
+debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_t* __restrict__ qa, int M, int N,
+                         int K, int* __restrict__ S) {
   const WMap L(N, K);
-  const UnitAddr ua{W, L.qh_base(), L.sc_base(), L.d_base(), WMap::slot(n, kb)};
+  const int KB = L.KB, G = L.KBp / TILE_KB;
+  const int t = blockIdx.x, lane = threadIdx.x & 63;
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = (t / G) * TILE_ROWS + lane % TILE_ROWS, kb = (t % G) * TILE_KB + lane / TILE_ROWS;
+  const UnitAddr ua{W, L.qh_base(), L.sc_base(), L.d_base(), lane};
+  GemvUnit<QT> u;
+  load_unit<QT>(ua, (size_t)t, q, u);
+  QDec<QT> o;
+  decode_unit<QT>(u, q, o);
+  constexpr int NS = QT == QT_Q6K ? 16 : 8;
   const uint4 ones = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
-  constexpr int NS = QT == QT_Q6K ? 16 : 8;           // sub-blocks per block
-  for (int q = 0; q < 4; ++q) {
-    GemvUnit<QT> u;
-    load_unit<QT>(ua, L.tile(n, kb), q, u);
-    QDec<QT> o;
-    decode_unit<QT>(u, q, o);
-    for (int m = 0; m < M; ++m) {
-      const uint4* a = (const uint4*)(qa + (size_t)m * K + kb * QK);
-      int* out = S + ((size_t)m * N + n) * (K / QK * NS) + kb * NS;
+  for (int s = 0; 4 * s < M; ++s) {                   // wave-uniform
+    const int md = 4 * s + (lane & 3);
+    const bool live = mx_diag(lane) && md < M && kb < KB;
+    uint4 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[j] = live ? *(const uint4*)(qa + (size_t)md * K + kb * QK + mx_off<QT>(q, j))
+                  : make_uint4(0, 0, 0, 0);
+    int4v R[4];
+    mx_sums<QT>(o, a, R);
+    if (n >= N || kb >= KB) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * s + r;
+      if (m >= M) break;
+      int* out = S + ((size_t)m * N + n) * (KB * NS) + kb * NS;
       if constexpr (QT != QT_Q6K) {
-        out[2 * q] = dot16u(o.lo, a[4 * q]) + dot16u(o.lo + 4, a[4 * q + 1]);
-        out[2 * q + 1] = dot16u(o.hi, a[4 * q + 2]) + dot16u(o.hi + 4, a[4 * q + 3]);
+        out[2 * q] = R[0][r];
+        out[2 * q + 1] = R[1][r];
       } else {
         const int s0 = 4 * (q & 2) + 2 * (q & 1);
         const uint32_t* e = (const uint32_t*)&ones;
-        out[s0] = dot16u(o.lo, a[s0]) - 32 * dot16u(e, a[s0]);
-        out[s0 + 1] = dot16u(o.lo + 4, a[s0 + 1]) - 32 * dot16u(e, a[s0 + 1]);
-        out[s0 + 4] = dot16u(o.hi, a[s0 + 4]) - 32 * dot16u(e, a[s0 + 4]);
-        out[s0 + 5] = dot16u(o.hi + 4, a[s0 + 5]) - 32 * dot16u(e, a[s0 + 5]);
+        const uint4* ar = (const uint4*)(qa + (size_t)m * K + kb * QK);
+        out[s0] = R[0][r] - 32 * dot16u(e, ar[s0]);
+        out[s0 + 1] = R[1][r] - 32 * dot16u(e, ar[s0 + 1]);
+        out[s0 + 4] = R[2][r] - 32 * dot16u(e, ar[s0 + 4]);
+        out[s0 + 5] = R[3][r] - 32 * dot16u(e, ar[s0 + 5]);
       }
     }
   }
@@ -617,14 +701,13 @@ __global__ void debug_int_dots_kernel(const uint8_t* __restrict__ W, const int8_
 
 hipError_t launch_debug_int_dots(int qtype, const uint8_t* W, const int8_t* qa, int M, int N, int K,
                                  int* S, hipStream_t st) {
-  const long long total = (long long)N * (K / QK);
-  const int grid = (int)((total + 255) / 256);
+  const int tiles = (tiled_rows(N) / TILE_ROWS) * (tiled_kb(K / QK) / TILE_KB);
   if (qtype == QT_Q4K)
-    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q4K>, dim3(grid), dim3(256), 0, st, W, qa, M, N, K, S);
+    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q4K>, dim3(tiles), dim3(256), 0, st, W, qa, M, N, K, S);
   else if (qtype == QT_Q5K)
-    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q5K>, dim3(grid), dim3(256), 0, st, W, qa, M, N, K, S);
+    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q5K>, dim3(tiles), dim3(256), 0, st, W, qa, M, N, K, S);
   else
-    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q6K>, dim3(grid), dim3(256), 0, st, W, qa, M, N, K, S);
+    hipLaunchKernelGGL(debug_int_dots_kernel<QT_Q6K>, dim3(tiles), dim3(256), 0, st, W, qa, M, N, K, S);
   return hipGetLastError();
 }
 

@@ -99,7 +99,7 @@ def test_layout_helper_is_a_permutation():
 # --------------------------------------------------------------- int sums --
 
 @pytest.mark.parametrize("qtype", QTYPES)
-@pytest.mark.parametrize("M,N,K", [(1, 512, 2048), (7, 37, 768), (4, 16, 8192)])
+@pytest.mark.parametrize("M,N,K", [(1, 512, 2048), (7, 37, 768), (4, 16, 8192), (2, 100, 3072), (5, 24, 1024)])
 def test_int_dots_bit_exact(gpu_lib, qtype, M, N, K):
     w, A, _ = case(qtype, M, N, K, 52, M * N, with_r=False)
     qa, _, _ = ofc.quantize_act(A)
