@@ -43,6 +43,7 @@ _SIGS = {
                                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_c_i64)]),
     "fc_gguf_debug_quantize": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "fc_gguf_debug_quantize_f32": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "fc_gguf_debug_bucketing": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "fc_gguf_debug_int_dots": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp]),
     "fc_gguf_debug_weights": (ctypes.c_int, [_vp, _vp, _vp]),
     "fc_gguf_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -232,3 +233,21 @@ def debug_quantize(A):
     _check(f(_ptr(A.contiguous()), M, K, _ptr(qa), _ptr(s), _ptr(T), _ptr(H), _stream()),
            "fc_gguf_debug_quantize")
     return qa, s, T, H
+
+
+def debug_bucketing(ids, E: int, BM: int):
+    """The grouped path's expert bucketing of device i32 routing ids (any
+    shape, pairs in row-major order): (offsets i32[E+2], pairs i32[P] grouped
+    by bucket, in no fixed order within a bucket, tiles i32[n, 2])."""
+    torch = _torch()
+    ids = ids.contiguous().reshape(-1)
+    assert ids.dtype == torch.int32
+    P = ids.numel()
+    cap = -(-P // BM) + min(E + 1, P)
+    offsets = torch.empty(E + 2, dtype=torch.int32, device=ids.device)
+    pairs = torch.empty(max(P, 1), dtype=torch.int32, device=ids.device)
+    tiles = torch.empty((max(cap, 1), 2), dtype=torch.int32, device=ids.device)
+    n = torch.zeros(1, dtype=torch.int32, device=ids.device)
+    _check(lib().fc_gguf_debug_bucketing(_ptr(ids), P, E, BM, _ptr(offsets), _ptr(pairs), _ptr(tiles),
+                                         _ptr(n), _stream()), "fc_gguf_debug_bucketing")
+    return offsets, pairs[:P], tiles[:int(n.item())]

@@ -525,6 +525,17 @@ int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S,
   return e == hipSuccess ? FC_GGUF_OK : hip_fail(h, e);
 }
 
+int fc_gguf_debug_bucketing(const int32_t* ids, int64_t P, int64_t E, int64_t BM, int32_t* offsets,
+                            int32_t* pairs, int32_t* tiles, int32_t* ntiles, void* stream) {
+  if (P < 0 || E < 1 || BM < 1 || BM > 4096) return FC_GGUF_EINVAL;
+  if (E > fcg::MOE_MAX_E || P > ((int64_t)1 << 30)) return FC_GGUF_ERANGE;
+  if (P == 0) return FC_GGUF_OK;
+  if (!ids || !offsets || !pairs || !tiles || !ntiles || !aligned(tiles, 8)) return FC_GGUF_EINVAL;
+  hipError_t e = fcg::launch_debug_bucketing(ids, (int)P, (int)E, (int)BM, offsets, pairs, tiles,
+                                             ntiles, (hipStream_t)stream);
+  return e == hipSuccess ? FC_GGUF_OK : FC_GGUF_EHIP;
+}
+
 int fc_gguf_debug_weights(fc_gguf_t h, void* dst, void* stream) {
   if (!h || !dst) return FC_GGUF_EINVAL;
   if (const int rc = check_device(h); rc != FC_GGUF_OK) return rc;

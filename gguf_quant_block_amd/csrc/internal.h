@@ -96,4 +96,7 @@ size_t moe_workspace_bytes(int E, int T, int top_k);
 hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, int N, int K,
                       const f16* A, int T, int a_per_slot, const int32_t* ids, int top_k, f16* Y,
                       void* ws, bool bucket, hipStream_t st);
+// the grouped path's bucketing alone, into caller buffers (test export)
+hipError_t launch_debug_bucketing(const int32_t* ids, int P, int E, int BM, int* offsets, int* pairs,
+                                  int* tiles, int* ntiles, hipStream_t st);
 }  // namespace fcg

@@ -28,7 +28,9 @@
 // own activation row and its expert's weights, and the order in which its
 // sum is accumulated (the K stages from a starting stage fixed by the expert
 // and the weight-row tile, the same matrix-core instruction sequence) does
-// not depend on the row's tile or position.
+// not depend on the row's tile or position.  (An ordered scatter, each
+// wave ranking its pairs per expert with ballots, made the one-workgroup
+// bucketing about 3 us slower.)
 #include "common.h"
 #include "internal.h"
 #include "mfma_tile.h"
@@ -299,6 +301,14 @@ hipError_t launch_moe(int qtype, const uint8_t* W, size_t expert_bytes, int E, i
   }
 #undef FCG_MOE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_debug_bucketing(const int32_t* ids, int P, int E, int BM, int* offsets, int* pairs,
+                                  int* tiles, int* ntiles, hipStream_t st) {
+  if (E > MOE_MAX_E) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(MOE_BUCKET_THREADS), 0, st, ids, P, E, BM,
+                     (int2*)tiles, offsets, pairs, ntiles);
+  return hipGetLastError();
 }
 
 }  // namespace fcg

@@ -236,6 +236,19 @@ int fc_gguf_run_grouped_noalloc(fc_gguf_t h, const void* A, int64_t T, int a_per
  *   q in [0,15] / [0,31]);
  *   Q6_K [M, N, K/16] (sum of qa*(q-32) over each 16-value sub-block).
  *
+ * fc_gguf_debug_bucketing: the grouped path's expert bucketing alone
+ *   (llama.cpp PR #28301, Overview: routed rows grouped by expert, then cut
+ *   into row tiles), as fc_gguf_run_grouped runs it before the grouped FC.
+ *   ids device i32[P] (pair p = t*top_k + j); E experts; BM rows per tile
+ *   (the grouped FC uses 32, 64 or 128).  Outputs, all device i32:
+ *   offsets[E+2] (bucket b's pairs are pairs[offsets[b] .. offsets[b+1]);
+ *   bucket E holds the pairs whose id is outside [0, E)); pairs[P], the pair
+ *   indices grouped by bucket (in no fixed order within a bucket); tiles[2*n]
+ *   (bucket, first row within the bucket) for every BM rows of a bucket,
+ *   buckets in order, with n <= ceil(P/BM) + min(E+1, P) and tiles 8-byte
+ *   aligned; ntiles[1] = n.  EINVAL for NULL buffers, P < 0, E < 1 or BM
+ *   outside [1, 4096]; ERANGE for E above 4096 or P above 2^30.
+ *
  * fc_gguf_debug_weights: copies the handle's device weight bytes to device
  *   memory `dst` (fc_gguf_info's weight_bytes long).  Device layout, per
  *   matrix (experts one after another), block (n, kb) being the kb-th
@@ -254,6 +267,8 @@ int fc_gguf_debug_quantize(const void* A, int64_t M, int64_t K, int8_t* qa, floa
 int fc_gguf_debug_quantize_f32(const float* A, int64_t M, int64_t K, int8_t* qa, float* s,
                                int32_t* T, int32_t* H, void* stream);
 int fc_gguf_debug_int_dots(fc_gguf_t h, const int8_t* qa, int64_t M, int32_t* S, void* stream);
+int fc_gguf_debug_bucketing(const int32_t* ids, int64_t P, int64_t E, int64_t BM, int32_t* offsets,
+                            int32_t* pairs, int32_t* tiles, int32_t* ntiles, void* stream);
 int fc_gguf_debug_weights(fc_gguf_t h, void* dst, void* stream);
 
 /* Static description of an error code. */

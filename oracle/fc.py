@@ -167,6 +167,32 @@ def fc_ref_int8(A, w_bytes, qtype, R=None):
 
 # ------------------------------------------------------------------- MoE --
 
+def moe_bucketing(ids, E: int, BM: int):
+    """Expert bucketing of the (token, slot) pairs (llama.cpp PR #28301,
+    Overview: the routed rows are grouped by expert, and each expert's rows
+    form row tiles).
+
+    ids: routing ids of any shape; pair p is the p-th id in row-major order.
+    Bucket e < E holds the pairs routed to expert e, bucket E those whose id
+    is outside [0, E).  Returns
+      offsets int64[E+2]: bucket b's pairs are pairs[offsets[b]:offsets[b+1]];
+      pairs   int64[P]:   pair indices grouped by bucket, listed in
+                          increasing order within a bucket (the page leaves
+                          the order inside an expert open, and no result
+                          depends on it: a comparison takes each bucket as a
+                          set);
+      tiles   int64[n, 2]: (bucket, first row within the bucket) for every BM
+                          rows of every bucket, buckets in increasing order.
+    """
+    ids = np.asarray(ids).reshape(-1)
+    b = np.where((ids >= 0) & (ids < E), ids, E)
+    counts = np.bincount(b, minlength=E + 1)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    pairs = np.argsort(b, kind="stable").astype(np.int64)
+    tiles = [(e, r0) for e in range(E + 1) for r0 in range(0, int(counts[e]), BM)]
+    return offsets, pairs, np.array(tiles, dtype=np.int64).reshape(-1, 2)
+
+
 def moe_ref(A, w_bytes_e, qtype, ids, a_per_slot: bool):
     """float64 Y[T, top_k, N]: Y[t, j] = A_row(t, j) . W_{ids[t, j]}^T.
 

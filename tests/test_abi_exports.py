@@ -96,3 +96,15 @@ def test_size_limits_without_gpu(L):
     assert L.fc_gguf_run_grouped_noalloc(None, None, 1, 0, None, 1, None, None) == -1
     assert L.fc_gguf_debug_quantize(buf, 1, 33, buf, buf, buf, None, None) == -1
     assert L.fc_gguf_debug_quantize_f32(buf, -1, 32, buf, buf, buf, None, None) == -1
+
+
+def test_bucketing_argument_checks_without_gpu(L):
+    buf = (ctypes.c_int32 * 64)()
+    assert L.fc_gguf_debug_bucketing(buf, 4, 8, 16, buf, buf, None, buf, None) == -1   # NULL tiles
+    assert L.fc_gguf_debug_bucketing(buf, -1, 8, 16, buf, buf, buf, buf, None) == -1   # P < 0
+    assert L.fc_gguf_debug_bucketing(buf, 4, 0, 16, buf, buf, buf, buf, None) == -1    # E < 1
+    assert L.fc_gguf_debug_bucketing(buf, 4, 8, 0, buf, buf, buf, buf, None) == -1     # BM < 1
+    assert L.fc_gguf_debug_bucketing(buf, 4, 8, 4097, buf, buf, buf, buf, None) == -1  # BM too large
+    assert L.fc_gguf_debug_bucketing(buf, 4, 4097, 16, buf, buf, buf, buf, None) == -5  # E too large
+    assert L.fc_gguf_debug_bucketing(buf, (1 << 30) + 1, 8, 16, buf, buf, buf, buf, None) == -5
+    assert L.fc_gguf_debug_bucketing(None, 0, 8, 16, None, None, None, None, None) == 0  # P = 0: no-op

@@ -4,9 +4,11 @@ Relative Frobenius error <= 2e-3, over the whole output and per expert, so a
 bug in a 1-row expert is not hidden by the hot experts.  Covers experts
 spanning several ragged tiles, N tails, shared
 and per-pair activation rows, ids outside [0, E), empty experts, T = 0,
-repeat calls (the pair order inside an expert is free, the result must not
-depend on it), the 32-, 64- and 128-row tile variants, and the full-size routed Q6_K expert FCs (128 experts, top-8,
-256 tokens, Zipf 1.1 routing) on sampled experts.
+repeat calls, the 32-, 64- and 128-row tile variants, and the full-size
+routed Q6_K expert FCs (128 experts, top-8, 256 tokens, Zipf 1.1 routing) on
+sampled experts.  The bucketing alone is compared with the oracle's exactly:
+offsets and tile list element by element, the pair list bucket by bucket as
+sets (the kernel's order inside a bucket is free).
 """
 
 import numpy as np
@@ -279,3 +281,40 @@ def test_moe_reuse_checks(gpu_lib):
     assert reuse(b, a.handle, T, idd, top_k) == -1
     assert reuse(b, a.handle, T, idd2, top_k) == 0
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------- bucketing ----
+
+def _check_bucketing(ids, E, BM):
+    from gguf_quant_block_amd.binding import debug_bucketing
+    off, pairs, tiles = debug_bucketing(_dev(ids.astype(np.int32)), E, BM)
+    want_off, want_pairs, want_tiles = ofc.moe_bucketing(ids, E, BM)
+    assert np.array_equal(_host(off).astype(np.int64), want_off)
+    got = _host(pairs).astype(np.int64)
+    for b in range(E + 1):
+        lo, hi = want_off[b], want_off[b + 1]
+        assert np.array_equal(np.sort(got[lo:hi]), want_pairs[lo:hi]), f"bucket {b}"
+    assert np.array_equal(_host(tiles).astype(np.int64).reshape(-1, 2), want_tiles)
+
+
+@pytest.mark.parametrize("BM", [32, 64, 128])
+def test_bucketing_benchmark_routing(gpu_lib, BM):
+    m = synth.MOE
+    ids = synth.moe_routing(m["T"], m["E"], m["top_k"], synth.rng(5, 0, synth.TAG_ROUTING), s=m["zipf_s"])
+    _check_bucketing(ids, m["E"], BM)
+
+
+@pytest.mark.parametrize("E,P,BM,seed", [
+    (1, 1, 16, 0),          # one pair, one expert
+    (7, 300, 32, 1),        # ids outside [0, E) as well
+    (1000, 3000, 64, 2),    # more than 512 buckets: two scatter passes
+    (4096, 5000, 128, 3),   # the largest E; more rounds than the ids kept in registers
+    (64, 9000, 16, 4),      # long rounds loop, hot and empty buckets
+])
+def test_bucketing_random(gpu_lib, E, P, BM, seed):
+    g = np.random.default_rng(seed)
+    if seed == 4:
+        ids = np.where(g.random(P) < 0.5, 3, g.integers(0, 8, size=P))
+    else:
+        ids = g.integers(-3, E + 3, size=P)
+    _check_bucketing(ids.astype(np.int32), E, BM)

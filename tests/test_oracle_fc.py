@@ -258,3 +258,36 @@ def test_routing_distinct_and_skewed():
         assert len(set(row.tolist())) == 8
     counts = np.bincount(ids.reshape(-1), minlength=128)
     assert counts.sum() == 2048 and counts.max() > 100 and np.median(counts) < 16
+
+
+@pytest.mark.parametrize("E,BM", [(1, 16), (5, 4), (13, 32)])
+def test_moe_bucketing_brute_force(E, BM):
+    # the bucketing against a pair-by-pair walk: each bucket collects its
+    # pairs in increasing index order, then is cut into BM-row tiles
+    g = np.random.default_rng(1000 + E)
+    ids = g.integers(-2, E + 2, size=(37, 3)).astype(np.int32)   # ids outside [0, E) too
+    offsets, pairs, tiles = fc.moe_bucketing(ids, E, BM)
+    flat = ids.reshape(-1).tolist()
+    buckets = [[] for _ in range(E + 1)]
+    for p, e in enumerate(flat):
+        buckets[e if 0 <= e < E else E].append(p)
+    want_pairs = [p for bk in buckets for p in bk]
+    want_offsets = [0]
+    for bk in buckets:
+        want_offsets.append(want_offsets[-1] + len(bk))
+    want_tiles = []
+    for e, bk in enumerate(buckets):
+        r0 = 0
+        while r0 < len(bk):
+            want_tiles.append((e, r0))
+            r0 += BM
+    assert pairs.tolist() == want_pairs
+    assert offsets.tolist() == want_offsets
+    assert [tuple(t) for t in tiles.tolist()] == want_tiles
+
+
+def test_moe_bucketing_empty_buckets_and_no_invalid():
+    offsets, pairs, tiles = fc.moe_bucketing(np.array([[2, 0], [2, 3]], dtype=np.int32), 4, 2)
+    assert offsets.tolist() == [0, 1, 1, 3, 4, 4]
+    assert pairs.tolist() == [1, 0, 2, 3]
+    assert tiles.tolist() == [[0, 0], [2, 0], [3, 0]]
