@@ -107,6 +107,28 @@ def prefill_traffic_from_profile():
     return rec.get("hbm_bytes_per_call")
 
 
+def moe_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("moe.hip", "mfma_tile.h", "common.h", "layout.h"):
+        with open(os.path.join(ROOT, "gguf_quant_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def moe_traffic_from_profile():
+    """HBM bytes per grouped (MoE) call from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "moe_grouped_q6k_traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("moe_source_hash") != moe_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -676,6 +698,69 @@ def prefill_traffic_summary(fetch_csv, write_csv):
     print(json.dumps(rec))
 
 
+def moe_traffic_summary(fetch_csv, write_csv):
+    """Turn the two counter passes over --pmc-moe-target into HBM bytes per
+    grouped call: gate/up (bucketing + grouped FC) and down (grouped FC on
+    gate/up's bucketing), three rounds each, the counters scaled by the
+    factors the decode record measured on the 256 MiB device copy."""
+    import csv
+
+    import numpy as np
+    from gguf_quant_block_amd import synth
+
+    with open(os.path.join(ROOT, "profiles", "decode_gemv_q5k_m1_traffic.json")) as f:
+        dec = json.load(f)
+    f_factor, w_factor = dec["fetch_factor"], dec["write_factor"]
+
+    def read(path, counter):
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id") or 0))
+        calls, cur = [], 0.0
+        for r in rows:
+            v = float(r["Counter_Value"]) * 1024.0
+            if "moe_bucket_kernel" in r["Kernel_Name"]:
+                cur += v
+            elif "moe_grouped_kernel" in r["Kernel_Name"]:
+                calls.append(cur + v)
+                cur = 0.0
+        return calls
+
+    fc, wc = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    assert len(fc) == len(wc) == 6, (len(fc), len(wc))
+    per = [fc[i] * f_factor + wc[i] * w_factor for i in range(6)]
+    m = synth.MOE
+    E, T, top_k = m["E"], m["T"], m["top_k"]
+    ids = synth.moe_routing(T, E, top_k, synth.rng(5, 0, synth.TAG_ROUTING), s=m["zipf_s"])
+    nonempty = int((np.bincount(ids.ravel(), minlength=E) > 0).sum())
+    alg = {}
+    for which, per_slot in (("gate_up", False), ("down", True)):
+        N, K = m[which]
+        a_elems = T * top_k * K if per_slot else T * K
+        alg[which] = nonempty * N * (K // 256) * 210 + 2 * a_elems + 2 * T * top_k * N
+    hbm = {"gate_up": sum(per[0::2]) / 3, "down": sum(per[1::2]) / 3}
+    rec = {
+        "kernel": "moe_bucket_kernel + moe_grouped_kernel (Q6_K)",
+        "workload": "128 experts, top-8, 256 tokens, Zipf(1.1): gate/up [768, 2048] on token rows "
+                    "(bucketing + grouped FC), down [2048, 768] on pair rows (grouped FC on gate/up's "
+                    "bucketing); the benchmark's first routing and weight copy",
+        "moe_source_hash": moe_source_hash(),
+        "calls_counted": 6,
+        "fetch_factor": f_factor,
+        "write_factor": w_factor,
+        "hbm_bytes_per_call": round((hbm["gate_up"] + hbm["down"]) / 2),
+        "algorithmic_bytes_per_call": round((alg["gate_up"] + alg["down"]) / 2),
+        "traffic_over_algorithmic": round((hbm["gate_up"] + hbm["down"]) / (alg["gate_up"] + alg["down"]), 4),
+        "hbm_bytes_per_call_by_fc": {k: round(v) for k, v in hbm.items()},
+        "algorithmic_bytes_per_call_by_fc": alg,
+    }
+    out = os.path.join(ROOT, "profiles", "moe_grouped_q6k_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 # ----------------------------------------------------------------- main ----
 
 class Case:
@@ -753,6 +838,8 @@ def main():
                          "eagerly and a 256 MiB device copy, for rocprofv3 --pmc counter passes")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from the two counter passes over --pmc-target")
+    ap.add_argument("--moe-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/moe_grouped_q6k_traffic.json from two --pmc-moe-target counter passes")
     ap.add_argument("--prefill-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the prefill HBM traffic record from the two counter passes over "
                          "--pmc-prefill4-target")
@@ -762,6 +849,9 @@ def main():
         return
     if args.prefill_traffic_summary:
         prefill_traffic_summary(*args.prefill_traffic_summary)
+        return
+    if args.moe_traffic_summary:
+        moe_traffic_summary(*args.moe_traffic_summary)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU (across GPUs the FC would shard along N, each GPU "
@@ -1037,7 +1127,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(moe_alg / moe_case.seconds() / 1e9 / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": moe_traffic_from_profile(),
         },
         "layer_sets": {
             f"{p}_m{M}": {"weight_gbps": round(layer_rate(p, M)[0], 1),
