@@ -4,7 +4,8 @@ Relative Frobenius error <= 2e-3, over the whole output and per expert, so a
 bug in a 1-row expert is not hidden by the hot experts.  Covers experts
 spanning several ragged tiles, N tails, shared
 and per-pair activation rows, ids outside [0, E), empty experts, T = 0,
-repeat calls, the 32-, 64- and 128-row tile variants, and the full-size
+repeat calls, the 32- and 128-row tile variants (four and two workgroups
+per CU), and the full-size
 routed Q6_K expert FCs (128 experts, top-8, 256 tokens, Zipf 1.1 routing) on
 sampled experts.  The bucketing alone is compared with the oracle's exactly:
 offsets and tile list element by element, the pair list bucket by bucket as
@@ -72,7 +73,7 @@ def _check_experts(y, w, qtype, A, ids, a_per_slot, experts):
 @pytest.mark.parametrize("a_per_slot", [False, True])
 @pytest.mark.parametrize("E,N,K,T,top_k", [
     (8, 200, 512, 37, 2),      # 32-row tiles, N tail, sparse experts
-    (4, 128, 768, 64, 2),      # 128 pairs over 4 experts: 64-row tiles
+    (4, 128, 768, 64, 2),      # 128 pairs over 4 experts: 32-row tiles, all four halves busy
     (16, 96, 256, 90, 4),      # several ragged tiles per hot expert
     (32, 256, 512, 5, 3),      # more experts than pairs: most experts empty
     (2, 96, 1024, 100, 2),     # dense routing: 128-row tiles
