@@ -73,7 +73,7 @@ def _check_experts(y, w, qtype, A, ids, a_per_slot, experts):
 @pytest.mark.parametrize("a_per_slot", [False, True])
 @pytest.mark.parametrize("E,N,K,T,top_k", [
     (8, 200, 512, 37, 2),      # 32-row tiles, N tail, sparse experts
-    (4, 128, 768, 64, 2),      # 128 pairs over 4 experts: 32-row tiles, all four halves busy
+    (4, 128, 768, 64, 2),      # 128 pairs over 4 experts: full 32-row tiles
     (16, 96, 256, 90, 4),      # several ragged tiles per hot expert
     (32, 256, 512, 5, 3),      # more experts than pairs: most experts empty
     (2, 96, 1024, 100, 2),     # dense routing: 128-row tiles
