@@ -245,41 +245,64 @@ __device__ __forceinline__ void tile_mainloop(const uint8_t* W, int N,
 
   const WMap L(N, K);
   // raw bytes of the lane's rows for stage s (half-block hb of block kb):
-  // 8-byte slices of the 16-byte pieces
+  // 8-byte slices of the 16-byte pieces.  A piece's byte offset in a plane
+  // of P pieces per block, ((n/16 * KBp/4 + kb/4) * P + p) * 1024 +
+  // ((kb%4) * 16 + n%16) * 16, splits into a part that depends on the lane
+  // only (its row, its k-quarter's piece and half) and a part that depends on
+  // the stage only, so each load is a wave-uniform base plus a 32-bit lane
+  // offset fixed for the whole loop (one matrix is far below 4 GB).
+  const uint32_t G4 = (uint32_t)(L.KBp / TILE_KB);
+  const uint32_t sub = 8u * (uint32_t)(kq & 1), pq = (uint32_t)(kq >> 1);
+  uint32_t rtile[NT], drow[NT];   // tiles before the row's row tile; the row's offset in D
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    rtile[j] = (uint32_t)nrow[j] / TILE_ROWS * G4;
+    drow[j] = rtile[j] * 128u + ((uint32_t)nrow[j] % TILE_ROWS) * 2u;
+  }
+  auto rowoff = [&](int j, uint32_t P) -> uint32_t {  // the lane's offset in a P-piece plane
+    return ((rtile[j] * P) << 10) + ((uint32_t)nrow[j] % TILE_ROWS) * 16u;
+  };
+  // the stage part: block kb's tile and slot column
+  auto kbterm = [&](int kb, uint32_t P) -> uint32_t {
+    return (((uint32_t)kb >> 2) * P << 10) + (((uint32_t)kb & 3u) << 8);
+  };
   auto load_raw_q5 = [&](int s, RawQ5* raw) {
     const int kb = s >> 1, hb = s & 1;
-    const int sub = 8 * (kq & 1), pq = kq >> 1;
+    const uint8_t* Ws = W + kbterm(kb, 11);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int n = nrow[j];
-      raw[j].hdr = *(const uint4*)(W + L.piece(n, kb, 11, 0));
-      raw[j].qsA = *(const uint2*)(W + L.piece(n, kb, 11, 3 + 4 * hb + pq) + sub);
-      raw[j].qsB = *(const uint2*)(W + L.piece(n, kb, 11, 5 + 4 * hb + pq) + sub);
-      raw[j].qh = *(const uint2*)(W + L.piece(n, kb, 11, 1 + pq) + sub);
+      const uint32_t o = rowoff(j, 11);
+      raw[j].hdr = *(const uint4*)(Ws + o);
+      raw[j].qsA = *(const uint2*)(Ws + (o + ((3u + 4u * hb + pq) << 10) + sub));
+      raw[j].qsB = *(const uint2*)(Ws + (o + ((5u + 4u * hb + pq) << 10) + sub));
+      raw[j].qh = *(const uint2*)(Ws + (o + ((1u + pq) << 10) + sub));
     }
   };
   auto load_raw_q4 = [&](int s, RawQ4* raw) {
     const int kb = s >> 1, hb = s & 1;
-    const int sub = 8 * (kq & 1), pq = kq >> 1;
+    const uint8_t* Ws = W + kbterm(kb, 9);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int n = nrow[j];
-      raw[j].hdr = *(const uint4*)(W + L.piece(n, kb, 9, 0));
-      raw[j].qsA = *(const uint2*)(W + L.piece(n, kb, 9, 1 + 4 * hb + pq) + sub);
-      raw[j].qsB = *(const uint2*)(W + L.piece(n, kb, 9, 3 + 4 * hb + pq) + sub);
+      const uint32_t o = rowoff(j, 9);
+      raw[j].hdr = *(const uint4*)(Ws + o);
+      raw[j].qsA = *(const uint2*)(Ws + (o + ((1u + 4u * hb + pq) << 10) + sub));
+      raw[j].qsB = *(const uint2*)(Ws + (o + ((3u + 4u * hb + pq) << 10) + sub));
     }
   };
   auto load_raw_q6 = [&](int s, RawQ6* raw) {
     const int kb = s >> 1, hb = s & 1;
-    const int sub = 8 * (kq & 1), pq = kq >> 1;
+    const uint8_t* Wl = W + kbterm(kb, 8);
+    const uint8_t* Wh = W + L.qh_base() + kbterm(kb, 4);
+    const uint8_t* Wc = W + L.sc_base() + kbterm(kb, 1);
+    const uint8_t* Wd = W + L.d_base() + ((uint32_t)kb >> 2) * 128u + ((uint32_t)kb & 3u) * 32u;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int n = nrow[j];
-      raw[j].qlA = *(const uint2*)(W + L.piece(n, kb, 8, 4 * hb + pq) + sub);
-      raw[j].qlB = *(const uint2*)(W + L.piece(n, kb, 8, 4 * hb + 2 + pq) + sub);
-      raw[j].qh = *(const uint2*)(W + L.qh_base() + L.piece(n, kb, 4, 2 * hb + pq) + sub);
-      raw[j].sc = *(const uint2*)(W + L.sc(n, kb) + 8 * hb);
-      raw[j].d = *(const uint16_t*)(W + L.d(n, kb));
+      const uint32_t ol = rowoff(j, 8), oh = rowoff(j, 4), oc = rowoff(j, 1);
+      raw[j].qlA = *(const uint2*)(Wl + (ol + ((4u * hb + pq) << 10) + sub));
+      raw[j].qlB = *(const uint2*)(Wl + (ol + ((4u * hb + 2u + pq) << 10) + sub));
+      raw[j].qh = *(const uint2*)(Wh + (oh + ((2u * hb + pq) << 10) + sub));
+      raw[j].sc = *(const uint2*)(Wc + (oc + 8u * hb));
+      raw[j].d = *(const uint16_t*)(Wd + drow[j]);
     }
   };
   using Raw = typename std::conditional<
