@@ -210,7 +210,7 @@ int fc_gguf_run_grouped_reuse(fc_gguf_t h, fc_gguf_t routed, const void* A, int6
  * 512 KB device array of the library (one per GPU, held until the process
  * ends) instead of the handle's workspace; no hipMalloc, hipFree or other
  * allocating call is made.  Calls whose bucketing needs more than 512 KB
- * (about E*8 + T*top_k*4.25 bytes) return FC_GGUF_ERANGE.  Every call on one
+ * (about E*12 + T*top_k*4.25 bytes) return FC_GGUF_ERANGE.  Every call on one
  * GPU shares that GPU's array: calls that overlap in time on one GPU (two
  * streams, or two host threads) race and must not be issued; calls ordered on
  * one stream are safe.
