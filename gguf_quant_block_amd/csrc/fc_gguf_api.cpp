@@ -276,9 +276,11 @@ hipError_t run_decode(fc_gguf_t h, const AT* a, const AT* r, AT* y, int64_t M, h
   hipError_t e = hipSuccess;
   for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += cap) {
     const int mc = (int)(M - m0 < cap ? M - m0 : cap);
-    // measured: one activation row streams best with two workgroups per CU,
-    // several rows (more arithmetic per weight byte) with one
-    const int max_wgs = (mc == 1 ? 2 : 1) * h->num_cu;
+    // measured: one or two activation rows stream best with two workgroups
+    // per CU (two rows: Q5_K layer set 7.29 -> 7.04 us per launch), four and
+    // more (more arithmetic per weight byte) with one (two per CU: Q6_K
+    // qkv at four rows 9.26 -> 11.07 us, Q5_K at seven rows +26-29 %)
+    const int max_wgs = (mc <= 2 ? 2 : 1) * h->num_cu;
     if constexpr (sizeof(AT) == 2)
       e = fcg::launch_gemv(h->qtype, h->w, a + m0 * K, r ? r + m0 * N : nullptr, y + m0 * N, mc, N,
                            K, max_wgs, st);
